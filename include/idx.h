@@ -1,0 +1,151 @@
+/*
+ * idx.h -- C ABI of the MI355X (gfx950) sparse-attention indexer library (libidx.so).
+ *
+ * The operation is the indexer of the GLM-5.3 indexer page
+ * (sgl-amd-mono-upstream pull request 18).  For every decode or MTP-verify
+ * row it scores each cached key of the row's request against the row's index
+ * query and selects the row's exact top-k keys (Motivation; Modifications
+ * item 0, the exact top-k check; items 2 and 3):
+ *
+ *   score[r][p] = sum_h w[r][h] * ReLU( s[p] * sum_d q[r][h][d] * k8[p][d] )
+ *
+ * with q the bf16 index query, w the bf16 head weights, k8 the key's OCP
+ * FP8-E4M3FN code value and s its per-key f32 scale, for every logical
+ * position p < n_keys[r].  The top-k set is the first k positions by score
+ * descending, then position ascending (the page's definition of exactness);
+ * the list is emitted in ascending position order, padded with -1 when a row
+ * has fewer than k keys.
+ *
+ * Conventions shared by every entry point
+ *  - Every array argument is a DEVICE pointer owned by the caller, except
+ *    idx_problem.req_indptr, which is a HOST array.  The library allocates
+ *    nothing on a call path and keeps no pointer after a call returns; buffers
+ *    must stay alive until the stream has passed the call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is only enqueued; results follow stream order.
+ *  - Return codes: IDX_OK, or one of the IDX_E* codes below.  Invalid
+ *    arguments are rejected on the host before any HIP call.  No exception
+ *    crosses the ABI and nothing is printed.
+ *  - Device-resident values (n_keys, page ids) are checked by the kernels:
+ *    an n_keys entry outside [0, max_keys] is clamped into range and a page
+ *    id outside [0, num_pages) is replaced by page 0; either raises a sticky
+ *    error bit in the workspace, read back with idx_device_status().
+ *  - A workspace is used by one stream at a time; calls on distinct
+ *    workspaces are independent.  It must be initialised once with
+ *    idx_workspace_init() (and again after a device error).
+ */
+#ifndef IDX_H
+#define IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Compiled shape (the GLM-5.3 indexer: 64 index heads of dimension 128,
+ * pages of 64 keys; at most 4 rows of one request are scored together,
+ * Modifications item 2). */
+#define IDX_HEADS 64
+#define IDX_DIM 128
+#define IDX_PAGE_SIZE 64
+#define IDX_KMAX 2048
+#define IDX_GROUP_ROWS 4
+#define IDX_MAX_REQ 256
+#define IDX_ABI_VERSION 1
+
+/* Return codes. */
+#define IDX_OK 0
+#define IDX_EINVAL 1       /* null pointer, bad size/stride/alignment, k out of [1, IDX_KMAX], bad req_indptr */
+#define IDX_EUNSUPPORTED 2 /* heads/dim/page size not the compiled ones, > IDX_GROUP_ROWS rows in a request, > IDX_MAX_REQ requests */
+#define IDX_EWORKSPACE 3   /* workspace null or smaller than idx_workspace_bytes() */
+#define IDX_EHIP 4         /* a HIP runtime call or launch failed; see idx_last_hip_error() */
+#define IDX_EDEVICE 5      /* a sticky device-side error was found by idx_device_status() */
+
+/* Sticky device error bits (idx_device_status(), *detail). */
+#define IDX_DERR_NKEYS 0x1u       /* an n_keys entry was outside [0, max_keys] */
+#define IDX_DERR_PAGE 0x2u        /* a page id was outside [0, num_pages) */
+#define IDX_DERR_WS 0x4u          /* the workspace was not initialised */
+#define IDX_DERR_TIMEOUT 0x8u     /* a bounded wait between workgroups ran out */
+#define IDX_DERR_SELECT 0x10u     /* internal selection invariant failed (list count != k) */
+
+typedef struct idx_problem {
+  int32_t rows;              /* R >= 1 step rows */
+  int32_t num_req;           /* 1 <= num_req <= IDX_MAX_REQ */
+  const int32_t* req_indptr; /* HOST [num_req + 1]: request j owns rows [req_indptr[j], req_indptr[j+1]);
+                                req_indptr[0] = 0, strictly increasing, req_indptr[num_req] = rows,
+                                at most IDX_GROUP_ROWS rows per request */
+  int32_t heads;             /* must be IDX_HEADS */
+  int32_t dim;               /* must be IDX_DIM */
+  int32_t page_size;         /* must be IDX_PAGE_SIZE */
+  int32_t num_pages;         /* pages in the cache pool, >= 1 */
+  int32_t max_pages;         /* columns of page_table, >= 1 */
+  int32_t max_keys;          /* host bound on every n_keys[r]; 0 <= max_keys <= max_pages * page_size */
+  const void* q;             /* bf16 [rows][heads][dim], contiguous, 16-byte aligned */
+  const void* w;             /* bf16 [rows][heads], contiguous, 4-byte aligned */
+  const uint8_t* k_cache;    /* E4M3FN codes [num_pages][page_size][dim], 16-byte aligned */
+  const float* k_scale;      /* f32 [num_pages][page_size], finite and >= 0, 16-byte aligned */
+  const int32_t* page_table; /* int32 [rows][max_pages]: logical page j of row r is physical page
+                                page_table[r][j]; rows of one request must hold the same entries for
+                                the pages they use (the kernels walk the row with the most keys) */
+  const int32_t* n_keys;     /* int32 [rows]: keys row r sees, 0 <= n_keys[r] <= max_keys */
+  const int32_t* req_max_keys; /* HOST [num_req] or NULL: a bound on n_keys over each request's rows
+                                  (<= max_keys).  Only sizes the launch: workgroups past a request's
+                                  bound exit at once.  A row above its request's bound is clamped to
+                                  it and raises IDX_DERR_NKEYS. */
+} idx_problem;
+
+/* ABI version (IDX_ABI_VERSION). */
+int idx_abi_version(void);
+
+/* Bytes of workspace any entry point needs for up to `rows` rows of up to
+ * `max_keys` keys and top-k size k.  Returns IDX_OK and sets *bytes, or
+ * IDX_EINVAL. */
+int idx_workspace_bytes(int32_t rows, int32_t max_keys, int32_t k, size_t* bytes);
+
+/* Zero the workspace and stamp it initialised (a device fill kernel on
+ * `stream`; no host synchronisation).  ws must be 256-byte aligned and
+ * ws_bytes a multiple of 256 and >= 256. */
+int idx_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Scores only: scores[r * ld_scores + p] for p < n_keys[r] (entries past
+ * n_keys[r] are not written).  ld_scores >= max(1, max_keys). */
+int idx_score(const idx_problem* p, float* scores, int64_t ld_scores,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Exact top-k over given scores: for each row r, topk[r * k + i] (i < k) is
+ * the ascending list of the first k positions p < n_keys[r] by (score desc,
+ * position asc), padded with -1; scores compare as real numbers (-0 == +0).
+ * scores must be finite.  n_keys is a device array of `rows` entries. */
+int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys,
+             int32_t rows, int32_t max_keys, int32_t k, int32_t* topk,
+             void* ws, size_t ws_bytes, void* stream);
+
+/* Fused scoring and exact top-k in one launch: writes the scores exactly as
+ * idx_score() does and the lists exactly as idx_topk() over those scores. */
+int idx_score_topk(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores,
+                   int32_t* topk, void* ws, size_t ws_bytes, void* stream);
+
+/* Synchronise `stream`, read and clear the workspace's sticky device error.
+ * Returns IDX_OK, IDX_EDEVICE (with *detail = IDX_DERR_* bits when detail is
+ * not NULL), or IDX_EHIP. */
+int idx_device_status(void* ws, size_t ws_bytes, void* stream, uint32_t* detail);
+
+/* Static description of a return code. */
+const char* idx_strerror(int code);
+
+/* The last HIP error string seen by this thread (empty if none). */
+const char* idx_last_hip_error(void);
+
+/* Test hook for the failure paths, not for production use: key 1 sets the
+ * bound (in polls) of every wait between workgroups (0 = the default);
+ * key 2 makes the workgroup with this chunk index skip publishing its
+ * candidates (-1 = off).  Returns IDX_OK or IDX_EINVAL. */
+int idx_debug_set(int32_t key, int32_t value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDX_H */

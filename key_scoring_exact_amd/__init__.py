@@ -1,0 +1,190 @@
+"""MI355X sparse-attention indexer: exact key scoring and exact top-k (Python binding).
+
+A thin ctypes layer over libidx.so (include/idx.h).  Every step runs in the HIP
+kernels; this module only turns torch tensors into device pointers, picks the
+current HIP stream and raises on error codes.  torch provides device memory and
+streams.  There is no CPU fallback: without the built library, import of the
+entry points fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import (IDX_DIM, IDX_GROUP_ROWS, IDX_HEADS, IDX_KMAX, IDX_MAX_REQ,  # noqa: F401
+                   IDX_PAGE_SIZE, IdxProblem)
+
+__all__ = ["IdxError", "DeviceProblem", "Workspace", "score", "topk", "score_topk",
+           "device_status", "workspace_bytes", "lib"]
+
+
+class IdxError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        L = lib()
+        msg = L.idx_strerror(code).decode()
+        if code == _lib.IDX_EHIP:
+            msg += ": " + L.idx_last_hip_error().decode()
+        super().__init__(f"{where}: {msg} (code {code})")
+        self.code = code
+
+
+def lib():
+    return _lib.load()
+
+
+def _check(code: int, where: str):
+    if code != _lib.IDX_OK:
+        raise IdxError(code, where)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor, dtype=None) -> int:
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"expected dtype {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def workspace_bytes(rows: int, max_keys: int, k: int = IDX_KMAX) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().idx_workspace_bytes(int(rows), int(max_keys), int(k), ctypes.byref(out)), "idx_workspace_bytes")
+    return int(out.value)
+
+
+class Workspace:
+    """Caller-owned device workspace (torch memory), initialised on creation."""
+
+    def __init__(self, rows: int, max_keys: int, k: int = IDX_KMAX, device="cuda", stream=None):
+        nbytes = workspace_bytes(rows, max_keys, k)
+        self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        base = self.buf.data_ptr()
+        self.offset = (-base) % 256
+        self.nbytes = nbytes
+        self.reset(stream)
+
+    @property
+    def ptr(self) -> int:
+        return self.buf.data_ptr() + self.offset
+
+    def reset(self, stream=None):
+        _check(lib().idx_workspace_init(ctypes.c_void_p(self.ptr), self.nbytes, ctypes.c_void_p(_stream(stream))),
+               "idx_workspace_init")
+
+
+@dataclasses.dataclass
+class DeviceProblem:
+    """Device-resident inputs of one call; req_indptr (and req_max_keys) stay on the host."""
+
+    q: torch.Tensor           # bf16 (or int16 bit patterns) [rows, 64, 128]
+    w: torch.Tensor           # bf16 (or int16) [rows, 64]
+    k_cache: torch.Tensor     # uint8 [num_pages, 64, 128] (E4M3FN codes)
+    k_scale: torch.Tensor     # float32 [num_pages, 64]
+    page_table: torch.Tensor  # int32 [rows, max_pages]
+    n_keys: torch.Tensor      # int32 [rows]
+    req_indptr: Sequence[int]
+    max_keys: int
+    req_max_keys: Optional[Sequence[int]] = None
+
+    @property
+    def rows(self) -> int:
+        return int(self.q.shape[0])
+
+    @classmethod
+    def from_arrays(cls, q, w, k_cache, k_scale, page_table, n_keys, req_indptr, max_keys=None,
+                    req_max_keys=None, device="cuda") -> "DeviceProblem":
+        def up(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+
+        n_keys = np.asarray(n_keys, dtype=np.int32)
+        if max_keys is None:
+            max_keys = int(n_keys.max()) if n_keys.size else 0
+        return cls(q=up(q, np.int16), w=up(w, np.int16), k_cache=up(k_cache, np.uint8),
+                   k_scale=up(k_scale, np.float32), page_table=up(page_table, np.int32),
+                   n_keys=up(n_keys, np.int32), req_indptr=[int(x) for x in req_indptr],
+                   max_keys=int(max_keys),
+                   req_max_keys=None if req_max_keys is None else [int(x) for x in req_max_keys])
+
+    def struct(self):
+        """The idx_problem struct and the host arrays it points to (keep both alive)."""
+        ip = (ctypes.c_int32 * len(self.req_indptr))(*self.req_indptr)
+        rm = None
+        if self.req_max_keys is not None:
+            rm = (ctypes.c_int32 * len(self.req_max_keys))(*self.req_max_keys)
+        s = IdxProblem(
+            rows=self.rows, num_req=len(self.req_indptr) - 1,
+            req_indptr=ctypes.cast(ip, ctypes.POINTER(ctypes.c_int32)),
+            heads=int(self.q.shape[1]), dim=int(self.q.shape[2]), page_size=int(self.k_cache.shape[1]),
+            num_pages=int(self.k_cache.shape[0]), max_pages=int(self.page_table.shape[1]),
+            max_keys=int(self.max_keys),
+            q=_ptr(self.q, (torch.bfloat16, torch.int16)), w=_ptr(self.w, (torch.bfloat16, torch.int16)),
+            k_cache=_ptr(self.k_cache, (torch.uint8, torch.float8_e4m3fn)),
+            k_scale=_ptr(self.k_scale, torch.float32),
+            page_table=_ptr(self.page_table, torch.int32), n_keys=_ptr(self.n_keys, torch.int32),
+            req_max_keys=None if rm is None else ctypes.cast(rm, ctypes.POINTER(ctypes.c_int32)))
+        return s, (ip, rm)
+
+
+def score(p: DeviceProblem, ws: Workspace, scores: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """f32 scores [rows, ld]; entries at positions >= n_keys[r] are left untouched."""
+    if scores is None:
+        scores = torch.empty((p.rows, max(1, p.max_keys)), dtype=torch.float32, device=p.q.device)
+    s, keep = p.struct()
+    _check(lib().idx_score(ctypes.byref(s), ctypes.c_void_p(_ptr(scores, torch.float32)), scores.shape[1],
+                           ctypes.c_void_p(ws.ptr), ws.nbytes, ctypes.c_void_p(_stream(stream))), "idx_score")
+    return scores
+
+
+def score_topk(p: DeviceProblem, k: int, ws: Workspace, scores: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None, stream=None):
+    """(scores [rows, ld] f32, lists [rows, k] int32) in one launch."""
+    if scores is None:
+        scores = torch.empty((p.rows, max(1, p.max_keys)), dtype=torch.float32, device=p.q.device)
+    if out is None:
+        out = torch.empty((p.rows, k), dtype=torch.int32, device=p.q.device)
+    s, keep = p.struct()
+    _check(lib().idx_score_topk(ctypes.byref(s), int(k), ctypes.c_void_p(_ptr(scores, torch.float32)),
+                                scores.shape[1], ctypes.c_void_p(_ptr(out, torch.int32)),
+                                ctypes.c_void_p(ws.ptr), ws.nbytes, ctypes.c_void_p(_stream(stream))),
+           "idx_score_topk")
+    return scores, out
+
+
+def topk(scores: torch.Tensor, n_keys: torch.Tensor, k: int, max_keys: int, ws: Workspace,
+         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Exact top-k lists [rows, k] int32 of given f32 scores [rows, ld]."""
+    rows = int(scores.shape[0])
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    _check(lib().idx_topk(ctypes.c_void_p(_ptr(scores, torch.float32)), scores.shape[1],
+                          ctypes.c_void_p(_ptr(n_keys, torch.int32)), rows, int(max_keys), int(k),
+                          ctypes.c_void_p(_ptr(out, torch.int32)), ctypes.c_void_p(ws.ptr), ws.nbytes,
+                          ctypes.c_void_p(_stream(stream))), "idx_topk")
+    return out
+
+
+def device_status(ws: Workspace, stream=None):
+    """(code, detail bits): synchronises the stream, reads and clears the sticky error."""
+    detail = ctypes.c_uint32(0)
+    code = lib().idx_device_status(ctypes.c_void_p(ws.ptr), ws.nbytes, ctypes.c_void_p(_stream(stream)),
+                                   ctypes.byref(detail))
+    return int(code), int(detail.value)
+
+
+def debug_set(key: int, value: int):
+    """Test hook of the failure paths (see idx_debug_set in include/idx.h)."""
+    _check(lib().idx_debug_set(int(key), int(value)), "idx_debug_set")

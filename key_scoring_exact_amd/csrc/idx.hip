@@ -1,0 +1,1179 @@
+// libidx: MI355X (gfx950) sparse-attention indexer -- key scoring and exact top-k.
+//
+// The operation is the indexer of the GLM-5.3 indexer page (sgl-amd-mono-upstream
+// pull request 18): every key of a request is scored against each row's bf16 index
+// query (Modifications item 2: a request's rows scored together, each key read once),
+// and each row's exact top-k is selected (item 3), exact in the sense of item 0:
+// the first k positions by score descending, then position.
+//
+//   score[r][p] = sum_h w[r][h] * ReLU( s[p] * <q[r][h][:], k8[p][:]> )
+//
+// One kernel template covers the three entry points:
+//   * scoring:  each workgroup stages whole pages of its chunk of the request's keys
+//     in LDS (16-byte global->LDS DMA loads, XOR-swizzled 16-byte chunks), and every
+//     wave multiplies one row's 64 heads against them on FP8 MFMA (32x32x64).  The
+//     bf16 query is split exactly into two E4M3 terms, q = 2^-a (hi + 2^-5 lo), per
+//     (row, head); lo is fed through the block-scaled MFMA with scale 2^-5 so both
+//     terms land in one f32 accumulator.  The epilogue applies ReLU and the
+//     head weights (pre-multiplied by 2^-a), sums across the 64 heads in f32 and
+//     multiplies by the key's scale (s >= 0 factors out of the ReLU).
+//   * selection over the scores of a row: each workgroup publishes, per row, every key
+//     of its chunk at or above a local threshold t_w (the m-th largest of its 64 lane
+//     maxima), write-through, then a tagged arrival word.  One designated workgroup
+//     per row gathers the candidates, finds the exact k-th key T by radix select in
+//     LDS and checks t_w <= T for every chunk (then no key left behind can reach
+//     the top k); chunks that fail are re-read in full.  The selected positions are
+//     marked in an LDS bitmap (ties at T resolved by lowest position) and emitted in
+//     ascending order.  Rows of up to ALL_MAX keys skip the candidates and select
+//     from all their scores directly; anything beyond the LDS capacities takes an
+//     exact multi-pass radix select over the row's scores in global memory.
+//   * fused: scoring then selection in the same launch, the scores staying in LDS
+//     for the candidate step.
+//
+// All waits between workgroups are bounded polls; a timeout sets a sticky error bit.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "idx.h"
+
+namespace {
+
+constexpr int H = IDX_HEADS;
+constexpr int D = IDX_DIM;
+constexpr int PS = IDX_PAGE_SIZE;
+constexpr int GR = IDX_GROUP_ROWS;
+constexpr int NT = 512;                 // threads per workgroup (8 waves, 2 per SIMD)
+constexpr int PMAX = 8;                 // pages per workgroup at most
+constexpr int CMAX = PMAX * PS;         // keys per chunk at most (512)
+constexpr int ALL_MAX = 24576;          // rows up to this many keys select from all scores at once
+constexpr int FIN_ENT = 12288;          // candidate capacity of a finishing workgroup
+constexpr int BITMAP_KEYS = 131072;     // positions covered by the finisher's LDS bitmap
+constexpr int CAP_MAX = 144;            // candidate slots per chunk and row
+constexpr int LOAD_BATCH = 64;          // candidate loads in flight per thread
+constexpr uint32_t WS_MAGIC = 0x1D5C0DE5u;
+constexpr int DEFAULT_SPIN = 1 << 20;   // polls before a wait gives up (about a second)
+
+constexpr int MODE_SCORE = 1;           // compute scores (else read them from args.scores)
+constexpr int MODE_SELECT = 2;          // select the top k
+
+// LDS layout, scoring phase (bytes)
+constexpr int L_KEYS = 0;                                   // [PMAX][64 keys][128 B], swizzled
+constexpr int L_KSC = PMAX * PS * D;                        // [PMAX][64] f32 key scales
+constexpr int L_WQ = L_KSC + PMAX * PS * 4;                 // [GR][64] f32 head weights * 2^-a
+constexpr int L_SC = L_WQ + GR * H * 4;                     // [GR][CMAX] f32 scores of the chunk
+constexpr int L_Q = L_SC + GR * CMAX * 4;                   // [GR][64 heads][256 B] bf16 queries, swizzled
+constexpr int L_W = L_Q + GR * H * D * 2;                   // [GR][64] bf16 head weights
+constexpr int L_SCORE_END = L_W + GR * H * 2;
+// LDS layout, finishing phase
+constexpr int L_FK = 0;                                     // keys: FIN_ENT (or ALL_MAX when positions are implicit)
+constexpr int L_FP = FIN_ENT * 4;                           // positions: FIN_ENT
+constexpr int L_BM = ALL_MAX * 4;                           // bitmap: BITMAP_KEYS / 32 words
+constexpr int L_HIST = L_BM + BITMAP_KEYS / 8;              // 256 u32 histogram
+constexpr int L_MISC = L_HIST + 256 * 4;                    // 64 u32 scratch
+constexpr int L_FIN_END = L_MISC + 64 * 4;
+constexpr int LDS_BYTES = (L_FIN_END > L_SCORE_END ? L_FIN_END : L_SCORE_END);
+static_assert(FIN_ENT * 8 <= ALL_MAX * 4, "candidate keys+positions must fit the key region");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+
+// workspace header (bytes)
+constexpr int WS_MAGIC_OFF = 0;
+constexpr int WS_ERR_OFF = 4;
+constexpr int WS_HDR = 256;
+
+struct KArgs {
+  const uint32_t* q;        // bf16 [rows][64][128] viewed as u32 pairs
+  const uint16_t* w;        // bf16 [rows][64]
+  const uint8_t* kc;        // E4M3 [num_pages][64][128]
+  const float* ks;          // f32 [num_pages][64]
+  const int32_t* pt;        // int32 [rows][max_pages]
+  const int32_t* nk;        // int32 [rows]
+  float* scores;            // [rows][ld]: written (MODE_SCORE) or read
+  int32_t* topk;            // [rows][k]
+  uint8_t* ws;
+  int64_t ld;
+  int64_t ws_bytes;
+  int32_t rows, max_pages, max_keys, num_pages, k;
+  int32_t chunk;            // keys per workgroup chunk (P * 64)
+  int32_t mode;
+  int32_t spin_limit;
+  int32_t skip_chunk;       // test hook: this chunk publishes nothing (-1 = off)
+  int32_t meta_stride;      // chunk slots per row (>= gridDim.x)
+  uint64_t off_epoch, off_meta, off_tw, off_ent;
+  uint32_t grp[IDX_MAX_REQ];// row0 | nrows << 24
+  int32_t gmax[IDX_MAX_REQ];     // host bound on the keys of each group's rows
+};
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR(T, off) (reinterpret_cast<T*>(smem + (off)))
+
+// ---------------------------------------------------------------------------
+// memory helpers
+// ---------------------------------------------------------------------------
+// Cache policy bits of buffer instructions on gfx950: sc0 = 1, nt = 2, sc1 = 16.
+// sc0|sc1 reads miss the non-coherent caches and writes go through to memory, so
+// data handed between workgroups on different XCDs needs no cache-wide fence.
+constexpr int CP_COHERENT = 1 | 16;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  int64_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16-byte global -> LDS DMA per lane: lane l writes LDS bytes [lds + 16 l, lds + 16 l + 16).
+// Written as inline assembly so that the compiler neither tracks it nor inserts its own
+// conservative waits before LDS reads; callers wait with explicit vmcnt counts.
+__device__ inline void dma16(const void* gptr, uint32_t lds_wave_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base))
+               : "memory");
+}
+
+__device__ inline uint32_t ld_co32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t ld_co64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_co32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_co64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void raise_error(uint8_t* ws, uint32_t bits) {
+  __hip_atomic_fetch_or(reinterpret_cast<uint32_t*>(ws + WS_ERR_OFF), bits, __ATOMIC_RELAXED,
+                        __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Monotone map of a finite f32 score to an unsigned key (larger score, larger key);
+// -0 is first folded into +0 so that equal reals get equal keys.  Finite scores map
+// to keys >= 0x00800000, so 0 never denotes a real score.
+__device__ inline uint32_t radix_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline int lane_id() { return (int)(threadIdx.x & 63); }
+
+// m-th largest of one value per lane (m >= 1): the largest t with #{v >= t} >= m.
+__device__ inline uint32_t wave_kth_largest(uint32_t v, int m) {
+  uint32_t t = 0;
+  for (int b = 31; b >= 0; --b) {
+    uint32_t cand = t | (1u << b);
+    uint64_t bal = __ballot(v >= cand);
+    if (__popcll(bal) >= m) t = cand;
+  }
+  return t;
+}
+
+__device__ inline int wave_incl_scan(int x) {
+  const int l = lane_id();
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (l >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive scan over the workgroup; `tmp` is NT/64 (8) ints of LDS.  Every thread must call.
+__device__ inline int block_excl_scan(int v, int* tmp, int* total) {
+  const int l = lane_id(), wv = threadIdx.x >> 6;
+  int x = wave_incl_scan(v);
+  if (l == 63) tmp[wv] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; i++) {
+    int s = tmp[i];
+    before += (i < wv) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  if (total) *total = tot;
+  return x - v + before;
+}
+
+// ---------------------------------------------------------------------------
+// Exact k-th largest key among LDS keys K[0..E): radix select, 8-bit digits from the
+// top.  Returns T; *rem = how many keys equal to T belong to the top k, *ceq = how
+// many keys equal T.  Requires 1 <= k <= E.  Every thread must call.
+// ---------------------------------------------------------------------------
+__device__ uint32_t block_kth_lds(const uint32_t* K, int E, int k, uint32_t* hist, int* misc,
+                                  int* rem_out, int* ceq_out) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  int rem = k;
+  int ceq = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int e = tid; e < E; e += NT) {
+      uint32_t key = K[e];
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const int cnt = (tid < 256) ? (int)hist[255 - tid] : 0;
+    int tot;
+    const int excl = block_excl_scan(cnt, misc, &tot);
+    if (tid < 256 && excl < rem && rem <= excl + cnt) {
+      misc[8] = 255 - tid;
+      misc[9] = rem - excl;
+      misc[10] = cnt;
+    }
+    __syncthreads();
+    const uint32_t d = (uint32_t)misc[8];
+    rem = misc[9];
+    ceq = misc[10];
+    prefix |= d << shift;
+    mask |= 0xFFu << shift;
+    __syncthreads();
+  }
+  *rem_out = rem;
+  *ceq_out = ceq;
+  return prefix;
+}
+
+// Mark the top-k of candidate set (K, P)[0..E) in the bitmap and emit positions in
+// ascending order to out[0..k).  T / rem / ceq from block_kth_lds.  P == nullptr means
+// P[e] = e.  n = the row's key count (bitmap covers [0, n)).  Returns the number of
+// positions emitted.  Every thread must call.
+__device__ int bitmap_emit(const uint32_t* K, const uint32_t* P, int E, int n, uint32_t T, int rem,
+                           int ceq, uint32_t* bm, int* misc, int32_t* out, int kk) {
+  const int tid = threadIdx.x;
+  const int words = (n + 31) >> 5;
+  for (int i = tid; i < words; i += NT) bm[i] = 0;
+  __syncthreads();
+  uint32_t pos_cut = 0xFFFFFFFFu;  // ties at T with position <= pos_cut are taken
+  if (ceq > rem) {
+    for (int e = tid; e < E; e += NT)
+      if (K[e] == T) {
+        uint32_t p = P ? P[e] : (uint32_t)e;
+        atomicOr(&bm[p >> 5], 1u << (p & 31));
+      }
+    __syncthreads();
+    // position of the rem-th set bit
+    const int wpt = (words + NT - 1) / NT;
+    const int w0 = tid * wpt;
+    int c = 0;
+    for (int i = 0; i < wpt; i++) c += (w0 + i < words) ? __popc(bm[w0 + i]) : 0;
+    int tot;
+    int before = block_excl_scan(c, misc, &tot);
+    if (before < rem && rem <= before + c) {
+      int need = rem - before;
+      for (int i = 0; i < wpt; i++) {
+        uint32_t x = (w0 + i < words) ? bm[w0 + i] : 0u;
+        int pc = __popc(x);
+        if (need <= pc) {
+          for (int b = 0; b < 32; b++)
+            if ((x >> b) & 1u) {
+              if (--need == 0) { misc[12] = (w0 + i) * 32 + b; break; }
+            }
+          break;
+        }
+        need -= pc;
+      }
+    }
+    __syncthreads();
+    pos_cut = (uint32_t)misc[12];
+    for (int i = tid; i < words; i += NT) bm[i] = 0;
+    __syncthreads();
+  }
+  for (int e = tid; e < E; e += NT) {
+    uint32_t key = K[e];
+    uint32_t p = P ? P[e] : (uint32_t)e;
+    if (key > T || (key == T && p <= pos_cut)) atomicOr(&bm[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  const int wpt = (words + NT - 1) / NT;
+  const int w0 = tid * wpt;
+  int c = 0;
+  for (int i = 0; i < wpt; i++) c += (w0 + i < words) ? __popc(bm[w0 + i]) : 0;
+  int tot;
+  int o = block_excl_scan(c, misc, &tot);
+  for (int i = 0; i < wpt; i++) {
+    if (w0 + i >= words) break;
+    uint32_t x = bm[w0 + i];
+    while (x) {
+      int b = __ffs(x) - 1;
+      x &= x - 1;
+      if (o < kk) out[o] = (w0 + i) * 32 + b;
+      o++;
+    }
+  }
+  return tot;
+}
+
+// Exact top-k of row scores in global memory (n > k), one workgroup, no LDS limits
+// beyond the histogram: radix select over all scores, then an ordered emission.
+__device__ void global_select_row(const float* row, int n, int k, int32_t* out, uint32_t* hist,
+                                  int* misc) {
+  const int tid = threadIdx.x;
+  __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (int64_t)n * 4);
+  uint32_t prefix = 0, mask = 0;
+  int rem = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int base = 0; base < n; base += NT * 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        int p = base + j * NT + tid;
+        v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, p * 4, 0, CP_COHERENT));
+      }
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        int p = base + j * NT + tid;
+        uint32_t key = radix_key(v[j]);
+        if (p < n && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    const int cnt = (tid < 256) ? (int)hist[255 - tid] : 0;
+    int tot;
+    const int excl = block_excl_scan(cnt, misc, &tot);
+    if (tid < 256 && excl < rem && rem <= excl + cnt) {
+      misc[8] = 255 - tid;
+      misc[9] = rem - excl;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)misc[8] << shift;
+    mask |= 0xFFu << shift;
+    rem = misc[9];
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  int eq_carry = 0, sel_carry = 0;
+  for (int base = 0; base < n; base += NT * 8) {
+    const int p0 = base + tid * 8;
+    uint32_t key[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      key[j] = radix_key(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (p0 + j) * 4, 0, CP_COHERENT)));
+    int ceq = 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) ceq += (p0 + j < n && key[j] == T) ? 1 : 0;
+    int eq_tot;
+    int eq_before = block_excl_scan(ceq, misc, &eq_tot) + eq_carry;
+    bool sel[8];
+    int cs = 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      bool valid = p0 + j < n;
+      bool s = valid && key[j] > T;
+      if (valid && key[j] == T) {
+        s = eq_before < rem;
+        eq_before++;
+      }
+      sel[j] = s;
+      cs += s ? 1 : 0;
+    }
+    int sel_tot;
+    int o = block_excl_scan(cs, misc, &sel_tot) + sel_carry;
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      if (sel[j]) {
+        if (o < k) out[o] = p0 + j;
+        o++;
+      }
+    eq_carry += eq_tot;
+    sel_carry += sel_tot;
+  }
+}
+
+// m (lane-maximum rank used as the local threshold) and the candidate cap, from the
+// row length n, chunk size C and k.  About k*C/n keys of a chunk reach the top k.
+__device__ inline void candidate_params(int n, int C, int k, int* m, int* cap) {
+  int64_t lam = ((int64_t)k * C + n - 1) / n;
+  int mm = (int)(lam + lam / 4 + 12);
+  mm = mm > 64 ? 64 : mm;
+  int cc = 2 * mm + 16;
+  cc = cc > C ? C : cc;
+  cc = cc > CAP_MAX ? CAP_MAX : cc;
+  *m = mm;
+  *cap = cc;
+}
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+template <int P>
+__global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int c = blockIdx.x;
+  const int g = blockIdx.y;
+  const uint32_t ge = a.grp[g];
+  const int row0 = (int)(ge & 0xFFFFFFu);
+  const int R = (int)(ge >> 24);
+  const int C = a.chunk;
+  const int chunk_base = c * C;
+  uint8_t* const ws = a.ws;
+
+  const int gbound = a.gmax[g];
+  if (c > 0 && chunk_base >= gbound) return;      // beyond every row of this group
+  if (*reinterpret_cast<const uint32_t*>(ws + WS_MAGIC_OFF) != WS_MAGIC) {
+    if (tid == 0 && c == 0 && g == 0) raise_error(ws, IDX_DERR_WS);
+    return;
+  }
+  const bool do_score = (a.mode & MODE_SCORE) != 0;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  if (do_score) {
+    // Queries and head weights of the group's rows into LDS first (2R + 1 DMA per
+    // wave); their latency overlaps the n_keys / page-table load below.  Head h's 16
+    // chunks of 16 bytes sit at chunk positions c ^ (h & 15), so the A-operand reads
+    // (16 lanes on 16 heads, same chunk) hit distinct banks.
+    for (int ii = wv * 2 * R; ii < (wv + 1) * 2 * R; ii++) {
+      const int rr = ii >> 4;
+      const int s16 = (ii & 15) * 64 + lane;
+      const int h = s16 >> 4, cpos = s16 & 15;
+      const int ch = cpos ^ (h & 15);
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)(row0 + rr) * H * D + h * D) * 2 + ch * 16;
+      dma16(src, lds0 + L_Q + rr * (H * D * 2) + (ii & 15) * 1024);
+    }
+    {
+      const int rr = wv % R;
+      if (lane < 8)
+        dma16(reinterpret_cast<const uint8_t*>(a.w) + (int64_t)(row0 + rr) * H * 2 + lane * 16, lds0 + L_W + rr * (H * 2));
+    }
+  }
+  // n_keys of the group's rows and the chunk's page ids of every row, in one load
+  // (lanes [0, R): n_keys; lanes [8, 8 + R*P): page_table[row][c*P + j])
+  int ld_lane = 0;
+  if (lane < R) {
+    ld_lane = a.nk[row0 + lane];
+  } else if (do_score && lane >= 8 && lane < 8 + R * P) {
+    const int i = (lane - 8) / P, j = (lane - 8) % P;
+    if (c * P + j < a.max_pages) ld_lane = a.pt[(int64_t)(row0 + i) * a.max_pages + c * P + j];
+  }
+  wait_vmcnt<0>();
+
+  int n[GR];
+  int nmax = 0, rmax = 0;
+  uint32_t err = 0;
+#pragma unroll
+  for (int i = 0; i < GR; i++) {
+    int v = 0;
+    if (i < R) {
+      v = __builtin_amdgcn_readlane(ld_lane, i);
+      if (v < 0 || v > gbound) {
+        err |= IDX_DERR_NKEYS;
+        v = v < 0 ? 0 : gbound;
+      }
+    }
+    n[i] = v;
+    if (v > nmax) { nmax = v; rmax = i; }
+  }
+  if (err && tid == 0) raise_error(ws, err);
+  const bool do_select = (a.mode & MODE_SELECT) != 0;
+  if (nmax == 0) {                                // every row of the group is empty
+    if (c == 0 && do_select)
+      for (int i = 0; i < R; i++)
+        for (int p = tid; p < a.k; p += NT) a.topk[(int64_t)(row0 + i) * a.k + p] = -1;
+    return;
+  }
+  if (chunk_base >= nmax) return;                 // nothing of this group here
+  const int wact = (nmax + C - 1) / C;            // chunks holding keys of this group
+  float* const sc_lds = LDS_PTR(float, L_SC);
+  const int k = a.k;
+
+  // epochs of the rows this group selects (tags of this call's hand-off words)
+  uint32_t* const epochs = reinterpret_cast<uint32_t*>(ws + a.off_epoch);
+  uint64_t* const meta = reinterpret_cast<uint64_t*>(ws + a.off_meta);
+  uint32_t* const twv = reinterpret_cast<uint32_t*>(ws + a.off_tw);
+  uint64_t* const ent = reinterpret_cast<uint64_t*>(ws + a.off_ent);
+
+  if (do_score) {
+    // ---------------- pages of this chunk, walked through the longest row's table ----
+    int phys[P];
+    uint32_t perr = 0;
+#pragma unroll
+    for (int j = 0; j < P; j++) {
+      int ph = __builtin_amdgcn_readlane(ld_lane, 8 + rmax * P + j);
+      if ((c * P + j) * PS < nmax) {
+        if (ph < 0 || ph >= a.num_pages) { perr = IDX_DERR_PAGE; ph = 0; }
+      } else {
+        ph = (j == 0) ? 0 : phys[0];
+      }
+      phys[j] = ph;
+    }
+    if (perr && tid == 0) raise_error(ws, perr);
+
+    // waves per row: 8 / R (R = 3 leaves two waves without tiles)
+    const int parts = (R == 1) ? 8 : (R == 2) ? 4 : 2;
+    const int lr = wv % R;
+    const int part = wv / R;
+    const bool mma_wave = part < parts;
+
+    // ---------------- every page's DMA into LDS: 2 per page per wave ---------------
+    // Key kn of a page occupies 8 16-byte chunks; chunk ch is stored at position
+    // ch ^ ((kn >> 1) & 7) so that the B reads below hit distinct banks.
+#pragma unroll
+    for (int j = 0; j < P; j++) {
+      const uint8_t* pg = a.kc + (int64_t)phys[j] * (PS * D);
+      const int kn = tid >> 3, cs = tid & 7;
+      const int ch = cs ^ ((kn >> 1) & 7);
+      dma16(pg + kn * D + ch * 16, lds0 + L_KEYS + j * (PS * D) + wv * 1024);
+      if (lane < 2) dma16(a.ks + (int64_t)phys[j] * PS + wv * 8 + lane * 4, lds0 + L_KSC + j * (PS * 4) + wv * 32);
+    }
+    // the queries and head weights landed before the page DMAs were issued
+    __syncthreads();
+
+    // ---------------- A operands: the row's bf16 query, straight from LDS --------------
+    // bf16 MFMA 32x32x16: lane l supplies row l % 32 and 8 consecutive k of its half
+    // l / 32.  K step s of half g covers d = 64 g + 8 s .. +8 (the same d mapping is
+    // used for the keys), M tile mt covers heads 32 mt .. +32.
+    const int g2 = lane >> 5;
+    v8bf aq[2][8];
+    float wr[2][16];
+    if (mma_wave) {
+      const uint8_t* qrow = smem + L_Q + lr * (H * D * 2);
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++) {
+        const int h = mt * 32 + (lane & 31);
+#pragma unroll
+        for (int st = 0; st < 8; st++) {
+          const v4i x = *reinterpret_cast<const v4i*>(qrow + h * (D * 2) + (((g2 * 8 + st) ^ (h & 15)) << 4));
+          aq[mt][st] = __builtin_bit_cast(v8bf, x);
+        }
+      }
+      const uint16_t* wl = LDS_PTR(const uint16_t, L_W) + lr * H;
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+          wr[mt][i] = __uint_as_float(((uint32_t)wl[mt * 32 + (i >> 2) * 8 + g2 * 4 + (i & 3)]) << 16);
+    }
+
+    // ---------------- pages: wait, then MFMA + epilogue ---------------------------
+    const float* ksl = LDS_PTR(float, L_KSC);
+#pragma unroll
+    for (int j = 0; j < P; j++) {
+      // each page was issued as 2 DMA instructions per wave, in page order
+      switch (P - 1 - j) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<2>(); break;
+        case 2: wait_vmcnt<4>(); break;
+        case 3: wait_vmcnt<6>(); break;
+        case 4: wait_vmcnt<8>(); break;
+        case 5: wait_vmcnt<10>(); break;
+        case 6: wait_vmcnt<12>(); break;
+        default: wait_vmcnt<14>(); break;
+      }
+      __syncthreads();
+      if (mma_wave && (c * P + j) * PS < nmax) {
+#pragma unroll
+        for (int tt = 0; tt < 2; tt++) {
+          const int t = 2 * j + tt;
+          if ((t % parts) != part) continue;
+          const int kn = tt * 32 + (lane & 31);
+          const uint8_t* kb = smem + L_KEYS + j * (PS * D) + kn * D;
+          const int swz = (kn >> 1) & 7;
+          uint32_t kw[16];
+#pragma unroll
+          for (int cc = 0; cc < 4; cc++) {
+            const v4i x = *reinterpret_cast<const v4i*>(kb + (((4 * g2 + cc) ^ swz) << 4));
+            kw[4 * cc + 0] = (uint32_t)x[0];
+            kw[4 * cc + 1] = (uint32_t)x[1];
+            kw[4 * cc + 2] = (uint32_t)x[2];
+            kw[4 * cc + 3] = (uint32_t)x[3];
+          }
+          v16f acc0 = {}, acc1 = {};
+#pragma unroll
+          for (int st = 0; st < 8; st++) {
+            // 8 E4M3 codes of d = 64 g + 8 st .. +8, widened exactly to bf16
+            const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st], 1.0f, false);
+            const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st], 1.0f, true);
+            const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st + 1], 1.0f, false);
+            const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st + 1], 1.0f, true);
+            const v8bf b = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0][st], b, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[1][st], b, acc1, 0, 0, 0);
+          }
+          float sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; i++) sum = fmaf(wr[0][i], fmaxf(acc0[i], 0.f), sum);
+#pragma unroll
+          for (int i = 0; i < 16; i++) sum = fmaf(wr[1][i], fmaxf(acc1[i], 0.f), sum);
+          sum += __shfl_xor(sum, 32);
+          const float score = sum * ksl[j * PS + kn] + 0.0f;
+          if (lane < 32) sc_lds[lr * CMAX + t * 32 + lane] = score;
+        }
+      }
+    }
+    __syncthreads();
+    // ---------------- scores out (write-through, they may be re-read by a finisher)
+#pragma unroll
+    for (int i = 0; i < GR; i++) {
+      if (i >= R) break;
+      const int nv = n[i] - chunk_base;
+      float* dst = a.scores + (int64_t)(row0 + i) * a.ld + chunk_base;
+      __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, (int64_t)(nv > 0 ? (nv < C ? nv : C) : 0) * 4);
+      for (int p = tid; p < C; p += NT)
+        if (p < nv)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_lds[i * CMAX + p]), rs, p * 4, 0, CP_COHERENT);
+    }
+  } else {
+    // ---------------- given scores into LDS -------------------------------------
+#pragma unroll
+    for (int i = 0; i < GR; i++) {
+      if (i >= R) break;
+      const int nv = n[i] - chunk_base;
+      const float* src = a.scores + (int64_t)(row0 + i) * a.ld + chunk_base;
+      for (int p = tid; p < C; p += NT) sc_lds[i * CMAX + p] = (p < nv) ? src[p] : 0.f;
+    }
+    __syncthreads();
+  }
+
+  if (!do_select) return;
+
+  // ---------------- publish candidates (wave i handles row i) -----------------------
+  const bool given = !do_score;
+  uint32_t tag[GR];
+#pragma unroll
+  for (int i = 0; i < GR; i++) tag[i] = (i < R) ? ld_co32(epochs + row0 + i) + 1u : 0u;
+  int* misc = LDS_PTR(int, L_MISC);
+  const bool skip_me = (c == a.skip_chunk);
+
+  if (wv < R) {
+    const int i = wv;
+    const int nr = n[i];
+    const bool all_mode = nr <= ALL_MAX;
+    const bool publish = nr > k && !(all_mode && given);
+    uint32_t cw = 0;
+    if (publish && !all_mode && !skip_me) {
+      const int grow = row0 + i;
+      int m, cap;
+      candidate_params(nr, C, k, &m, &cap);
+      const int nv = nr - chunk_base;
+      uint32_t key[8];
+      uint32_t lmax = 0;
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int p = lane * 8 + j;
+        key[j] = (p < nv && p < C) ? radix_key(sc_lds[i * CMAX + p]) : 0u;
+        lmax = lmax > key[j] ? lmax : key[j];
+      }
+      const uint32_t thr = wave_kth_largest(lmax, m);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < 8; j++) cnt += (key[j] != 0u && key[j] >= thr) ? 1 : 0;
+      const int incl = wave_incl_scan(cnt);
+      const int total = __shfl(incl, 63);
+      if (total > cap) {
+        cw = 1u << 16;  // overflow: nothing published, the finisher re-reads this chunk
+      } else {
+        int o = incl - cnt;
+        uint64_t* dst = ent + (int64_t)grow * CAP_MAX * a.meta_stride + c;
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+          if (key[j] != 0u && key[j] >= thr) {
+            st_co64(dst + (int64_t)o * a.meta_stride,
+                    ((uint64_t)key[j] << 32) | (uint32_t)(chunk_base + lane * 8 + j));
+            o++;
+          }
+        cw = (uint32_t)total;
+      }
+      if (lane == 0) st_co32(twv + (int64_t)grow * a.meta_stride + c, thr);
+    }
+    if (lane == 0) misc[32 + i] = (int)cw;
+  }
+  // every wave's score and candidate stores are complete before any arrival word
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (wv < R && lane == 0 && !skip_me) {
+    const int i = wv;
+    const int nr = n[i];
+    const bool all_mode = nr <= ALL_MAX;
+    if (nr > k && !(all_mode && given))
+      st_co64(meta + (int64_t)(row0 + i) * a.meta_stride + c, ((uint64_t)tag[i] << 32) | (uint32_t)misc[32 + i]);
+  }
+  __syncthreads();
+
+  // ---------------- finish the rows this chunk is designated for ---------------------
+  const int spin_limit = a.spin_limit > 0 ? a.spin_limit : DEFAULT_SPIN;
+  uint32_t* hist = LDS_PTR(uint32_t, L_HIST);
+  uint32_t* FK = LDS_PTR(uint32_t, L_FK);
+  uint32_t* FP = LDS_PTR(uint32_t, L_FP);
+  uint32_t* bm = LDS_PTR(uint32_t, L_BM);
+  for (int i = 0; i < R; i++) {
+    const int fin = wact - 1 - (i % wact);
+    if (c != fin) continue;
+    const int grow = row0 + i;
+    const int nr = n[i];
+    int32_t* out = a.topk + (int64_t)grow * k;
+    if (nr <= k) {
+      for (int p = tid; p < k; p += NT) out[p] = p < nr ? p : -1;
+      continue;
+    }
+    const bool all_mode = nr <= ALL_MAX;
+    const bool waits = !(all_mode && given);
+    const float* srow = a.scores + (int64_t)grow * a.ld;
+    __amdgpu_buffer_rsrc_t rs = make_rsrc(srow, (int64_t)nr * 4);
+    const uint64_t* mrow = meta + (int64_t)grow * a.meta_stride;
+    __amdgpu_buffer_rsrc_t rmeta = make_rsrc(mrow, (int64_t)wact * 8);
+    __amdgpu_buffer_rsrc_t rtw = make_rsrc(twv + (int64_t)grow * a.meta_stride, (int64_t)wact * 4);
+    __amdgpu_buffer_rsrc_t rent =
+        make_rsrc(ent + (int64_t)grow * CAP_MAX * a.meta_stride, (int64_t)CAP_MAX * a.meta_stride * 8);
+    // ---- wait for every chunk's arrival word
+    bool ok = true;
+    if (waits) {
+      int spins = 0;
+      while (true) {
+        bool mine = true;
+        for (int w = tid; w < wact; w += NT) {
+          const uint32_t hi = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rmeta, w * 8 + 4, 0, CP_COHERENT);
+          mine &= hi == tag[i];
+        }
+        ok = __syncthreads_and(mine) != 0;
+        if (ok || ++spins >= spin_limit) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    if (!ok) {
+      if (tid == 0) raise_error(ws, IDX_DERR_TIMEOUT);
+      for (int p = tid; p < k; p += NT) out[p] = -1;
+    } else {
+      bool done = false;
+      if (all_mode) {
+        // ---- every score of the row into LDS (positions implicit)
+        for (int base = 0; base < nr; base += NT * 16) {
+          uint32_t v[16];
+#pragma unroll
+          for (int j = 0; j < 16; j++)
+            v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (base + j * NT + tid) * 4, 0, CP_COHERENT);
+#pragma unroll
+          for (int j = 0; j < 16; j++) {
+            const int p = base + j * NT + tid;
+            if (p < nr) FK[p] = radix_key(__uint_as_float(v[j]));
+          }
+        }
+        __syncthreads();
+        int rem, ceq;
+        const uint32_t T = block_kth_lds(FK, nr, k, hist, misc, &rem, &ceq);
+        const int got = bitmap_emit(FK, nullptr, nr, nr, T, rem, ceq, bm, misc, out, k);
+        if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
+        done = true;
+      } else if (nr <= BITMAP_KEYS && wact <= 4 * NT) {
+        // ---- candidate counts (chunk w = tid + NT*u), thresholds, offsets
+        int cnt[4], offv[4];
+        uint32_t tw[4];
+        bool ov[4];
+        int E = 0;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const int w = tid + NT * u;
+          uint32_t cwv = 0, t = 0;
+          if (w < wact) {
+            cwv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rmeta, w * 8, 0, CP_COHERENT);
+            t = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rtw, w * 4, 0, CP_COHERENT);
+          }
+          ov[u] = (cwv >> 16) & 1u;
+          cnt[u] = ov[u] ? 0 : (int)(cwv & 0xFFFFu);
+          tw[u] = t;
+          int tot;
+          offv[u] = E + block_excl_scan(cnt[u], misc, &tot);
+          E += tot;
+        }
+        if (E <= FIN_ENT) {
+          // ---- gather every candidate, LOAD_BATCH loads in flight per thread
+#pragma unroll
+          for (int u = 0; u < 4; u++) {
+            const int w = tid + NT * u;
+            if (w < wact) {
+              for (int j0 = 0; j0 < cnt[u]; j0 += LOAD_BATCH) {
+                v2i_t v[LOAD_BATCH];
+#pragma unroll
+                for (int j = 0; j < LOAD_BATCH; j++)
+                  v[j] = (j0 + j < cnt[u])
+                             ? __builtin_amdgcn_raw_buffer_load_b64(rent, ((j0 + j) * a.meta_stride + w) * 8, 0, CP_COHERENT)
+                             : v2i_t{0, 0};
+#pragma unroll
+                for (int j = 0; j < LOAD_BATCH; j++)
+                  if (j0 + j < cnt[u]) {
+                    FK[offv[u] + j0 + j] = (uint32_t)v[j][1];
+                    FP[offv[u] + j0 + j] = (uint32_t)v[j][0];
+                  }
+              }
+            }
+          }
+          __syncthreads();
+          int rem = 0, ceq = 0;
+          uint32_t T = 0;
+          if (E >= k) T = block_kth_lds(FK, E, k, hist, misc, &rem, &ceq);
+          // ---- certificate: a chunk whose local threshold is above T may hold unseen
+          // keys >= T; list such chunks (with the threshold below which nothing was
+          // published) in the bitmap area, which is free until the emission
+          int nfail = 0;
+          {
+            int myfail[4];
+            int base = 0;
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+              const int w = tid + NT * u;
+              const bool fail = (w < wact) && ((E < k) || ov[u] || tw[u] > T);
+              int tot;
+              myfail[u] = base + block_excl_scan(fail ? 1 : 0, misc, &tot);
+              if (fail) {
+                bm[2 * myfail[u]] = (uint32_t)w;
+                bm[2 * myfail[u] + 1] = ov[u] ? 0xFFFFFFFFu : tw[u];
+              }
+              base += tot;
+            }
+            nfail = base;
+            __syncthreads();
+          }
+          if (nfail > 0) {
+            // ---- re-read failing chunks: add their keys >= T that were not published
+            const uint32_t lowT = (E >= k) ? T : 0u;
+            int Ecur = E;
+            bool overflow = false;
+            for (int f = 0; f < nfail && !overflow; f++) {
+              const uint32_t w = bm[2 * f];
+              const uint32_t twf = bm[2 * f + 1];
+              const int p0 = (int)w * C;
+              for (int base = 0; base < C; base += NT) {
+                const int p = p0 + base + tid;
+                bool take = false;
+                uint32_t key = 0;
+                if (base + tid < C && p < nr) {
+                  key = radix_key(__uint_as_float(
+                      (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, p * 4, 0, CP_COHERENT)));
+                  take = key >= lowT && (twf == 0xFFFFFFFFu || key < twf);
+                }
+                int tot;
+                const int o = block_excl_scan(take ? 1 : 0, misc, &tot);
+                if (Ecur + tot > FIN_ENT) { overflow = true; break; }
+                if (take) { FK[Ecur + o] = key; FP[Ecur + o] = (uint32_t)p; }
+                Ecur += tot;
+              }
+            }
+            __syncthreads();
+            if (!overflow && Ecur >= k) {
+              T = block_kth_lds(FK, Ecur, k, hist, misc, &rem, &ceq);
+              E = Ecur;
+              nfail = 0;
+            }
+          }
+          if (nfail == 0) {
+            const int got = bitmap_emit(FK, FP, E, nr, T, rem, ceq, bm, misc, out, k);
+            if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
+            done = true;
+          }
+        }
+      }
+      if (!done) {
+        __syncthreads();
+        global_select_row(srow, nr, k, out, hist, misc);
+      }
+    }
+    __syncthreads();
+    // a fresh tag for the next call on this row (also after a timeout, so that
+    // late arrival words of this call can never pass for the next call's)
+    if (waits && tid == 0) st_co32(epochs + grow, tag[i]);
+  }
+}
+
+__global__ void fill_kernel(uint32_t* p, int64_t words, uint32_t magic) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < words) p[i] = (i == 0) ? magic : 0u;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+thread_local char g_hip_err[256] = "";
+int g_spin_limit = 0;
+int g_skip_chunk = -1;
+bool g_attr_done = false;
+
+int hip_fail(hipError_t e) {
+  snprintf(g_hip_err, sizeof g_hip_err, "%s", hipGetErrorString(e));
+  return IDX_EHIP;
+}
+
+struct Plan {
+  int pages_per_wg;   // P
+  int chunk;          // keys per chunk
+  int wg;             // chunks per group (grid x)
+};
+
+int pages_for(int max_keys) { return (max_keys + PS - 1) / PS; }
+
+Plan plan_score(int max_keys) {
+  const int pages = pages_for(max_keys);
+  int need = (pages + 255) / 256;
+  int P = 1;
+  while (P < need && P < PMAX) P <<= 1;
+  Plan pl;
+  pl.pages_per_wg = P;
+  pl.chunk = P * PS;
+  pl.wg = pages > 0 ? (pages + P - 1) / P : 1;
+  return pl;
+}
+
+Plan plan_topk(int max_keys) {
+  Plan pl;
+  pl.pages_per_wg = PMAX;
+  pl.chunk = CMAX;
+  pl.wg = max_keys > 0 ? (max_keys + CMAX - 1) / CMAX : 1;
+  return pl;
+}
+
+struct WsLayout {
+  uint64_t off_epoch, off_meta, off_tw, off_ent, total;
+  int meta_stride;
+};
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+WsLayout layout_for(int rows, int max_keys) {
+  const Plan a = plan_score(max_keys), b = plan_topk(max_keys);
+  const int stride = (a.wg > b.wg ? a.wg : b.wg);
+  WsLayout L;
+  L.meta_stride = stride;
+  L.off_epoch = WS_HDR;
+  L.off_meta = align256(L.off_epoch + (uint64_t)rows * 4);
+  L.off_tw = align256(L.off_meta + (uint64_t)rows * stride * 8);
+  L.off_ent = align256(L.off_tw + (uint64_t)rows * stride * 4);
+  L.total = align256(L.off_ent + (uint64_t)rows * stride * CAP_MAX * 8);
+  return L;
+}
+
+int check_ptr(const void* p, uintptr_t align) {
+  return (p != nullptr && (reinterpret_cast<uintptr_t>(p) % align) == 0) ? IDX_OK : IDX_EINVAL;
+}
+
+int validate_problem(const idx_problem* p) {
+  if (!p) return IDX_EINVAL;
+  if (p->heads != IDX_HEADS || p->dim != IDX_DIM || p->page_size != IDX_PAGE_SIZE) return IDX_EUNSUPPORTED;
+  if (p->rows < 1 || p->num_req < 1 || !p->req_indptr) return IDX_EINVAL;
+  if (p->num_req > IDX_MAX_REQ) return IDX_EUNSUPPORTED;
+  if (p->rows > (1 << 24) - 1) return IDX_EUNSUPPORTED;
+  if (p->req_indptr[0] != 0 || p->req_indptr[p->num_req] != p->rows) return IDX_EINVAL;
+  for (int j = 0; j < p->num_req; j++) {
+    const int32_t r = p->req_indptr[j + 1] - p->req_indptr[j];
+    if (r < 1) return IDX_EINVAL;
+    if (r > IDX_GROUP_ROWS) return IDX_EUNSUPPORTED;
+  }
+  if (p->num_pages < 1 || p->max_pages < 1 || p->max_keys < 0) return IDX_EINVAL;
+  if (p->req_max_keys)
+    for (int j = 0; j < p->num_req; j++)
+      if (p->req_max_keys[j] < 0 || p->req_max_keys[j] > p->max_keys) return IDX_EINVAL;
+  if ((int64_t)p->max_keys > (int64_t)p->max_pages * IDX_PAGE_SIZE) return IDX_EINVAL;
+  if (p->max_keys > (1 << 30)) return IDX_EUNSUPPORTED;
+  if (check_ptr(p->q, 16) || check_ptr(p->w, 4) || check_ptr(p->k_cache, 16) || check_ptr(p->k_scale, 16) ||
+      check_ptr(p->page_table, 4) || check_ptr(p->n_keys, 4))
+    return IDX_EINVAL;
+  return IDX_OK;
+}
+
+int set_attrs() {
+  if (g_attr_done) return IDX_OK;
+  hipError_t e;
+  if ((e = hipFuncSetAttribute((const void*)idx_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES)) != hipSuccess) return hip_fail(e);
+  if ((e = hipFuncSetAttribute((const void*)idx_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES)) != hipSuccess) return hip_fail(e);
+  if ((e = hipFuncSetAttribute((const void*)idx_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES)) != hipSuccess) return hip_fail(e);
+  if ((e = hipFuncSetAttribute((const void*)idx_kernel<8>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES)) != hipSuccess) return hip_fail(e);
+  g_attr_done = true;
+  return IDX_OK;
+}
+
+int launch(const KArgs& args, int P, dim3 grid, hipStream_t st) {
+  int rc = set_attrs();
+  if (rc) return rc;
+  switch (P) {
+    case 1: hipLaunchKernelGGL(idx_kernel<1>, grid, dim3(NT), LDS_BYTES, st, args); break;
+    case 2: hipLaunchKernelGGL(idx_kernel<2>, grid, dim3(NT), LDS_BYTES, st, args); break;
+    case 4: hipLaunchKernelGGL(idx_kernel<4>, grid, dim3(NT), LDS_BYTES, st, args); break;
+    default: hipLaunchKernelGGL(idx_kernel<8>, grid, dim3(NT), LDS_BYTES, st, args); break;
+  }
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? IDX_OK : hip_fail(e);
+}
+
+void fill_common(KArgs& args, const WsLayout& L, void* ws, size_t ws_bytes) {
+  args.ws = static_cast<uint8_t*>(ws);
+  args.ws_bytes = (int64_t)ws_bytes;
+  args.spin_limit = g_spin_limit;
+  args.skip_chunk = g_skip_chunk;
+  args.meta_stride = L.meta_stride;
+  args.off_epoch = L.off_epoch;
+  args.off_meta = L.off_meta;
+  args.off_tw = L.off_tw;
+  args.off_ent = L.off_ent;
+}
+
+int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int32_t* topk, void* ws,
+                size_t ws_bytes, void* stream, int mode) {
+  int rc = validate_problem(p);
+  if (rc) return rc;
+  if (!scores || ld < 1 || ld < (int64_t)p->max_keys) return IDX_EINVAL;
+  if ((int64_t)p->rows > INT64_MAX / ld) return IDX_EINVAL;
+  if (mode & MODE_SELECT) {
+    if (k < 1 || k > IDX_KMAX || !topk) return IDX_EINVAL;
+  } else {
+    k = 1;
+  }
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return IDX_EWORKSPACE;
+  const WsLayout L = layout_for(p->rows, p->max_keys);
+  if (ws_bytes < L.total) return IDX_EWORKSPACE;
+  const Plan pl = plan_score(p->max_keys);
+  KArgs args;
+  memset(&args, 0, sizeof args);
+  args.q = static_cast<const uint32_t*>(p->q);
+  args.w = static_cast<const uint16_t*>(p->w);
+  args.kc = p->k_cache;
+  args.ks = p->k_scale;
+  args.pt = p->page_table;
+  args.nk = p->n_keys;
+  args.scores = scores;
+  args.topk = topk;
+  args.ld = ld;
+  args.rows = p->rows;
+  args.max_pages = p->max_pages;
+  args.max_keys = p->max_keys;
+  args.num_pages = p->num_pages;
+  args.k = k;
+  args.chunk = pl.chunk;
+  args.mode = mode;
+  fill_common(args, L, ws, ws_bytes);
+  for (int j = 0; j < p->num_req; j++) {
+    args.grp[j] = (uint32_t)p->req_indptr[j] | ((uint32_t)(p->req_indptr[j + 1] - p->req_indptr[j]) << 24);
+    const int bound = p->req_max_keys ? p->req_max_keys[j] : p->max_keys;
+    args.gmax[j] = bound;
+  }
+  return launch(args, pl.pages_per_wg, dim3(pl.wg, p->num_req), static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int idx_abi_version(void) { return IDX_ABI_VERSION; }
+
+int idx_workspace_bytes(int32_t rows, int32_t max_keys, int32_t k, size_t* bytes) {
+  if (!bytes || rows < 1 || rows > (1 << 24) - 1 || max_keys < 0 || max_keys > (1 << 30) || k < 1 || k > IDX_KMAX)
+    return IDX_EINVAL;
+  *bytes = (size_t)layout_for(rows, max_keys).total;
+  return IDX_OK;
+}
+
+int idx_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255) || ws_bytes < WS_HDR || (ws_bytes & 255)) return IDX_EINVAL;
+  const int64_t words = (int64_t)(ws_bytes / 4);
+  const int blocks = (int)((words + 255) / 256);
+  hipLaunchKernelGGL(fill_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint32_t*>(ws), words, WS_MAGIC);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? IDX_OK : hip_fail(e);
+}
+
+int idx_score(const idx_problem* p, float* scores, int64_t ld_scores, void* ws, size_t ws_bytes, void* stream) {
+  return run_problem(p, 1, scores, ld_scores, nullptr, ws, ws_bytes, stream, MODE_SCORE);
+}
+
+int idx_score_topk(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores, int32_t* topk, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return run_problem(p, k, scores, ld_scores, topk, ws, ws_bytes, stream, MODE_SCORE | MODE_SELECT);
+}
+
+int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys, int32_t rows, int32_t max_keys,
+             int32_t k, int32_t* topk, void* ws, size_t ws_bytes, void* stream) {
+  if (!scores || !n_keys || !topk || rows < 1 || rows > (1 << 24) - 1 || max_keys < 0 || max_keys > (1 << 30))
+    return IDX_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(scores) & 3) || (reinterpret_cast<uintptr_t>(n_keys) & 3)) return IDX_EINVAL;
+  if (ld_scores < 1 || ld_scores < (int64_t)max_keys || (int64_t)rows > INT64_MAX / ld_scores) return IDX_EINVAL;
+  if (k < 1 || k > IDX_KMAX) return IDX_EINVAL;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return IDX_EWORKSPACE;
+  const WsLayout L = layout_for(rows, max_keys);
+  if (ws_bytes < L.total) return IDX_EWORKSPACE;
+  const Plan pl = plan_topk(max_keys);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // rows in groups of up to IDX_GROUP_ROWS, at most IDX_MAX_REQ groups per launch
+  const int per_launch = IDX_MAX_REQ * IDX_GROUP_ROWS;
+  for (int r0 = 0; r0 < rows; r0 += per_launch) {
+    const int rn = (rows - r0) < per_launch ? (rows - r0) : per_launch;
+    const int groups = (rn + IDX_GROUP_ROWS - 1) / IDX_GROUP_ROWS;
+    KArgs args;
+    memset(&args, 0, sizeof args);
+    args.nk = n_keys;
+    args.scores = const_cast<float*>(scores);
+    args.topk = topk;
+    args.ld = ld_scores;
+    args.rows = rows;
+    args.max_keys = max_keys;
+    args.k = k;
+    args.chunk = pl.chunk;
+    args.mode = MODE_SELECT;
+    fill_common(args, L, ws, ws_bytes);
+    for (int gi = 0; gi < groups; gi++) {
+      const int a0 = r0 + gi * IDX_GROUP_ROWS;
+      const int an = (rows - a0) < IDX_GROUP_ROWS ? (rows - a0) : IDX_GROUP_ROWS;
+      args.grp[gi] = (uint32_t)a0 | ((uint32_t)an << 24);
+      args.gmax[gi] = max_keys;
+    }
+    int rc = launch(args, pl.pages_per_wg, dim3(pl.wg, groups), st);
+    if (rc) return rc;
+  }
+  return IDX_OK;
+}
+
+int idx_device_status(void* ws, size_t ws_bytes, void* stream, uint32_t* detail) {
+  if (!ws || ws_bytes < WS_HDR) return IDX_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e);
+  uint32_t hdr[2] = {0, 0};
+  e = hipMemcpy(hdr, ws, sizeof hdr, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e);
+  const uint32_t err = (hdr[0] != WS_MAGIC) ? (hdr[1] | IDX_DERR_WS) : hdr[1];
+  if (detail) *detail = err;
+  if (err) {
+    uint32_t zero = 0;
+    e = hipMemcpy(static_cast<uint8_t*>(ws) + WS_ERR_OFF, &zero, 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e);
+    return IDX_EDEVICE;
+  }
+  return IDX_OK;
+}
+
+const char* idx_strerror(int code) {
+  switch (code) {
+    case IDX_OK: return "ok";
+    case IDX_EINVAL: return "invalid argument";
+    case IDX_EUNSUPPORTED: return "unsupported shape (heads, dim, page size, rows per request or request count)";
+    case IDX_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case IDX_EHIP: return "HIP runtime error";
+    case IDX_EDEVICE: return "device-side error recorded in the workspace";
+    default: return "unknown error code";
+  }
+}
+
+const char* idx_last_hip_error(void) { return g_hip_err; }
+
+int idx_debug_set(int32_t key, int32_t value) {
+  if (key == 1 && value >= 0) { g_spin_limit = value; return IDX_OK; }
+  if (key == 2 && value >= -1) { g_skip_chunk = value; return IDX_OK; }
+  return IDX_EINVAL;
+}
+
+}  // extern "C"

@@ -116,7 +116,7 @@ def make_problem(contexts: Sequence[int], rows_per_req: Sequence[int], *, seed: 
     w = bf16_bits((rng.standard_normal((rows, heads), dtype=np.float32) / np.float32(8.0)).astype(np.float32))
 
     req_pages = [(c + page - 1) // page for c in contexts]
-    total_pages = sum(req_pages) + pad_pages
+    total_pages = max(1, sum(req_pages) + pad_pages)   # an empty pool still holds one page
     k_cache = np.zeros((total_pages, page, dim), dtype=np.uint8)
     k_scale = np.zeros((total_pages, page), dtype=np.float32)
 
