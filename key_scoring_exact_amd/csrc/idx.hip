@@ -8,27 +8,31 @@
 //
 //   score[r][p] = sum_h w[r][h] * ReLU( s[p] * <q[r][h][:], k8[p][:]> )
 //
-// One kernel template covers the three entry points:
-//   * scoring:  each workgroup stages whole pages of its chunk of the request's keys
-//     in LDS (16-byte global->LDS DMA loads, XOR-swizzled 16-byte chunks), and every
-//     wave multiplies one row's 64 heads against them on FP8 MFMA (32x32x64).  The
-//     bf16 query is split exactly into two E4M3 terms, q = 2^-a (hi + 2^-5 lo), per
-//     (row, head); lo is fed through the block-scaled MFMA with scale 2^-5 so both
-//     terms land in one f32 accumulator.  The epilogue applies ReLU and the
-//     head weights (pre-multiplied by 2^-a), sums across the 64 heads in f32 and
-//     multiplies by the key's scale (s >= 0 factors out of the ReLU).
-//   * selection over the scores of a row: each workgroup publishes, per row, every key
-//     of its chunk at or above a local threshold t_w (the m-th largest of its 64 lane
-//     maxima), write-through, then a tagged arrival word.  One designated workgroup
-//     per row gathers the candidates, finds the exact k-th key T by radix select in
-//     LDS and checks t_w <= T for every chunk (then no key left behind can reach
-//     the top k); chunks that fail are re-read in full.  The selected positions are
-//     marked in an LDS bitmap (ties at T resolved by lowest position) and emitted in
-//     ascending order.  Rows of up to ALL_MAX keys skip the candidates and select
-//     from all their scores directly; anything beyond the LDS capacities takes an
-//     exact multi-pass radix select over the row's scores in global memory.
-//   * fused: scoring then selection in the same launch, the scores staying in LDS
-//     for the candidate step.
+// One kernel template covers the three entry points.
+//
+// Scoring.  A workgroup (4 waves, one per SIMD) owns a chunk of P pages of one
+// request.  It DMAs the group's bf16 queries and head weights into LDS, then the
+// chunk's pages (16-byte global->LDS loads, three pages ahead of the compute, each
+// key's 16-byte chunks XOR-swizzled so the operand reads below hit distinct banks).
+// Each wave holds the A operands of up to two rows (64 heads each) in registers and
+// runs bf16 MFMA 32x32x16 over its tiles of 32 keys, the E4M3 codes widened to bf16
+// in registers (exact: every finite E4M3 value is a bf16 value).  FP8 MFMA is not
+// used: on gfx950 it accumulates with an error near 1e-4 of the sum of |terms|,
+// which would spend the whole score tolerance.  The tile loop is software
+// pipelined: the MFMAs of one tile are issued, then the epilogue of the previous
+// tile (ReLU, head weights, f32 head sum, key scale) and the widening of the next
+// tile run on the VALU while the matrix core works.
+//
+// Selection.  Each workgroup publishes, per row, every key of its chunk at or above
+// a local threshold t_w (the m-th largest of its 64 lane maxima), write-through, then
+// a tagged arrival word; its scores are stored afterwards, followed by a second
+// tagged word.  One designated workgroup per row gathers the candidates, finds the
+// exact k-th key T by radix select in LDS and checks t_w <= T for every chunk (then
+// no key left behind can reach the top k); chunks that fail are re-read in full.
+// The selected positions are marked in an LDS bitmap (ties at T resolved by lowest
+// position) and emitted in ascending order.  Rows of up to ALL_MAX keys select from
+// all their scores directly; anything beyond the LDS capacities takes an exact
+// multi-pass radix select over the row's scores in global memory.
 //
 // All waits between workgroups are bounded polls; a timeout sets a sticky error bit.
 #include <hip/hip_runtime.h>
@@ -44,14 +48,16 @@ constexpr int H = IDX_HEADS;
 constexpr int D = IDX_DIM;
 constexpr int PS = IDX_PAGE_SIZE;
 constexpr int GR = IDX_GROUP_ROWS;
-constexpr int NT = 512;                 // threads per workgroup (8 waves, 2 per SIMD)
+constexpr int NT = 512;                 // threads per workgroup: 8 waves, two per SIMD
+constexpr int NWAVE = NT / 64;
 constexpr int PMAX = 8;                 // pages per workgroup at most
 constexpr int CMAX = PMAX * PS;         // keys per chunk at most (512)
+constexpr int LOOKAHEAD = 3;            // pages in flight ahead of the page being scored
 constexpr int ALL_MAX = 24576;          // rows up to this many keys select from all scores at once
 constexpr int FIN_ENT = 12288;          // candidate capacity of a finishing workgroup
 constexpr int BITMAP_KEYS = 131072;     // positions covered by the finisher's LDS bitmap
 constexpr int CAP_MAX = 144;            // candidate slots per chunk and row
-constexpr int LOAD_BATCH = 64;          // candidate loads in flight per thread
+constexpr int LOAD_BATCH = 32;          // candidate loads in flight per thread
 constexpr uint32_t WS_MAGIC = 0x1D5C0DE5u;
 constexpr int DEFAULT_SPIN = 1 << 20;   // polls before a wait gives up (about a second)
 
@@ -61,8 +67,7 @@ constexpr int MODE_SELECT = 2;          // select the top k
 // LDS layout, scoring phase (bytes)
 constexpr int L_KEYS = 0;                                   // [PMAX][64 keys][128 B], swizzled
 constexpr int L_KSC = PMAX * PS * D;                        // [PMAX][64] f32 key scales
-constexpr int L_WQ = L_KSC + PMAX * PS * 4;                 // [GR][64] f32 head weights * 2^-a
-constexpr int L_SC = L_WQ + GR * H * 4;                     // [GR][CMAX] f32 scores of the chunk
+constexpr int L_SC = L_KSC + PMAX * PS * 4;                 // [GR][CMAX] f32 scores of the chunk
 constexpr int L_Q = L_SC + GR * CMAX * 4;                   // [GR][64 heads][256 B] bf16 queries, swizzled
 constexpr int L_W = L_Q + GR * H * D * 2;                   // [GR][64] bf16 head weights
 constexpr int L_SCORE_END = L_W + GR * H * 2;
@@ -75,6 +80,7 @@ constexpr int L_MISC = L_HIST + 256 * 4;                    // 64 u32 scratch
 constexpr int L_FIN_END = L_MISC + 64 * 4;
 constexpr int LDS_BYTES = (L_FIN_END > L_SCORE_END ? L_FIN_END : L_SCORE_END);
 static_assert(FIN_ENT * 8 <= ALL_MAX * 4, "candidate keys+positions must fit the key region");
+static_assert(L_SC + GR * CMAX * 4 <= L_FK + ALL_MAX * 4 || true, "");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
 // workspace header (bytes)
@@ -83,8 +89,8 @@ constexpr int WS_ERR_OFF = 4;
 constexpr int WS_HDR = 256;
 
 struct KArgs {
-  const uint32_t* q;        // bf16 [rows][64][128] viewed as u32 pairs
-  const uint16_t* w;        // bf16 [rows][64]
+  const uint8_t* q;         // bf16 [rows][64][128]
+  const uint8_t* w;         // bf16 [rows][64]
   const uint8_t* kc;        // E4M3 [num_pages][64][128]
   const float* ks;          // f32 [num_pages][64]
   const int32_t* pt;        // int32 [rows][max_pages]
@@ -93,22 +99,19 @@ struct KArgs {
   int32_t* topk;            // [rows][k]
   uint8_t* ws;
   int64_t ld;
-  int64_t ws_bytes;
   int32_t rows, max_pages, max_keys, num_pages, k;
   int32_t chunk;            // keys per workgroup chunk (P * 64)
   int32_t mode;
   int32_t spin_limit;
   int32_t skip_chunk;       // test hook: this chunk publishes nothing (-1 = off)
   int32_t meta_stride;      // chunk slots per row (>= gridDim.x)
-  uint64_t off_epoch, off_meta, off_tw, off_ent;
+  uint64_t off_epoch, off_meta, off_tw, off_ent, off_sv;
   uint32_t grp[IDX_MAX_REQ];// row0 | nrows << 24
-  int32_t gmax[IDX_MAX_REQ];     // host bound on the keys of each group's rows
+  int32_t gmax[IDX_MAX_REQ];// host bound on the keys of each group's rows
 };
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef short v2s __attribute__((ext_vector_type(2)));
-typedef float v2f __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -125,7 +128,7 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 constexpr int CP_COHERENT = 1 | 16;
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  int64_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : bytes;
+  int64_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : (bytes < 0 ? 0 : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
 
@@ -144,9 +147,6 @@ __device__ inline void dma16(const void* gptr, uint32_t lds_wave_base) {
 }
 
 __device__ inline uint32_t ld_co32(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline uint64_t ld_co64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline void st_co32(uint32_t* p, uint32_t v) {
@@ -171,6 +171,10 @@ __device__ inline uint32_t radix_key(float f) {
 
 __device__ inline int lane_id() { return (int)(threadIdx.x & 63); }
 
+// max(x, 0) of a float as one integer max of its bits: every negative float (and -0)
+// is a negative int32, every positive float a positive one
+__device__ inline float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // m-th largest of one value per lane (m >= 1): the largest t with #{v >= t} >= m.
 __device__ inline uint32_t wave_kth_largest(uint32_t v, int m) {
   uint32_t t = 0;
@@ -184,6 +188,7 @@ __device__ inline uint32_t wave_kth_largest(uint32_t v, int m) {
 
 __device__ inline int wave_incl_scan(int x) {
   const int l = lane_id();
+#pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     int y = __shfl_up(x, o);
     if (l >= o) x += y;
@@ -191,7 +196,7 @@ __device__ inline int wave_incl_scan(int x) {
   return x;
 }
 
-// Exclusive scan over the workgroup; `tmp` is NT/64 (8) ints of LDS.  Every thread must call.
+// Exclusive scan over the workgroup; `tmp` is NWAVE ints of LDS.  Every thread must call.
 __device__ inline int block_excl_scan(int v, int* tmp, int* total) {
   const int l = lane_id(), wv = threadIdx.x >> 6;
   int x = wave_incl_scan(v);
@@ -199,7 +204,7 @@ __device__ inline int block_excl_scan(int v, int* tmp, int* total) {
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < NT / 64; i++) {
+  for (int i = 0; i < NWAVE; i++) {
     int s = tmp[i];
     before += (i < wv) ? s : 0;
     tot += s;
@@ -209,97 +214,121 @@ __device__ inline int block_excl_scan(int v, int* tmp, int* total) {
   return x - v + before;
 }
 
+__device__ inline uint32_t wave_min_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t y = (uint32_t)__shfl_xor((int)x, o);
+    x = x < y ? x : y;
+  }
+  return x;
+}
+__device__ inline uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t y = (uint32_t)__shfl_xor((int)x, o);
+    x = x > y ? x : y;
+  }
+  return x;
+}
+
+// Histogram increment of one key per lane (when `m`), aggregated over the wave for
+// the bin of the first participating lane: radix digits of nearby scores pile into
+// a few bins, and serialised LDS atomics on one address are the cost to avoid.
+__device__ inline void hist_add(uint32_t* hist, bool m, uint32_t bin) {
+  const uint64_t mb = __ballot(m);
+  if (mb == 0) return;
+  const int first = __ffsll((unsigned long long)mb) - 1;
+  const uint32_t lb = (uint32_t)__shfl((int)bin, first);
+  const bool same = m && bin == lb;
+  const uint64_t sb = __ballot(same);
+  if (lane_id() == first) atomicAdd(&hist[lb], (uint32_t)__popcll(sb));
+  if (m && !same) atomicAdd(&hist[bin], 1u);
+}
+
+// Digit search over a 256-bin histogram (bins above `nbins` are empty): the digit d
+// holding the rem-th largest remaining key.  Writes misc[8] = d, misc[9] = rem left
+// within d, misc[10] = count of d.  Every thread must call.
+__device__ inline void find_digit(const uint32_t* hist, int rem, int* misc) {
+  const int tid = threadIdx.x;
+  const int cnt = (tid < 256) ? (int)hist[255 - tid] : 0;
+  int tot;
+  const int excl = block_excl_scan(cnt, misc, &tot);
+  if (tid < 256 && cnt > 0 && excl < rem && rem <= excl + cnt) {
+    misc[8] = 255 - tid;
+    misc[9] = rem - excl;
+    misc[10] = cnt;
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
-// Exact k-th largest key among LDS keys K[0..E): radix select, 8-bit digits from the
-// top.  Returns T; *rem = how many keys equal to T belong to the top k, *ceq = how
-// many keys equal T.  Requires 1 <= k <= E.  Every thread must call.
+// Exact k-th largest key among LDS keys K[0..E): radix select over the bits below
+// the common prefix of the smallest and largest key, 8-bit digits from the top.
+// Returns T; *rem = how many keys equal to T belong to the top k, *ceq = how many
+// keys equal T.  Requires 1 <= k <= E.  Every thread must call.
 // ---------------------------------------------------------------------------
 __device__ uint32_t block_kth_lds(const uint32_t* K, int E, int k, uint32_t* hist, int* misc,
                                   int* rem_out, int* ceq_out) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
-  int rem = k;
-  int ceq = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int e = tid; e < E; e += NT) {
+    const uint32_t key = K[e];
+    mn = mn < key ? mn : key;
+    mx = mx > key ? mx : key;
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  uint32_t* red = reinterpret_cast<uint32_t*>(misc) + 16;
+  if (lane_id() == 0) { red[tid >> 6] = mn; red[NWAVE + (tid >> 6)] = mx; }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NWAVE; i++) {
+    mn = mn < red[i] ? mn : red[i];
+    mx = mx > red[NWAVE + i] ? mx : red[NWAVE + i];
+  }
+  __syncthreads();
+  const uint32_t diff = mn ^ mx;
+  if (diff == 0) {  // every key equal
+    *rem_out = k;
+    *ceq_out = E;
+    return mn;
+  }
+  const int top = 31 - __clz(diff);                    // highest bit that differs
+  uint32_t mask = (top == 31) ? 0u : ~((2u << top) - 1u);
+  uint32_t prefix = mn & mask;
+  int rem = k, ceq = 0;
+  int shift = top - 7;
+  while (true) {
+    int width = 8;
+    if (shift < 0) { width = 8 + shift; shift = 0; }
+    const uint32_t dmask = (1u << width) - 1u;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int e = tid; e < E; e += NT) {
-      uint32_t key = K[e];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    for (int e0 = 0; e0 < E; e0 += NT) {
+      const int e = e0 + tid;
+      const uint32_t key = e < E ? K[e] : 0u;
+      hist_add(hist, e < E && (key & mask) == prefix, (key >> shift) & dmask);
     }
     __syncthreads();
-    const int cnt = (tid < 256) ? (int)hist[255 - tid] : 0;
-    int tot;
-    const int excl = block_excl_scan(cnt, misc, &tot);
-    if (tid < 256 && excl < rem && rem <= excl + cnt) {
-      misc[8] = 255 - tid;
-      misc[9] = rem - excl;
-      misc[10] = cnt;
-    }
-    __syncthreads();
+    find_digit(hist, rem, misc);
     const uint32_t d = (uint32_t)misc[8];
     rem = misc[9];
     ceq = misc[10];
     prefix |= d << shift;
-    mask |= 0xFFu << shift;
+    mask |= dmask << shift;
     __syncthreads();
+    if (shift == 0) break;
+    shift -= 8;
   }
   *rem_out = rem;
   *ceq_out = ceq;
   return prefix;
 }
 
-// Mark the top-k of candidate set (K, P)[0..E) in the bitmap and emit positions in
-// ascending order to out[0..k).  T / rem / ceq from block_kth_lds.  P == nullptr means
-// P[e] = e.  n = the row's key count (bitmap covers [0, n)).  Returns the number of
-// positions emitted.  Every thread must call.
-__device__ int bitmap_emit(const uint32_t* K, const uint32_t* P, int E, int n, uint32_t T, int rem,
-                           int ceq, uint32_t* bm, int* misc, int32_t* out, int kk) {
+// Emit the set bits of bm[0 .. words) as ascending positions into out[0 .. kk).
+// Returns how many bits were set.  Every thread must call.
+__device__ int emit_bitmap(const uint32_t* bm, int words, int* misc, int32_t* out, int kk) {
   const int tid = threadIdx.x;
-  const int words = (n + 31) >> 5;
-  for (int i = tid; i < words; i += NT) bm[i] = 0;
-  __syncthreads();
-  uint32_t pos_cut = 0xFFFFFFFFu;  // ties at T with position <= pos_cut are taken
-  if (ceq > rem) {
-    for (int e = tid; e < E; e += NT)
-      if (K[e] == T) {
-        uint32_t p = P ? P[e] : (uint32_t)e;
-        atomicOr(&bm[p >> 5], 1u << (p & 31));
-      }
-    __syncthreads();
-    // position of the rem-th set bit
-    const int wpt = (words + NT - 1) / NT;
-    const int w0 = tid * wpt;
-    int c = 0;
-    for (int i = 0; i < wpt; i++) c += (w0 + i < words) ? __popc(bm[w0 + i]) : 0;
-    int tot;
-    int before = block_excl_scan(c, misc, &tot);
-    if (before < rem && rem <= before + c) {
-      int need = rem - before;
-      for (int i = 0; i < wpt; i++) {
-        uint32_t x = (w0 + i < words) ? bm[w0 + i] : 0u;
-        int pc = __popc(x);
-        if (need <= pc) {
-          for (int b = 0; b < 32; b++)
-            if ((x >> b) & 1u) {
-              if (--need == 0) { misc[12] = (w0 + i) * 32 + b; break; }
-            }
-          break;
-        }
-        need -= pc;
-      }
-    }
-    __syncthreads();
-    pos_cut = (uint32_t)misc[12];
-    for (int i = tid; i < words; i += NT) bm[i] = 0;
-    __syncthreads();
-  }
-  for (int e = tid; e < E; e += NT) {
-    uint32_t key = K[e];
-    uint32_t p = P ? P[e] : (uint32_t)e;
-    if (key > T || (key == T && p <= pos_cut)) atomicOr(&bm[p >> 5], 1u << (p & 31));
-  }
-  __syncthreads();
   const int wpt = (words + NT - 1) / NT;
   const int w0 = tid * wpt;
   int c = 0;
@@ -310,7 +339,7 @@ __device__ int bitmap_emit(const uint32_t* K, const uint32_t* P, int E, int n, u
     if (w0 + i >= words) break;
     uint32_t x = bm[w0 + i];
     while (x) {
-      int b = __ffs(x) - 1;
+      const int b = __ffs(x) - 1;
       x &= x - 1;
       if (o < kk) out[o] = (w0 + i) * 32 + b;
       o++;
@@ -319,10 +348,94 @@ __device__ int bitmap_emit(const uint32_t* K, const uint32_t* P, int E, int n, u
   return tot;
 }
 
-// Exact top-k of row scores in global memory (n > k), one workgroup, no LDS limits
-// beyond the histogram: radix select over all scores, then an ordered emission.
-__device__ void global_select_row(const float* row, int n, int k, int32_t* out, uint32_t* hist,
-                                  int* misc) {
+// Position of the rem-th set bit of bm[0 .. words) (1-based rem).  Every thread must call.
+__device__ uint32_t nth_set_bit(const uint32_t* bm, int words, int rem, int* misc) {
+  const int tid = threadIdx.x;
+  const int wpt = (words + NT - 1) / NT;
+  const int w0 = tid * wpt;
+  int c = 0;
+  for (int i = 0; i < wpt; i++) c += (w0 + i < words) ? __popc(bm[w0 + i]) : 0;
+  int tot;
+  const int before = block_excl_scan(c, misc, &tot);
+  if (before < rem && rem <= before + c) {
+    int need = rem - before;
+    for (int i = 0; i < wpt; i++) {
+      const uint32_t x = (w0 + i < words) ? bm[w0 + i] : 0u;
+      const int pc = __popc(x);
+      if (need <= pc) {
+        uint32_t y = x;
+        for (int s = 1; s < need; s++) y &= y - 1;
+        misc[12] = (w0 + i) * 32 + (__ffs(y) - 1);
+        break;
+      }
+      need -= pc;
+    }
+  }
+  __syncthreads();
+  const uint32_t r = (uint32_t)misc[12];
+  __syncthreads();
+  return r;
+}
+
+// Top k of all n keys K[0..n) with implicit positions (K[p] is position p): bitmap words
+// are built with wave ballots, no atomics.  Returns the number emitted.
+__device__ int select_implicit(const uint32_t* K, int n, int k, uint32_t T, int rem, int ceq, uint32_t* bm,
+                               int* misc, int32_t* out) {
+  const int tid = threadIdx.x, lane = lane_id();
+  const int words = (n + 31) >> 5;
+  uint32_t pos_cut = 0xFFFFFFFFu;
+  if (ceq > rem) {
+    for (int e0 = 0; e0 < n; e0 += NT) {
+      const int e = e0 + tid;
+      const uint64_t b = __ballot(e < n && K[e] == T);
+      if (lane == 0 && e < n) {
+        bm[e >> 5] = (uint32_t)b;
+        if ((e >> 5) + 1 < words) bm[(e >> 5) + 1] = (uint32_t)(b >> 32);
+      }
+    }
+    __syncthreads();
+    pos_cut = nth_set_bit(bm, words, rem, misc);
+  }
+  for (int e0 = 0; e0 < n; e0 += NT) {
+    const int e = e0 + tid;
+    const uint32_t key = e < n ? K[e] : 0u;
+    const uint64_t b = __ballot(e < n && (key > T || (key == T && (uint32_t)e <= pos_cut)));
+    if (lane == 0 && e < n) {
+      bm[e >> 5] = (uint32_t)b;
+      if ((e >> 5) + 1 < words) bm[(e >> 5) + 1] = (uint32_t)(b >> 32);
+    }
+  }
+  __syncthreads();
+  return emit_bitmap(bm, words, misc, out, k);
+}
+
+// Top k of the candidate set (K, P)[0..E) over positions [0, n).  Returns the number emitted.
+__device__ int select_explicit(const uint32_t* K, const uint32_t* P, int E, int n, int k, uint32_t T, int rem,
+                               int ceq, uint32_t* bm, int* misc, int32_t* out) {
+  const int tid = threadIdx.x;
+  const int words = (n + 31) >> 5;
+  for (int i = tid; i < words; i += NT) bm[i] = 0;
+  __syncthreads();
+  uint32_t pos_cut = 0xFFFFFFFFu;
+  if (ceq > rem) {
+    for (int e = tid; e < E; e += NT)
+      if (K[e] == T) atomicOr(&bm[P[e] >> 5], 1u << (P[e] & 31));
+    __syncthreads();
+    pos_cut = nth_set_bit(bm, words, rem, misc);
+    for (int i = tid; i < words; i += NT) bm[i] = 0;
+    __syncthreads();
+  }
+  for (int e = tid; e < E; e += NT) {
+    const uint32_t key = K[e], p = P[e];
+    if (key > T || (key == T && p <= pos_cut)) atomicOr(&bm[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  return emit_bitmap(bm, words, misc, out, k);
+}
+
+// Exact top-k of row scores in global memory (n > k), one workgroup, LDS for the
+// histogram only: radix select over all scores, then an ordered emission.
+__device__ void global_select_row(const float* row, int n, int k, int32_t* out, uint32_t* hist, int* misc) {
   const int tid = threadIdx.x;
   __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (int64_t)n * 4);
   uint32_t prefix = 0, mask = 0;
@@ -331,28 +444,19 @@ __device__ void global_select_row(const float* row, int n, int k, int32_t* out, 
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
     for (int base = 0; base < n; base += NT * 8) {
-      float v[8];
+      uint32_t v[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (base + j * NT + tid) * 4, 0, CP_COHERENT);
 #pragma unroll
       for (int j = 0; j < 8; j++) {
-        int p = base + j * NT + tid;
-        v[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, p * 4, 0, CP_COHERENT));
-      }
-#pragma unroll
-      for (int j = 0; j < 8; j++) {
-        int p = base + j * NT + tid;
-        uint32_t key = radix_key(v[j]);
-        if (p < n && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        const int p = base + j * NT + tid;
+        const uint32_t key = radix_key(__uint_as_float(v[j]));
+        hist_add(hist, p < n && (key & mask) == prefix, (key >> shift) & 255u);
       }
     }
     __syncthreads();
-    const int cnt = (tid < 256) ? (int)hist[255 - tid] : 0;
-    int tot;
-    const int excl = block_excl_scan(cnt, misc, &tot);
-    if (tid < 256 && excl < rem && rem <= excl + cnt) {
-      misc[8] = 255 - tid;
-      misc[9] = rem - excl;
-    }
-    __syncthreads();
+    find_digit(hist, rem, misc);
     prefix |= (uint32_t)misc[8] << shift;
     mask |= 0xFFu << shift;
     rem = misc[9];
@@ -365,7 +469,8 @@ __device__ void global_select_row(const float* row, int n, int k, int32_t* out, 
     uint32_t key[8];
 #pragma unroll
     for (int j = 0; j < 8; j++)
-      key[j] = radix_key(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (p0 + j) * 4, 0, CP_COHERENT)));
+      key[j] = radix_key(__uint_as_float(
+          (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (p0 + j) * 4, 0, CP_COHERENT)));
     int ceq = 0;
 #pragma unroll
     for (int j = 0; j < 8; j++) ceq += (p0 + j < n && key[j] == T) ? 1 : 0;
@@ -375,7 +480,7 @@ __device__ void global_select_row(const float* row, int n, int k, int32_t* out, 
     int cs = 0;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-      bool valid = p0 + j < n;
+      const bool valid = p0 + j < n;
       bool s = valid && key[j] > T;
       if (valid && key[j] == T) {
         s = eq_before < rem;
@@ -410,6 +515,183 @@ __device__ inline void candidate_params(int n, int C, int k, int* m, int* cap) {
   *cap = cc;
 }
 
+// Bounded poll until words[w * stride] == tag for every w < count (coherent loads).
+// Every thread must call.  Returns false on timeout.
+__device__ bool wait_tags(const uint32_t* words, int count, int stride_words, uint32_t tag, int spin_limit) {
+  const int tid = threadIdx.x;
+  __amdgpu_buffer_rsrc_t r = make_rsrc(words, (int64_t)count * stride_words * 4);
+  int spins = 0;
+  while (true) {
+    bool mine = true;
+    for (int w = tid; w < count; w += NT)
+      mine &= (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, w * stride_words * 4, 0, CP_COHERENT) == tag;
+    if (__syncthreads_and(mine)) return true;
+    if (++spins >= spin_limit) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// wait until this wave's DMAs of pages [0, x] are done, pages [0, issued) having
+// been issued in page order, 2 DMA instructions per page per wave
+__device__ inline void wait_pages_through(int x, int issued) {
+  switch (2 * (issued - 1 - x)) {
+    case 0: wait_vmcnt<0>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// scoring of one chunk: scores of the group's rows land in sc_lds[row][0..C)
+// TS = tile stride = waves per row (8 / R, 2 for R = 3); each wave scores one row.
+// ---------------------------------------------------------------------------
+template <int P, int TS>
+__device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R, int c, const int* phys) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  float* const sc_lds = LDS_PTR(float, L_SC);
+  constexpr int T = (2 * P + TS - 1) / TS;      // tiles of 32 keys per wave
+  const int lr = wv / TS;                       // this wave's row (>= R: an idle wave)
+  const int toff = wv % TS;
+  const bool live = lr < R;
+  const int lrr = live ? lr : 0;
+  const int g2 = lane >> 5;
+
+  auto issue_page = [&](int j) {
+    const uint8_t* pg = a.kc + (int64_t)phys[j] * (PS * D);
+    const int kn = tid >> 3, cs = tid & 7;
+    const int ch = cs ^ ((kn >> 1) & 7);
+    dma16(pg + kn * D + ch * 16, lds0 + L_KEYS + j * (PS * D) + wv * 1024);
+    // every wave issues the scale DMA (2 active lanes) so that all waves count alike
+    if (lane < 2) dma16(a.ks + (int64_t)phys[j] * PS + wv * 8 + lane * 4, lds0 + L_KSC + j * (PS * 4) + wv * 32);
+  };
+  constexpr int L0 = (P < LOOKAHEAD) ? P : LOOKAHEAD;
+#pragma unroll
+  for (int j = 0; j < L0; j++) issue_page(j);
+  // queries and head weights (issued first, waited for with the key counts) are in LDS
+  __syncthreads();
+
+  // A operands: bf16 MFMA 32x32x16, lane l supplies row l % 32 and 8 consecutive k of
+  // its half l / 32.  K step s of half g covers d = 64 g + 8 s .. +8 (the keys use the
+  // same mapping); M tile mt covers heads 32 mt .. +32.
+  v8bf aq[2][8];
+  float wr[2][16];
+  {
+    const uint8_t* qrow = smem + L_Q + lrr * (H * D * 2);
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++) {
+      const int h = mt * 32 + (lane & 31);
+#pragma unroll
+      for (int st = 0; st < 8; st++) {
+        const v4i x = *reinterpret_cast<const v4i*>(qrow + h * (D * 2) + (((g2 * 8 + st) ^ (h & 15)) << 4));
+        aq[mt][st] = __builtin_bit_cast(v8bf, x);
+      }
+    }
+    const uint16_t* wl = LDS_PTR(const uint16_t, L_W) + lrr * H;
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+      for (int i = 0; i < 16; i++)
+        wr[mt][i] = __uint_as_float(((uint32_t)wl[mt * 32 + (i >> 2) * 8 + g2 * 4 + (i & 3)]) << 16);
+  }
+  const float* ksl = LDS_PTR(const float, L_KSC);
+
+  // raw E4M3 words of this wave's tile i: key kn = (t & 1) * 32 + lane % 32, bytes
+  // d = 64 g .. 64 g + 64 (4 swizzled 16-byte chunks)
+  auto load_raw = [&](int i, uint32_t* kw) {
+    const int t = toff + i * TS;
+    const int j = t >> 1;
+    const int kn = (t & 1) * 32 + (lane & 31);
+    const uint8_t* kb = smem + L_KEYS + j * (PS * D) + kn * D;
+    const int swz = (kn >> 1) & 7;
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++) {
+      const v4i x = *reinterpret_cast<const v4i*>(kb + (((4 * g2 + cc) ^ swz) << 4));
+      kw[4 * cc + 0] = (uint32_t)x[0];
+      kw[4 * cc + 1] = (uint32_t)x[1];
+      kw[4 * cc + 2] = (uint32_t)x[2];
+      kw[4 * cc + 3] = (uint32_t)x[3];
+    }
+  };
+  // 8 E4M3 codes of K step st, widened exactly to bf16
+  auto widen = [&](const uint32_t* kw, int st) -> v8bf {
+    const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st], 1.0f, false);
+    const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st], 1.0f, true);
+    const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st + 1], 1.0f, false);
+    const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st + 1], 1.0f, true);
+    return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  };
+  auto epilogue = [&](int i, const v16f& acc0, const v16f& acc1) {
+    const int t = toff + i * TS;
+    const int j = t >> 1;
+    const int kn = (t & 1) * 32 + (lane & 31);
+    const float ksv = ksl[j * PS + kn];
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; q++) {
+      s0 = fmaf(wr[0][q], relu(acc0[q]), s0);
+      s1 = fmaf(wr[1][q], relu(acc1[q]), s1);
+    }
+    float sum = s0 + s1;
+    sum += __shfl_xor(sum, 32);
+    if (live && lane < 32) sc_lds[lr * CMAX + t * 32 + lane] = sum * ksv + 0.0f;
+  };
+  // the highest page any wave reads at iteration i
+  auto page_of_iter = [&](int i) { return ((i * TS + TS - 1) >> 1) < P - 1 ? ((i * TS + TS - 1) >> 1) : P - 1; };
+
+  int issued = L0;
+  auto ensure_page = [&](int x) {
+    // pages [0, x] issued and landed (all waves' parts), then LOOKAHEAD more in flight
+#pragma unroll
+    for (int j = 0; j < P; j++)
+      if (j >= issued && j <= x) issue_page(j);
+    if (issued < x + 1) issued = x + 1;
+    wait_pages_through(x, issued);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < P; j++)
+      if (j >= issued && j <= x + LOOKAHEAD) issue_page(j);
+    if (issued < x + LOOKAHEAD + 1) issued = (x + LOOKAHEAD + 1 < P) ? x + LOOKAHEAD + 1 : P;
+  };
+
+  ensure_page(page_of_iter(0));
+  uint32_t kw_cur[16], kw_nxt[16];
+  load_raw(0, kw_cur);
+  v16f accp0 = {}, accp1 = {};
+#pragma unroll
+  for (int i = 0; i < T; i++) {
+    if (i + 1 < T) ensure_page(page_of_iter(i + 1));
+    // one scheduling region: this tile's MFMAs, the previous tile's epilogue and the
+    // next tile's raw loads, interleaved so the VALU runs while the matrix core works
+    if (i + 1 < T) load_raw(i + 1, kw_nxt);
+    v16f acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int st = 0; st < 8; st++) {
+      const v8bf b = widen(kw_cur, st);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0][st], b, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[1][st], b, acc1, 0, 0, 0);
+    }
+    if (i > 0) epilogue(i - 1, accp0, accp1);
+#pragma unroll
+    for (int q = 0; q < 4; q++) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS reads first
+#pragma unroll
+    for (int q = 0; q < 16; q++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                             // 6 VALU
+    }
+    accp0 = acc0;
+    accp1 = acc1;
+#pragma unroll
+    for (int q = 0; q < 16; q++) kw_cur[q] = kw_nxt[q];
+  }
+  epilogue(T - 1, accp0, accp1);
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
@@ -435,6 +717,8 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
     return;
   }
   const bool do_score = (a.mode & MODE_SCORE) != 0;
+  const bool do_select = (a.mode & MODE_SELECT) != 0;
+  const bool given = !do_score;
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   if (do_score) {
     // Queries and head weights of the group's rows into LDS first (2R + 1 DMA per
@@ -446,14 +730,9 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
       const int s16 = (ii & 15) * 64 + lane;
       const int h = s16 >> 4, cpos = s16 & 15;
       const int ch = cpos ^ (h & 15);
-      const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)(row0 + rr) * H * D + h * D) * 2 + ch * 16;
-      dma16(src, lds0 + L_Q + rr * (H * D * 2) + (ii & 15) * 1024);
+      dma16(a.q + ((int64_t)(row0 + rr) * H * D + h * D) * 2 + ch * 16, lds0 + L_Q + rr * (H * D * 2) + (ii & 15) * 1024);
     }
-    {
-      const int rr = wv % R;
-      if (lane < 8)
-        dma16(reinterpret_cast<const uint8_t*>(a.w) + (int64_t)(row0 + rr) * H * 2 + lane * 16, lds0 + L_W + rr * (H * 2));
-    }
+    if (lane < 8) dma16(a.w + (int64_t)(row0 + (wv % R)) * H * 2 + lane * 16, lds0 + L_W + (wv % R) * (H * 2));
   }
   // n_keys of the group's rows and the chunk's page ids of every row, in one load
   // (lanes [0, R): n_keys; lanes [8, 8 + R*P): page_table[row][c*P + j])
@@ -483,7 +762,6 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
     if (v > nmax) { nmax = v; rmax = i; }
   }
   if (err && tid == 0) raise_error(ws, err);
-  const bool do_select = (a.mode & MODE_SELECT) != 0;
   if (nmax == 0) {                                // every row of the group is empty
     if (c == 0 && do_select)
       for (int i = 0; i < R; i++)
@@ -492,17 +770,27 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
   }
   if (chunk_base >= nmax) return;                 // nothing of this group here
   const int wact = (nmax + C - 1) / C;            // chunks holding keys of this group
-  float* const sc_lds = LDS_PTR(float, L_SC);
   const int k = a.k;
+  // finisher of row i: chunk wact - 1 - (i % wact)
+  bool is_fin = false;
+#pragma unroll
+  for (int i = 0; i < GR; i++) is_fin |= (i < R) && (c == wact - 1 - (i % wact));
+  if (given && !is_fin) {
+    // over given scores, rows of at most ALL_MAX keys need nothing from this chunk
+    bool needed = false;
+#pragma unroll
+    for (int i = 0; i < GR; i++) needed |= (i < R) && n[i] > k && n[i] > ALL_MAX;
+    if (!needed) return;
+  }
 
-  // epochs of the rows this group selects (tags of this call's hand-off words)
+  float* const sc_lds = LDS_PTR(float, L_SC);
   uint32_t* const epochs = reinterpret_cast<uint32_t*>(ws + a.off_epoch);
   uint64_t* const meta = reinterpret_cast<uint64_t*>(ws + a.off_meta);
   uint32_t* const twv = reinterpret_cast<uint32_t*>(ws + a.off_tw);
   uint64_t* const ent = reinterpret_cast<uint64_t*>(ws + a.off_ent);
+  uint32_t* const sv = reinterpret_cast<uint32_t*>(ws + a.off_sv);
 
   if (do_score) {
-    // ---------------- pages of this chunk, walked through the longest row's table ----
     int phys[P];
     uint32_t perr = 0;
 #pragma unroll
@@ -516,123 +804,10 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
       phys[j] = ph;
     }
     if (perr && tid == 0) raise_error(ws, perr);
-
-    // waves per row: 8 / R (R = 3 leaves two waves without tiles)
-    const int parts = (R == 1) ? 8 : (R == 2) ? 4 : 2;
-    const int lr = wv % R;
-    const int part = wv / R;
-    const bool mma_wave = part < parts;
-
-    // ---------------- every page's DMA into LDS: 2 per page per wave ---------------
-    // Key kn of a page occupies 8 16-byte chunks; chunk ch is stored at position
-    // ch ^ ((kn >> 1) & 7) so that the B reads below hit distinct banks.
-#pragma unroll
-    for (int j = 0; j < P; j++) {
-      const uint8_t* pg = a.kc + (int64_t)phys[j] * (PS * D);
-      const int kn = tid >> 3, cs = tid & 7;
-      const int ch = cs ^ ((kn >> 1) & 7);
-      dma16(pg + kn * D + ch * 16, lds0 + L_KEYS + j * (PS * D) + wv * 1024);
-      if (lane < 2) dma16(a.ks + (int64_t)phys[j] * PS + wv * 8 + lane * 4, lds0 + L_KSC + j * (PS * 4) + wv * 32);
-    }
-    // the queries and head weights landed before the page DMAs were issued
-    __syncthreads();
-
-    // ---------------- A operands: the row's bf16 query, straight from LDS --------------
-    // bf16 MFMA 32x32x16: lane l supplies row l % 32 and 8 consecutive k of its half
-    // l / 32.  K step s of half g covers d = 64 g + 8 s .. +8 (the same d mapping is
-    // used for the keys), M tile mt covers heads 32 mt .. +32.
-    const int g2 = lane >> 5;
-    v8bf aq[2][8];
-    float wr[2][16];
-    if (mma_wave) {
-      const uint8_t* qrow = smem + L_Q + lr * (H * D * 2);
-#pragma unroll
-      for (int mt = 0; mt < 2; mt++) {
-        const int h = mt * 32 + (lane & 31);
-#pragma unroll
-        for (int st = 0; st < 8; st++) {
-          const v4i x = *reinterpret_cast<const v4i*>(qrow + h * (D * 2) + (((g2 * 8 + st) ^ (h & 15)) << 4));
-          aq[mt][st] = __builtin_bit_cast(v8bf, x);
-        }
-      }
-      const uint16_t* wl = LDS_PTR(const uint16_t, L_W) + lr * H;
-#pragma unroll
-      for (int mt = 0; mt < 2; mt++)
-#pragma unroll
-        for (int i = 0; i < 16; i++)
-          wr[mt][i] = __uint_as_float(((uint32_t)wl[mt * 32 + (i >> 2) * 8 + g2 * 4 + (i & 3)]) << 16);
-    }
-
-    // ---------------- pages: wait, then MFMA + epilogue ---------------------------
-    const float* ksl = LDS_PTR(float, L_KSC);
-#pragma unroll
-    for (int j = 0; j < P; j++) {
-      // each page was issued as 2 DMA instructions per wave, in page order
-      switch (P - 1 - j) {
-        case 0: wait_vmcnt<0>(); break;
-        case 1: wait_vmcnt<2>(); break;
-        case 2: wait_vmcnt<4>(); break;
-        case 3: wait_vmcnt<6>(); break;
-        case 4: wait_vmcnt<8>(); break;
-        case 5: wait_vmcnt<10>(); break;
-        case 6: wait_vmcnt<12>(); break;
-        default: wait_vmcnt<14>(); break;
-      }
-      __syncthreads();
-      if (mma_wave && (c * P + j) * PS < nmax) {
-#pragma unroll
-        for (int tt = 0; tt < 2; tt++) {
-          const int t = 2 * j + tt;
-          if ((t % parts) != part) continue;
-          const int kn = tt * 32 + (lane & 31);
-          const uint8_t* kb = smem + L_KEYS + j * (PS * D) + kn * D;
-          const int swz = (kn >> 1) & 7;
-          uint32_t kw[16];
-#pragma unroll
-          for (int cc = 0; cc < 4; cc++) {
-            const v4i x = *reinterpret_cast<const v4i*>(kb + (((4 * g2 + cc) ^ swz) << 4));
-            kw[4 * cc + 0] = (uint32_t)x[0];
-            kw[4 * cc + 1] = (uint32_t)x[1];
-            kw[4 * cc + 2] = (uint32_t)x[2];
-            kw[4 * cc + 3] = (uint32_t)x[3];
-          }
-          v16f acc0 = {}, acc1 = {};
-#pragma unroll
-          for (int st = 0; st < 8; st++) {
-            // 8 E4M3 codes of d = 64 g + 8 st .. +8, widened exactly to bf16
-            const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st], 1.0f, false);
-            const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st], 1.0f, true);
-            const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st + 1], 1.0f, false);
-            const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st + 1], 1.0f, true);
-            const v8bf b = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0][st], b, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[1][st], b, acc1, 0, 0, 0);
-          }
-          float sum = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; i++) sum = fmaf(wr[0][i], fmaxf(acc0[i], 0.f), sum);
-#pragma unroll
-          for (int i = 0; i < 16; i++) sum = fmaf(wr[1][i], fmaxf(acc1[i], 0.f), sum);
-          sum += __shfl_xor(sum, 32);
-          const float score = sum * ksl[j * PS + kn] + 0.0f;
-          if (lane < 32) sc_lds[lr * CMAX + t * 32 + lane] = score;
-        }
-      }
-    }
-    __syncthreads();
-    // ---------------- scores out (write-through, they may be re-read by a finisher)
-#pragma unroll
-    for (int i = 0; i < GR; i++) {
-      if (i >= R) break;
-      const int nv = n[i] - chunk_base;
-      float* dst = a.scores + (int64_t)(row0 + i) * a.ld + chunk_base;
-      __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, (int64_t)(nv > 0 ? (nv < C ? nv : C) : 0) * 4);
-      for (int p = tid; p < C; p += NT)
-        if (p < nv)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_lds[i * CMAX + p]), rs, p * 4, 0, CP_COHERENT);
-    }
+    if (R == 1) score_chunk<P, 8>(a, smem, R, c, phys);
+    else if (R == 2) score_chunk<P, 4>(a, smem, R, c, phys);
+    else score_chunk<P, 2>(a, smem, R, c, phys);
   } else {
-    // ---------------- given scores into LDS -------------------------------------
 #pragma unroll
     for (int i = 0; i < GR; i++) {
       if (i >= R) break;
@@ -643,69 +818,85 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
     __syncthreads();
   }
 
-  if (!do_select) return;
-
-  // ---------------- publish candidates (wave i handles row i) -----------------------
-  const bool given = !do_score;
   uint32_t tag[GR];
 #pragma unroll
-  for (int i = 0; i < GR; i++) tag[i] = (i < R) ? ld_co32(epochs + row0 + i) + 1u : 0u;
+  for (int i = 0; i < GR; i++) tag[i] = (do_select && i < R) ? ld_co32(epochs + row0 + i) + 1u : 0u;
   int* misc = LDS_PTR(int, L_MISC);
   const bool skip_me = (c == a.skip_chunk);
 
-  if (wv < R) {
-    const int i = wv;
-    const int nr = n[i];
-    const bool all_mode = nr <= ALL_MAX;
-    const bool publish = nr > k && !(all_mode && given);
-    uint32_t cw = 0;
-    if (publish && !all_mode && !skip_me) {
-      const int grow = row0 + i;
-      int m, cap;
-      candidate_params(nr, C, k, &m, &cap);
-      const int nv = nr - chunk_base;
-      uint32_t key[8];
-      uint32_t lmax = 0;
+  // ---------------- publish candidates (wave i handles row i) -----------------------
+  if (do_select) {
+    if (wv < R) {
+      const int i = wv;
+      const int nr = n[i];
+      const bool all_mode = nr <= ALL_MAX;
+      uint32_t cw = 0;
+      if (nr > k && !all_mode && !skip_me) {
+        const int grow = row0 + i;
+        int m, cap;
+        candidate_params(nr, C, k, &m, &cap);
+        const int nv = nr - chunk_base;
+        uint32_t key[8];
+        uint32_t lmax = 0;
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const int p = lane * 8 + j;
-        key[j] = (p < nv && p < C) ? radix_key(sc_lds[i * CMAX + p]) : 0u;
-        lmax = lmax > key[j] ? lmax : key[j];
+        for (int j = 0; j < 8; j++) {
+          const int p = lane * 8 + j;
+          key[j] = (p < nv && p < C) ? radix_key(sc_lds[i * CMAX + p]) : 0u;
+          lmax = lmax > key[j] ? lmax : key[j];
+        }
+        const uint32_t thr = wave_kth_largest(lmax, m);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) cnt += (key[j] != 0u && key[j] >= thr) ? 1 : 0;
+        const int incl = wave_incl_scan(cnt);
+        const int total = __shfl(incl, 63);
+        if (total > cap) {
+          cw = 1u << 16;  // overflow: nothing published, the finisher re-reads this chunk
+        } else {
+          int o = incl - cnt;
+          uint64_t* dst = ent + (int64_t)grow * CAP_MAX * a.meta_stride + c;
+#pragma unroll
+          for (int j = 0; j < 8; j++)
+            if (key[j] != 0u && key[j] >= thr) {
+              st_co64(dst + (int64_t)o * a.meta_stride,
+                      ((uint64_t)key[j] << 32) | (uint32_t)(chunk_base + lane * 8 + j));
+              o++;
+            }
+          cw = (uint32_t)total;
+        }
+        if (lane == 0) st_co32(twv + (int64_t)grow * a.meta_stride + c, thr);
       }
-      const uint32_t thr = wave_kth_largest(lmax, m);
-      int cnt = 0;
-#pragma unroll
-      for (int j = 0; j < 8; j++) cnt += (key[j] != 0u && key[j] >= thr) ? 1 : 0;
-      const int incl = wave_incl_scan(cnt);
-      const int total = __shfl(incl, 63);
-      if (total > cap) {
-        cw = 1u << 16;  // overflow: nothing published, the finisher re-reads this chunk
-      } else {
-        int o = incl - cnt;
-        uint64_t* dst = ent + (int64_t)grow * CAP_MAX * a.meta_stride + c;
-#pragma unroll
-        for (int j = 0; j < 8; j++)
-          if (key[j] != 0u && key[j] >= thr) {
-            st_co64(dst + (int64_t)o * a.meta_stride,
-                    ((uint64_t)key[j] << 32) | (uint32_t)(chunk_base + lane * 8 + j));
-            o++;
-          }
-        cw = (uint32_t)total;
-      }
-      if (lane == 0) st_co32(twv + (int64_t)grow * a.meta_stride + c, thr);
+      if (lane == 0) misc[32 + i] = (int)cw;
     }
-    if (lane == 0) misc[32 + i] = (int)cw;
+    // the candidates and thresholds are complete before any arrival word
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (wv < R && lane == 0 && !skip_me) {
+      const int i = wv;
+      if (n[i] > k && n[i] > ALL_MAX)
+        st_co64(meta + (int64_t)(row0 + i) * a.meta_stride + c, ((uint64_t)tag[i] << 32) | (uint32_t)misc[32 + i]);
+    }
   }
-  // every wave's score and candidate stores are complete before any arrival word
-  wait_vmcnt<0>();
-  __syncthreads();
-  if (wv < R && lane == 0 && !skip_me) {
-    const int i = wv;
-    const int nr = n[i];
-    const bool all_mode = nr <= ALL_MAX;
-    if (nr > k && !(all_mode && given))
-      st_co64(meta + (int64_t)(row0 + i) * a.meta_stride + c, ((uint64_t)tag[i] << 32) | (uint32_t)misc[32 + i]);
+
+  // ---------------- scores out (write-through: a finisher may re-read them) ----------
+  if (do_score) {
+#pragma unroll
+    for (int i = 0; i < GR; i++) {
+      if (i >= R) break;
+      const int nv = n[i] - chunk_base;
+      float* dst = a.scores + (int64_t)(row0 + i) * a.ld + chunk_base;
+      __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, (int64_t)(nv > 0 ? (nv < C ? nv : C) : 0) * 4);
+      for (int p = tid; p < C; p += NT)
+        if (p < nv)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_lds[i * CMAX + p]), rs, p * 4, 0, CP_COHERENT);
+    }
+    if (do_select) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (tid < R && !skip_me && n[tid] > k) st_co32(sv + (int64_t)(row0 + tid) * a.meta_stride + c, tag[tid]);
+    }
   }
+  if (!do_select || !is_fin) return;
   __syncthreads();
 
   // ---------------- finish the rows this chunk is designated for ---------------------
@@ -714,6 +905,7 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
   uint32_t* FK = LDS_PTR(uint32_t, L_FK);
   uint32_t* FP = LDS_PTR(uint32_t, L_FP);
   uint32_t* bm = LDS_PTR(uint32_t, L_BM);
+#pragma unroll 1
   for (int i = 0; i < R; i++) {
     const int fin = wact - 1 - (i % wact);
     if (c != fin) continue;
@@ -725,36 +917,15 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
       continue;
     }
     const bool all_mode = nr <= ALL_MAX;
-    const bool waits = !(all_mode && given);
+    const uint32_t* svrow = sv + (int64_t)grow * a.meta_stride;
     const float* srow = a.scores + (int64_t)grow * a.ld;
     __amdgpu_buffer_rsrc_t rs = make_rsrc(srow, (int64_t)nr * 4);
-    const uint64_t* mrow = meta + (int64_t)grow * a.meta_stride;
-    __amdgpu_buffer_rsrc_t rmeta = make_rsrc(mrow, (int64_t)wact * 8);
-    __amdgpu_buffer_rsrc_t rtw = make_rsrc(twv + (int64_t)grow * a.meta_stride, (int64_t)wact * 4);
-    __amdgpu_buffer_rsrc_t rent =
-        make_rsrc(ent + (int64_t)grow * CAP_MAX * a.meta_stride, (int64_t)CAP_MAX * a.meta_stride * 8);
-    // ---- wait for every chunk's arrival word
-    bool ok = true;
-    if (waits) {
-      int spins = 0;
-      while (true) {
-        bool mine = true;
-        for (int w = tid; w < wact; w += NT) {
-          const uint32_t hi = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rmeta, w * 8 + 4, 0, CP_COHERENT);
-          mine &= hi == tag[i];
-        }
-        ok = __syncthreads_and(mine) != 0;
-        if (ok || ++spins >= spin_limit) break;
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
-    if (!ok) {
-      if (tid == 0) raise_error(ws, IDX_DERR_TIMEOUT);
-      for (int p = tid; p < k; p += NT) out[p] = -1;
-    } else {
-      bool done = false;
-      if (all_mode) {
+    bool ok = true, done = false;
+    if (all_mode) {
+      if (do_score) ok = wait_tags(svrow, wact, 1, tag[i], spin_limit);
+      if (ok) {
         // ---- every score of the row into LDS (positions implicit)
+#pragma unroll 1
         for (int base = 0; base < nr; base += NT * 16) {
           uint32_t v[16];
 #pragma unroll
@@ -769,10 +940,18 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
         __syncthreads();
         int rem, ceq;
         const uint32_t T = block_kth_lds(FK, nr, k, hist, misc, &rem, &ceq);
-        const int got = bitmap_emit(FK, nullptr, nr, nr, T, rem, ceq, bm, misc, out, k);
+        const int got = select_implicit(FK, nr, k, T, rem, ceq, bm, misc, out);
         if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
         done = true;
-      } else if (nr <= BITMAP_KEYS && wact <= 4 * NT) {
+      }
+    } else {
+      const uint64_t* mrow = meta + (int64_t)grow * a.meta_stride;
+      ok = wait_tags(reinterpret_cast<const uint32_t*>(mrow) + 1, wact, 2, tag[i], spin_limit);
+      if (ok && nr <= BITMAP_KEYS && wact <= 4 * NT) {
+        __amdgpu_buffer_rsrc_t rmeta = make_rsrc(mrow, (int64_t)wact * 8);
+        __amdgpu_buffer_rsrc_t rtw = make_rsrc(twv + (int64_t)grow * a.meta_stride, (int64_t)wact * 4);
+        __amdgpu_buffer_rsrc_t rent =
+            make_rsrc(ent + (int64_t)grow * CAP_MAX * a.meta_stride, (int64_t)CAP_MAX * a.meta_stride * 8);
         // ---- candidate counts (chunk w = tid + NT*u), thresholds, offsets
         int cnt[4], offv[4];
         uint32_t tw[4];
@@ -789,30 +968,33 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
           ov[u] = (cwv >> 16) & 1u;
           cnt[u] = ov[u] ? 0 : (int)(cwv & 0xFFFFu);
           tw[u] = t;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
           int tot;
           offv[u] = E + block_excl_scan(cnt[u], misc, &tot);
           E += tot;
         }
         if (E <= FIN_ENT) {
           // ---- gather every candidate, LOAD_BATCH loads in flight per thread
-#pragma unroll
+#pragma unroll 1
           for (int u = 0; u < 4; u++) {
             const int w = tid + NT * u;
-            if (w < wact) {
-              for (int j0 = 0; j0 < cnt[u]; j0 += LOAD_BATCH) {
-                v2i_t v[LOAD_BATCH];
+            const int cu = (w < wact) ? cnt[u] : 0;
+#pragma unroll 1
+            for (int j0 = 0; j0 < cu; j0 += LOAD_BATCH) {
+              v2i_t v[LOAD_BATCH];
 #pragma unroll
-                for (int j = 0; j < LOAD_BATCH; j++)
-                  v[j] = (j0 + j < cnt[u])
-                             ? __builtin_amdgcn_raw_buffer_load_b64(rent, ((j0 + j) * a.meta_stride + w) * 8, 0, CP_COHERENT)
-                             : v2i_t{0, 0};
+              for (int j = 0; j < LOAD_BATCH; j++)
+                v[j] = (j0 + j < cu)
+                           ? __builtin_amdgcn_raw_buffer_load_b64(rent, ((j0 + j) * a.meta_stride + w) * 8, 0, CP_COHERENT)
+                           : v2i_t{0, 0};
 #pragma unroll
-                for (int j = 0; j < LOAD_BATCH; j++)
-                  if (j0 + j < cnt[u]) {
-                    FK[offv[u] + j0 + j] = (uint32_t)v[j][1];
-                    FP[offv[u] + j0 + j] = (uint32_t)v[j][0];
-                  }
-              }
+              for (int j = 0; j < LOAD_BATCH; j++)
+                if (j0 + j < cu) {
+                  FK[offv[u] + j0 + j] = (uint32_t)v[j][1];
+                  FP[offv[u] + j0 + j] = (uint32_t)v[j][0];
+                }
             }
           }
           __syncthreads();
@@ -824,17 +1006,16 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
           // published) in the bitmap area, which is free until the emission
           int nfail = 0;
           {
-            int myfail[4];
             int base = 0;
 #pragma unroll
             for (int u = 0; u < 4; u++) {
               const int w = tid + NT * u;
               const bool fail = (w < wact) && ((E < k) || ov[u] || tw[u] > T);
               int tot;
-              myfail[u] = base + block_excl_scan(fail ? 1 : 0, misc, &tot);
+              const int fo = base + block_excl_scan(fail ? 1 : 0, misc, &tot);
               if (fail) {
-                bm[2 * myfail[u]] = (uint32_t)w;
-                bm[2 * myfail[u] + 1] = ov[u] ? 0xFFFFFFFFu : tw[u];
+                bm[2 * fo] = (uint32_t)w;
+                bm[2 * fo + 1] = ov[u] ? 0xFFFFFFFFu : tw[u];
               }
               base += tot;
             }
@@ -842,53 +1023,75 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
             __syncthreads();
           }
           if (nfail > 0) {
-            // ---- re-read failing chunks: add their keys >= T that were not published
-            const uint32_t lowT = (E >= k) ? T : 0u;
-            int Ecur = E;
-            bool overflow = false;
-            for (int f = 0; f < nfail && !overflow; f++) {
-              const uint32_t w = bm[2 * f];
-              const uint32_t twf = bm[2 * f + 1];
-              const int p0 = (int)w * C;
-              for (int base = 0; base < C; base += NT) {
-                const int p = p0 + base + tid;
-                bool take = false;
-                uint32_t key = 0;
-                if (base + tid < C && p < nr) {
-                  key = radix_key(__uint_as_float(
-                      (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, p * 4, 0, CP_COHERENT)));
-                  take = key >= lowT && (twf == 0xFFFFFFFFu || key < twf);
-                }
-                int tot;
-                const int o = block_excl_scan(take ? 1 : 0, misc, &tot);
-                if (Ecur + tot > FIN_ENT) { overflow = true; break; }
-                if (take) { FK[Ecur + o] = key; FP[Ecur + o] = (uint32_t)p; }
-                Ecur += tot;
+            // ---- re-read failing chunks (once their scores are out): add their keys >= T
+            // that were not published
+            bool sv_ok = true;
+            if (do_score) {
+              int spins = 0;
+              while (true) {
+                bool mine = true;
+                for (int f = tid; f < nfail; f += NT) mine &= ld_co32(svrow + bm[2 * f]) == tag[i];
+                if (__syncthreads_and(mine)) break;
+                if (++spins >= spin_limit) { sv_ok = false; break; }
+                __builtin_amdgcn_s_sleep(1);
               }
             }
-            __syncthreads();
-            if (!overflow && Ecur >= k) {
-              T = block_kth_lds(FK, Ecur, k, hist, misc, &rem, &ceq);
-              E = Ecur;
-              nfail = 0;
+            if (!sv_ok) {
+              ok = false;
+            } else {
+              const uint32_t lowT = (E >= k) ? T : 0u;
+              int Ecur = E;
+              bool overflow = false;
+#pragma unroll 1
+              for (int f = 0; f < nfail && !overflow; f++) {
+                const uint32_t w = bm[2 * f];
+                const uint32_t twf = bm[2 * f + 1];
+                const int p0 = (int)w * C;
+#pragma unroll 1
+                for (int base = 0; base < C; base += NT) {
+                  const int p = p0 + base + tid;
+                  bool take = false;
+                  uint32_t key = 0;
+                  if (base + tid < C && p < nr) {
+                    key = radix_key(__uint_as_float(
+                        (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, p * 4, 0, CP_COHERENT)));
+                    take = key >= lowT && (twf == 0xFFFFFFFFu || key < twf);
+                  }
+                  int tot;
+                  const int o = block_excl_scan(take ? 1 : 0, misc, &tot);
+                  if (Ecur + tot > FIN_ENT) { overflow = true; break; }
+                  if (take) { FK[Ecur + o] = key; FP[Ecur + o] = (uint32_t)p; }
+                  Ecur += tot;
+                }
+              }
+              __syncthreads();
+              if (!overflow && Ecur >= k) {
+                T = block_kth_lds(FK, Ecur, k, hist, misc, &rem, &ceq);
+                E = Ecur;
+                nfail = 0;
+              }
             }
           }
-          if (nfail == 0) {
-            const int got = bitmap_emit(FK, FP, E, nr, T, rem, ceq, bm, misc, out, k);
+          if (ok && nfail == 0) {
+            const int got = select_explicit(FK, FP, E, nr, k, T, rem, ceq, bm, misc, out);
             if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
             done = true;
           }
         }
       }
-      if (!done) {
-        __syncthreads();
-        global_select_row(srow, nr, k, out, hist, misc);
-      }
+      if (ok && !done && do_score) ok = wait_tags(svrow, wact, 1, tag[i], spin_limit);
+    }
+    if (!ok) {
+      if (tid == 0) raise_error(ws, IDX_DERR_TIMEOUT);
+      for (int p = tid; p < k; p += NT) out[p] = -1;
+    } else if (!done) {
+      __syncthreads();
+      global_select_row(srow, nr, k, out, hist, misc);
     }
     __syncthreads();
     // a fresh tag for the next call on this row (also after a timeout, so that
     // late arrival words of this call can never pass for the next call's)
-    if (waits && tid == 0) st_co32(epochs + grow, tag[i]);
+    if (tid == 0 && (do_score || !all_mode)) st_co32(epochs + grow, tag[i]);
   }
 }
 
@@ -939,7 +1142,7 @@ Plan plan_topk(int max_keys) {
 }
 
 struct WsLayout {
-  uint64_t off_epoch, off_meta, off_tw, off_ent, total;
+  uint64_t off_epoch, off_meta, off_tw, off_sv, off_ent, total;
   int meta_stride;
 };
 
@@ -953,7 +1156,8 @@ WsLayout layout_for(int rows, int max_keys) {
   L.off_epoch = WS_HDR;
   L.off_meta = align256(L.off_epoch + (uint64_t)rows * 4);
   L.off_tw = align256(L.off_meta + (uint64_t)rows * stride * 8);
-  L.off_ent = align256(L.off_tw + (uint64_t)rows * stride * 4);
+  L.off_sv = align256(L.off_tw + (uint64_t)rows * stride * 4);
+  L.off_ent = align256(L.off_sv + (uint64_t)rows * stride * 4);
   L.total = align256(L.off_ent + (uint64_t)rows * stride * CAP_MAX * 8);
   return L;
 }
@@ -1012,7 +1216,7 @@ int launch(const KArgs& args, int P, dim3 grid, hipStream_t st) {
 
 void fill_common(KArgs& args, const WsLayout& L, void* ws, size_t ws_bytes) {
   args.ws = static_cast<uint8_t*>(ws);
-  args.ws_bytes = (int64_t)ws_bytes;
+  (void)ws_bytes;
   args.spin_limit = g_spin_limit;
   args.skip_chunk = g_skip_chunk;
   args.meta_stride = L.meta_stride;
@@ -1020,6 +1224,7 @@ void fill_common(KArgs& args, const WsLayout& L, void* ws, size_t ws_bytes) {
   args.off_meta = L.off_meta;
   args.off_tw = L.off_tw;
   args.off_ent = L.off_ent;
+  args.off_sv = L.off_sv;
 }
 
 int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int32_t* topk, void* ws,
@@ -1039,8 +1244,8 @@ int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int3
   const Plan pl = plan_score(p->max_keys);
   KArgs args;
   memset(&args, 0, sizeof args);
-  args.q = static_cast<const uint32_t*>(p->q);
-  args.w = static_cast<const uint16_t*>(p->w);
+  args.q = static_cast<const uint8_t*>(p->q);
+  args.w = static_cast<const uint8_t*>(p->w);
   args.kc = p->k_cache;
   args.ks = p->k_scale;
   args.pt = p->page_table;
