@@ -72,15 +72,17 @@ constexpr int L_Q = L_SC + GR * CMAX * 4;                   // [GR][64 heads][25
 constexpr int L_W = L_Q + GR * H * D * 2;                   // [GR][64] bf16 head weights
 constexpr int L_SCORE_END = L_W + GR * H * 2;
 // LDS layout, finishing phase
-constexpr int L_FK = 0;                                     // keys: FIN_ENT (or ALL_MAX when positions are implicit)
+constexpr int L_FK = 0;                                     // candidate keys: FIN_ENT
 constexpr int L_FP = FIN_ENT * 4;                           // positions: FIN_ENT
-constexpr int L_BM = ALL_MAX * 4;                           // bitmap: BITMAP_KEYS / 32 words
-constexpr int L_HIST = L_BM + BITMAP_KEYS / 8;              // 256 u32 histogram
-constexpr int L_MISC = L_HIST + 256 * 4;                    // 64 u32 scratch
-constexpr int L_FIN_END = L_MISC + 64 * 4;
+constexpr int L_BM = FIN_ENT * 8;                           // bitmap: BITMAP_KEYS / 32 words
+constexpr int L_HIST = L_BM + BITMAP_KEYS / 8;              // 2 x 4096 u32 histograms
+constexpr int L_MISC = L_HIST + 2 * 4096 * 4;               // 64 u32 scratch
+constexpr int L_CO = L_MISC + 64 * 4;                       // per chunk: offset << 8 | count (4 NT)
+constexpr int L_FIN_END = L_CO + 4 * NT * 4;
 constexpr int LDS_BYTES = (L_FIN_END > L_SCORE_END ? L_FIN_END : L_SCORE_END);
-static_assert(FIN_ENT * 8 <= ALL_MAX * 4, "candidate keys+positions must fit the key region");
-static_assert(L_SC + GR * CMAX * 4 <= L_FK + ALL_MAX * 4 || true, "");
+static_assert(BITMAP_KEYS / 8 >= 4 * NT * 8, "the failing-chunk list (2 words a chunk) fits the bitmap");
+static_assert(ALL_MAX % NT == 0 && FIN_ENT % NT == 0, "register segments");
+static_assert(CAP_MAX < 256, "a chunk's candidate count is packed in 8 bits");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
 // workspace header (bytes)
@@ -105,7 +107,9 @@ struct KArgs {
   int32_t spin_limit;
   int32_t skip_chunk;       // test hook: this chunk publishes nothing (-1 = off)
   int32_t meta_stride;      // chunk slots per row (>= gridDim.x)
-  uint64_t off_epoch, off_meta, off_tw, off_ent, off_sv;
+  int32_t ent_stride;       // chunk slots per row and candidate slot (min(meta_stride, 4 NT))
+  int32_t all_stride;       // keys per row of the all-keys area
+  uint64_t off_meta, off_ent, off_sv, off_allk;
   uint32_t grp[IDX_MAX_REQ];// row0 | nrows << 24
   int32_t gmax[IDX_MAX_REQ];// host bound on the keys of each group's rows
 };
@@ -176,7 +180,7 @@ __device__ inline int lane_id() { return (int)(threadIdx.x & 63); }
 __device__ inline float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // m-th largest of one value per lane (m >= 1): the largest t with #{v >= t} >= m.
-__device__ inline uint32_t wave_kth_largest(uint32_t v, int m) {
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int m) {
   uint32_t t = 0;
   for (int b = 31; b >= 0; --b) {
     uint32_t cand = t | (1u << b);
@@ -245,107 +249,191 @@ __device__ inline void hist_add(uint32_t* hist, bool m, uint32_t bin) {
   if (m && !same) atomicAdd(&hist[bin], 1u);
 }
 
-// Digit search over a 256-bin histogram (bins above `nbins` are empty): the digit d
-// holding the rem-th largest remaining key.  Writes misc[8] = d, misc[9] = rem left
-// within d, misc[10] = count of d.  Every thread must call.
-__device__ inline void find_digit(const uint32_t* hist, int rem, int* misc) {
-  const int tid = threadIdx.x;
-  const int cnt = (tid < 256) ? (int)hist[255 - tid] : 0;
-  int tot;
-  const int excl = block_excl_scan(cnt, misc, &tot);
-  if (tid < 256 && cnt > 0 && excl < rem && rem <= excl + cnt) {
-    misc[8] = 255 - tid;
-    misc[9] = rem - excl;
-    misc[10] = cnt;
+// Radix digit search, part of kth_regs: the digit d of hist[0 .. nbins) (nbins a power
+// of two, <= 4096) holding the rem-th largest remaining key, counting from the top bin.
+// Writes misc[8] = d, misc[9] = rem left within d, misc[10] = count of d.  Every thread
+// must call; two barriers.
+__device__ inline void find_digit(const uint32_t* hist, int nbins, int rem, int* misc) {
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  const int bpt = nbins > NT ? nbins / NT : 1;        // bins per thread, from the top
+  const int hi = nbins - 1 - tid * bpt;               // this thread's highest bin
+  int c = 0;
+  if (hi >= 0)
+    for (int i = 0; i < bpt; i++) c += (int)hist[hi - i];
+  const int incl = wave_incl_scan(c);
+  if (lane == 63) misc[wv] = incl;
+  __syncthreads();
+  int before = incl - c;
+#pragma unroll
+  for (int i = 0; i < NWAVE; i++) before += (i < wv) ? misc[i] : 0;
+  if (c > 0 && before < rem && rem <= before + c) {
+    int b = hi, r = rem - before;
+    for (int i = 0; i < bpt; i++, b--) {
+      const int h = (int)hist[b];
+      if (r <= h) break;
+      r -= h;
+    }
+    misc[8] = b;
+    misc[9] = r;
+    misc[10] = (int)hist[b];
   }
   __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// Exact k-th largest key among LDS keys K[0..E): radix select over the bits below
-// the common prefix of the smallest and largest key, 8-bit digits from the top.
-// Returns T; *rem = how many keys equal to T belong to the top k, *ceq = how many
-// keys equal T.  Requires 1 <= k <= E.  Every thread must call.
+// Exact k-th largest of the keys held in registers across the workgroup: thread t
+// holds kr[0 .. S) (slots past S hold 0), a zero key is absent, and only keys >= lo
+// count.  Radix select over the bits below the common prefix of the smallest and
+// largest counted key, in digits of up to 12 bits from the top, histograms in LDS
+// (hist: 2 x 4096 words).  Returns false if fewer than k keys count.  Otherwise the
+// top k of the counted keys (score descending, then position) are exactly: every key
+// > *T, then the first *rem keys equal to *T in position order (*rem may be 0).
+// Slots are visited in groups of 8, skipping whole groups past S.  Every thread must
+// call.
 // ---------------------------------------------------------------------------
-__device__ uint32_t block_kth_lds(const uint32_t* K, int E, int k, uint32_t* hist, int* misc,
-                                  int* rem_out, int* ceq_out) {
-  const int tid = threadIdx.x;
+template <int SMAX>
+__device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, uint32_t lo, int k, uint32_t* hist,
+                                         int* misc, uint32_t* T_out, int* rem_out) {
+  static_assert(SMAX % 8 == 0, "slot groups of 8");
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  lo = lo > 1u ? lo : 1u;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int e = tid; e < E; e += NT) {
-    const uint32_t key = K[e];
-    mn = mn < key ? mn : key;
-    mx = mx > key ? mx : key;
+  int cnt = 0;
+#pragma unroll
+  for (int g = 0; g < SMAX / 8; g++) {
+    if (g * 8 >= S) break;
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++) {
+      const uint32_t key = kr[g * 8 + jj];
+      const bool v = key >= lo;
+      mn = (v && key < mn) ? key : mn;
+      mx = (v && key > mx) ? key : mx;
+      cnt += v ? 1 : 0;
+    }
   }
   mn = wave_min_u32(mn);
   mx = wave_max_u32(mx);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
   uint32_t* red = reinterpret_cast<uint32_t*>(misc) + 16;
-  if (lane_id() == 0) { red[tid >> 6] = mn; red[NWAVE + (tid >> 6)] = mx; }
+  if (lane == 0) {
+    red[wv] = mn;
+    red[NWAVE + wv] = mx;
+    red[2 * NWAVE + wv] = (uint32_t)cnt;
+  }
+  {
+    v4i z = {0, 0, 0, 0};
+    v4i* h4 = reinterpret_cast<v4i*>(hist);
+    h4[tid] = z;                                        // first histogram buffer (4096 words)
+    h4[tid + NT] = z;
+  }
   __syncthreads();
+  cnt = 0;
 #pragma unroll
   for (int i = 0; i < NWAVE; i++) {
     mn = mn < red[i] ? mn : red[i];
     mx = mx > red[NWAVE + i] ? mx : red[NWAVE + i];
+    cnt += (int)red[2 * NWAVE + i];
   }
-  __syncthreads();
-  const uint32_t diff = mn ^ mx;
-  if (diff == 0) {  // every key equal
+  if (cnt < k) return false;
+  if (mn == mx) {  // every counted key equal: the first k of them
+    *T_out = mn;
     *rem_out = k;
-    *ceq_out = E;
-    return mn;
+    return true;
   }
-  const int top = 31 - __clz(diff);                    // highest bit that differs
+  const int top = 31 - __clz(mn ^ mx);               // highest bit that differs
   uint32_t mask = (top == 31) ? 0u : ~((2u << top) - 1u);
   uint32_t prefix = mn & mask;
-  int rem = k, ceq = 0;
-  int shift = top - 7;
+  const int nb = top + 1;                             // bits left to resolve
+  const int npass = (nb + 11) / 12;
+  const int wdef = (nb + npass - 1) / npass;
+  int rem = k, shift = nb, buf = 0;
   while (true) {
-    int width = 8;
-    if (shift < 0) { width = 8 + shift; shift = 0; }
+    const int width = wdef < shift ? wdef : shift;
+    shift -= width;
     const uint32_t dmask = (1u << width) - 1u;
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    for (int e0 = 0; e0 < E; e0 += NT) {
-      const int e = e0 + tid;
-      const uint32_t key = e < E ? K[e] : 0u;
-      hist_add(hist, e < E && (key & mask) == prefix, (key >> shift) & dmask);
+    uint32_t* h = hist + buf * 4096;
+#pragma unroll
+    for (int g = 0; g < SMAX / 8; g++) {
+      if (g * 8 >= S) break;
+#pragma unroll
+      for (int jj = 0; jj < 8; jj++) {
+        const uint32_t key = kr[g * 8 + jj];
+        if (key >= lo && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & dmask], 1u);
+      }
+    }
+    {
+      // the other buffer is free: clear it for the next pass
+      v4i z = {0, 0, 0, 0};
+      v4i* h4 = reinterpret_cast<v4i*>(hist + (buf ^ 1) * 4096);
+      h4[tid] = z;
+      h4[tid + NT] = z;
     }
     __syncthreads();
-    find_digit(hist, rem, misc);
+    find_digit(h, 1 << width, rem, misc);
     const uint32_t d = (uint32_t)misc[8];
-    rem = misc[9];
-    ceq = misc[10];
+    const int r = misc[9];
+    const int c = misc[10];
     prefix |= d << shift;
     mask |= dmask << shift;
-    __syncthreads();
-    if (shift == 0) break;
-    shift -= 8;
+    if (shift == 0) {
+      *T_out = prefix;
+      *rem_out = r;
+      return true;
+    }
+    if (c == r && prefix != 0u) {
+      // every key of this digit is selected: the top k are exactly the keys >= prefix
+      *T_out = prefix - 1u;
+      *rem_out = 0;
+      return true;
+    }
+    rem = r;
+    buf ^= 1;
   }
-  *rem_out = rem;
-  *ceq_out = ceq;
-  return prefix;
 }
 
-// Emit the set bits of bm[0 .. words) as ascending positions into out[0 .. kk).
-// Returns how many bits were set.  Every thread must call.
-__device__ int emit_bitmap(const uint32_t* bm, int words, int* misc, int32_t* out, int kk) {
-  const int tid = threadIdx.x;
-  const int wpt = (words + NT - 1) / NT;
-  const int w0 = tid * wpt;
-  int c = 0;
-  for (int i = 0; i < wpt; i++) c += (w0 + i < words) ? __popc(bm[w0 + i]) : 0;
-  int tot;
-  int o = block_excl_scan(c, misc, &tot);
-  for (int i = 0; i < wpt; i++) {
-    if (w0 + i >= words) break;
-    uint32_t x = bm[w0 + i];
-    while (x) {
-      const int b = __ffs(x) - 1;
-      x &= x - 1;
-      if (o < kk) out[o] = (w0 + i) * 32 + b;
-      o++;
+// Emission of the top k in segment order (thread t's slots j < S precede thread t + 1's;
+// the caller lays positions out ascending in that order; slots past S hold 0): a key
+// is selected when key > T, or key == T and it is among the first rem such keys.
+// out[0 .. k) receives the selected positions (pos_of(j)).  Returns the number
+// selected.  Every thread must call.
+template <int SMAX, typename PosF>
+__device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], int S, uint32_t T, int rem, int32_t* out,
+                                             int k, int* misc, PosF pos_of) {
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int g = 0; g < SMAX / 8; g++) {
+    if (g * 8 >= S) break;
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++) {
+      const uint32_t key = kr[g * 8 + jj];
+      gt += key > T ? 1 : 0;
+      eq += key == T ? 1 : 0;
     }
   }
-  return tot;
+  int tot;
+  const int packed = block_excl_scan(gt | (eq << 16), misc, &tot);
+  const int before_gt = packed & 0xFFFF, before_eq = packed >> 16;
+  if (gt + (eq > 0 ? 1 : 0) > 0) {
+    int o = before_gt + (before_eq < rem ? before_eq : rem);
+    int er = before_eq;
+#pragma unroll
+    for (int g = 0; g < SMAX / 8; g++) {
+      if (g * 8 >= S) break;
+#pragma unroll
+      for (int jj = 0; jj < 8; jj++) {
+        const uint32_t key = kr[g * 8 + jj];
+        bool sel = key > T;
+        if (key == T) sel = er++ < rem;
+        if (sel) {
+          if (o < k) out[o] = pos_of(g * 8 + jj);
+          o++;
+        }
+      }
+    }
+  }
+  const int tg = tot & 0xFFFF, te = tot >> 16;
+  return tg + (te < rem ? te : rem);
 }
 
 // Position of the rem-th set bit of bm[0 .. words) (1-based rem).  Every thread must call.
@@ -377,57 +465,50 @@ __device__ uint32_t nth_set_bit(const uint32_t* bm, int words, int rem, int* mis
   return r;
 }
 
-// Top k of all n keys K[0..n) with implicit positions (K[p] is position p): bitmap words
-// are built with wave ballots, no atomics.  Returns the number emitted.
-__device__ int select_implicit(const uint32_t* K, int n, int k, uint32_t T, int rem, int ceq, uint32_t* bm,
-                               int* misc, int32_t* out) {
-  const int tid = threadIdx.x, lane = lane_id();
-  const int words = (n + 31) >> 5;
-  uint32_t pos_cut = 0xFFFFFFFFu;
-  if (ceq > rem) {
-    for (int e0 = 0; e0 < n; e0 += NT) {
-      const int e = e0 + tid;
-      const uint64_t b = __ballot(e < n && K[e] == T);
-      if (lane == 0 && e < n) {
-        bm[e >> 5] = (uint32_t)b;
-        if ((e >> 5) + 1 < words) bm[(e >> 5) + 1] = (uint32_t)(b >> 32);
-      }
-    }
-    __syncthreads();
-    pos_cut = nth_set_bit(bm, words, rem, misc);
-  }
-  for (int e0 = 0; e0 < n; e0 += NT) {
-    const int e = e0 + tid;
-    const uint32_t key = e < n ? K[e] : 0u;
-    const uint64_t b = __ballot(e < n && (key > T || (key == T && (uint32_t)e <= pos_cut)));
-    if (lane == 0 && e < n) {
-      bm[e >> 5] = (uint32_t)b;
-      if ((e >> 5) + 1 < words) bm[(e >> 5) + 1] = (uint32_t)(b >> 32);
+// Emit the set bits of bm[0 .. words) as ascending positions into out[0 .. kk).
+// Returns how many bits were set.  Every thread must call.
+__device__ int emit_bitmap(const uint32_t* bm, int words, int* misc, int32_t* out, int kk) {
+  const int tid = threadIdx.x;
+  const int wpt = (words + NT - 1) / NT;
+  const int w0 = tid * wpt;
+  int c = 0;
+  for (int i = 0; i < wpt; i++) c += (w0 + i < words) ? __popc(bm[w0 + i]) : 0;
+  int tot;
+  int o = block_excl_scan(c, misc, &tot);
+  for (int i = 0; i < wpt; i++) {
+    if (w0 + i >= words) break;
+    uint32_t x = bm[w0 + i];
+    while (x) {
+      const int b = __ffs(x) - 1;
+      x &= x - 1;
+      if (o < kk) out[o] = (w0 + i) * 32 + b;
+      o++;
     }
   }
-  __syncthreads();
-  return emit_bitmap(bm, words, misc, out, k);
+  return tot;
 }
 
-// Top k of the candidate set (K, P)[0..E) over positions [0, n).  Returns the number emitted.
+// Top k of the candidate set (K, P)[0 .. E) over positions [0, n), given the threshold
+// (T, rem) of kth_regs, through a position bitmap (the candidates need not be in
+// position order).  Returns the number emitted.  Every thread must call.
 __device__ int select_explicit(const uint32_t* K, const uint32_t* P, int E, int n, int k, uint32_t T, int rem,
-                               int ceq, uint32_t* bm, int* misc, int32_t* out) {
+                               uint32_t* bm, int* misc, int32_t* out) {
   const int tid = threadIdx.x;
   const int words = (n + 31) >> 5;
   for (int i = tid; i < words; i += NT) bm[i] = 0;
   __syncthreads();
-  uint32_t pos_cut = 0xFFFFFFFFu;
-  if (ceq > rem) {
+  int pos_cut = -1;                                   // keys equal to T at positions <= pos_cut
+  if (rem > 0) {
     for (int e = tid; e < E; e += NT)
       if (K[e] == T) atomicOr(&bm[P[e] >> 5], 1u << (P[e] & 31));
     __syncthreads();
-    pos_cut = nth_set_bit(bm, words, rem, misc);
+    pos_cut = (int)nth_set_bit(bm, words, rem, misc);
     for (int i = tid; i < words; i += NT) bm[i] = 0;
     __syncthreads();
   }
   for (int e = tid; e < E; e += NT) {
     const uint32_t key = K[e], p = P[e];
-    if (key > T || (key == T && p <= pos_cut)) atomicOr(&bm[p >> 5], 1u << (p & 31));
+    if (key > T || (key == T && (int)p <= pos_cut)) atomicOr(&bm[p >> 5], 1u << (p & 31));
   }
   __syncthreads();
   return emit_bitmap(bm, words, misc, out, k);
@@ -456,7 +537,7 @@ __device__ void global_select_row(const float* row, int n, int k, int32_t* out, 
       }
     }
     __syncthreads();
-    find_digit(hist, rem, misc);
+    find_digit(hist, 256, rem, misc);
     prefix |= (uint32_t)misc[8] << shift;
     mask |= 0xFFu << shift;
     rem = misc[9];
@@ -515,16 +596,16 @@ __device__ inline void candidate_params(int n, int C, int k, int* m, int* cap) {
   *cap = cc;
 }
 
-// Bounded poll until words[w * stride] == tag for every w < count (coherent loads).
-// Every thread must call.  Returns false on timeout.
-__device__ bool wait_tags(const uint32_t* words, int count, int stride_words, uint32_t tag, int spin_limit) {
+// Bounded poll until words[w] != 0 for every w < count (coherent loads).  Every thread
+// must call.  Returns false on timeout.
+__device__ __forceinline__ bool wait_nonzero(const uint32_t* words, int count, int spin_limit) {
   const int tid = threadIdx.x;
-  __amdgpu_buffer_rsrc_t r = make_rsrc(words, (int64_t)count * stride_words * 4);
+  __amdgpu_buffer_rsrc_t r = make_rsrc(words, (int64_t)count * 4);
   int spins = 0;
   while (true) {
     bool mine = true;
     for (int w = tid; w < count; w += NT)
-      mine &= (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, w * stride_words * 4, 0, CP_COHERENT) == tag;
+      mine &= __builtin_amdgcn_raw_buffer_load_b32(r, w * 4, 0, CP_COHERENT) != 0;
     if (__syncthreads_and(mine)) return true;
     if (++spins >= spin_limit) return false;
     __builtin_amdgcn_s_sleep(1);
@@ -695,6 +776,35 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
+// x[u] for a runtime u < 4 without indexing registers
+__device__ inline int pick4(const int (&x)[4], int u) {
+  return u == 0 ? x[0] : u == 1 ? x[1] : u == 2 ? x[2] : x[3];
+}
+
+// Exclusive scan of v and maximum of m over the workgroup.  Every thread must call.
+__device__ inline int block_scan_max(int v, uint32_t m, int* misc, int* total, uint32_t* mall) {
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int x = wave_incl_scan(v);
+  m = wave_max_u32(m);
+  if (lane == 63) misc[wv] = x;
+  if (lane == 0) misc[NWAVE + wv] = (int)m;
+  __syncthreads();
+  int before = 0, tot = 0;
+  uint32_t mx = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; i++) {
+    const int s = misc[i];
+    before += (i < wv) ? s : 0;
+    tot += s;
+    const uint32_t mi = (uint32_t)misc[NWAVE + i];
+    mx = mx > mi ? mx : mi;
+  }
+  __syncthreads();
+  *total = tot;
+  *mall = mx;
+  return x - v + before;
+}
+
 template <int P>
 __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -712,13 +822,20 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
 
   const int gbound = a.gmax[g];
   if (c > 0 && chunk_base >= gbound) return;      // beyond every row of this group
-  if (*reinterpret_cast<const uint32_t*>(ws + WS_MAGIC_OFF) != WS_MAGIC) {
-    if (tid == 0 && c == 0 && g == 0) raise_error(ws, IDX_DERR_WS);
-    return;
-  }
   const bool do_score = (a.mode & MODE_SCORE) != 0;
   const bool do_select = (a.mode & MODE_SELECT) != 0;
   const bool given = !do_score;
+  {
+    // magic word and sticky error word in one load.  The exchange areas are clean
+    // (all zero) between calls unless a wait timed out; such a workspace is refused
+    // for selection until idx_device_status() has read the error and re-initialised it.
+    const uint64_t hdr = *reinterpret_cast<const uint64_t*>(ws + WS_MAGIC_OFF);
+    if ((uint32_t)hdr != WS_MAGIC) {
+      if (tid == 0 && c == 0 && g == 0) raise_error(ws, IDX_DERR_WS);
+      return;
+    }
+    if (do_select && ((uint32_t)(hdr >> 32) & IDX_DERR_TIMEOUT)) return;
+  }
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   if (do_score) {
     // Queries and head weights of the group's rows into LDS first (2R + 1 DMA per
@@ -771,24 +888,32 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
   if (chunk_base >= nmax) return;                 // nothing of this group here
   const int wact = (nmax + C - 1) / C;            // chunks holding keys of this group
   const int k = a.k;
+  // how row i selects: nothing to select (n <= k), from all its keys at once (n <=
+  // ALL_MAX), from per-chunk candidates (up to 4 chunks per finishing thread), or by
+  // a multi-pass select over its scores in memory
+  auto thr_mode = [&](int nr) { return nr > k && nr > ALL_MAX && wact <= 4 * NT; };
+  auto all_mode = [&](int nr) { return nr > k && nr <= ALL_MAX; };
+  // rows whose finisher may read scores back from memory (after "scores visible")
+  auto sv_row = [&](int nr) { return do_score && nr > k && nr > ALL_MAX; };
   // finisher of row i: chunk wact - 1 - (i % wact)
   bool is_fin = false;
 #pragma unroll
   for (int i = 0; i < GR; i++) is_fin |= (i < R) && (c == wact - 1 - (i % wact));
   if (given && !is_fin) {
-    // over given scores, rows of at most ALL_MAX keys need nothing from this chunk
+    // over given scores, only rows selecting from candidates need this chunk
     bool needed = false;
 #pragma unroll
-    for (int i = 0; i < GR; i++) needed |= (i < R) && n[i] > k && n[i] > ALL_MAX;
+    for (int i = 0; i < GR; i++) needed |= (i < R) && thr_mode(n[i]);
     if (!needed) return;
   }
 
   float* const sc_lds = LDS_PTR(float, L_SC);
-  uint32_t* const epochs = reinterpret_cast<uint32_t*>(ws + a.off_epoch);
+  const int64_t ms = a.meta_stride;
+  const int64_t es = a.ent_stride;      // chunk slots of the candidate area (<= 4 NT)
   uint64_t* const meta = reinterpret_cast<uint64_t*>(ws + a.off_meta);
-  uint32_t* const twv = reinterpret_cast<uint32_t*>(ws + a.off_tw);
   uint64_t* const ent = reinterpret_cast<uint64_t*>(ws + a.off_ent);
   uint32_t* const sv = reinterpret_cast<uint32_t*>(ws + a.off_sv);
+  uint32_t* const allk = reinterpret_cast<uint32_t*>(ws + a.off_allk);
 
   if (do_score) {
     int phys[P];
@@ -817,64 +942,60 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
     }
     __syncthreads();
   }
-
-  uint32_t tag[GR];
-#pragma unroll
-  for (int i = 0; i < GR; i++) tag[i] = (do_select && i < R) ? ld_co32(epochs + row0 + i) + 1u : 0u;
   int* misc = LDS_PTR(int, L_MISC);
   const bool skip_me = (c == a.skip_chunk);
 
-  // ---------------- publish candidates (wave i handles row i) -----------------------
-  if (do_select) {
-    if (wv < R) {
-      const int i = wv;
-      const int nr = n[i];
-      const bool all_mode = nr <= ALL_MAX;
-      uint32_t cw = 0;
-      if (nr > k && !all_mode && !skip_me) {
-        const int grow = row0 + i;
-        int m, cap;
-        candidate_params(nr, C, k, &m, &cap);
-        const int nv = nr - chunk_base;
-        uint32_t key[8];
-        uint32_t lmax = 0;
+  // ---------------- publish (wave i handles row i); no waits ------------------------
+  // Every exchange word is written through to memory and is nonzero once written; the
+  // finisher polls until it reads nonzero, then clears it, so the areas are all zero
+  // again when the call ends.
+  if (do_select && wv < R && !skip_me) {
+    const int i = wv;
+    const int nr = n[i];
+    const int grow = row0 + i;
+    const int nv = nr - chunk_base;
+    if (thr_mode(nr)) {
+      // candidates: every key of the chunk >= t_w (the m-th largest of the 64 lane
+      // maxima), as (key << 32 | position), in ascending position order
+      int m, cap;
+      candidate_params(nr, C, k, &m, &cap);
+      uint32_t key[8];
+      uint32_t lmax = 0;
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-          const int p = lane * 8 + j;
-          key[j] = (p < nv && p < C) ? radix_key(sc_lds[i * CMAX + p]) : 0u;
-          lmax = lmax > key[j] ? lmax : key[j];
-        }
-        const uint32_t thr = wave_kth_largest(lmax, m);
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < 8; j++) cnt += (key[j] != 0u && key[j] >= thr) ? 1 : 0;
-        const int incl = wave_incl_scan(cnt);
-        const int total = __shfl(incl, 63);
-        if (total > cap) {
-          cw = 1u << 16;  // overflow: nothing published, the finisher re-reads this chunk
-        } else {
-          int o = incl - cnt;
-          uint64_t* dst = ent + (int64_t)grow * CAP_MAX * a.meta_stride + c;
-#pragma unroll
-          for (int j = 0; j < 8; j++)
-            if (key[j] != 0u && key[j] >= thr) {
-              st_co64(dst + (int64_t)o * a.meta_stride,
-                      ((uint64_t)key[j] << 32) | (uint32_t)(chunk_base + lane * 8 + j));
-              o++;
-            }
-          cw = (uint32_t)total;
-        }
-        if (lane == 0) st_co32(twv + (int64_t)grow * a.meta_stride + c, thr);
+      for (int j = 0; j < 8; j++) {
+        const int p = lane * 8 + j;
+        key[j] = (p < nv && p < C) ? radix_key(sc_lds[i * CMAX + p]) : 0u;
+        lmax = lmax > key[j] ? lmax : key[j];
       }
-      if (lane == 0) misc[32 + i] = (int)cw;
-    }
-    // the candidates and thresholds are complete before any arrival word
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (wv < R && lane == 0 && !skip_me) {
-      const int i = wv;
-      if (n[i] > k && n[i] > ALL_MAX)
-        st_co64(meta + (int64_t)(row0 + i) * a.meta_stride + c, ((uint64_t)tag[i] << 32) | (uint32_t)misc[32 + i]);
+      const uint32_t thr = wave_kth_largest(lmax, m);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < 8; j++) cnt += (key[j] != 0u && key[j] >= thr) ? 1 : 0;
+      const int incl = wave_incl_scan(cnt);
+      const int total = __shfl(incl, 63);
+      uint32_t cw;
+      if (total > cap) {
+        cw = 1u << 16;  // overflow: nothing published, the finisher re-reads this chunk
+      } else {
+        int o = incl - cnt;
+        uint64_t* dst = ent + ((int64_t)grow * es + c) * CAP_MAX;
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+          if (key[j] != 0u && key[j] >= thr) {
+            st_co64(dst + o, ((uint64_t)key[j] << 32) | (uint32_t)(chunk_base + lane * 8 + j));
+            o++;
+          }
+        cw = (uint32_t)total;
+      }
+      if (lane == 0) st_co64(meta + (int64_t)grow * ms + c, ((uint64_t)thr << 32) | 0x80000000u | cw);
+    } else if (all_mode(nr) && do_score) {
+      // every key of the chunk, at its position (finite scores have nonzero keys)
+      uint32_t* dst = allk + (int64_t)grow * a.all_stride + chunk_base;
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int p = j * 64 + lane;
+        if (p < nv && p < C) st_co32(dst + p, radix_key(sc_lds[i * CMAX + p]));
+      }
     }
   }
 
@@ -890,13 +1011,20 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
         if (p < nv)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_lds[i * CMAX + p]), rs, p * 4, 0, CP_COHERENT);
     }
-    if (do_select) {
-      wait_vmcnt<0>();
-      __syncthreads();
-      if (tid < R && !skip_me && n[tid] > k) st_co32(sv + (int64_t)(row0 + tid) * a.meta_stride + c, tag[tid]);
-    }
   }
-  if (!do_select || !is_fin) return;
+  // "scores visible" words of rows selecting from candidates, once this chunk's scores
+  // have reached memory.  A finisher writes its own later, when it next waits anyway.
+  auto publish_sv = [&]() {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (tid < R && !skip_me && sv_row(n[tid])) st_co32(sv + (int64_t)(row0 + tid) * ms + c, 1u);
+  };
+  if (!do_select) return;
+  if (!is_fin) {
+    if (do_score) publish_sv();
+    return;
+  }
+  bool sv_done = !do_score;
   __syncthreads();
 
   // ---------------- finish the rows this chunk is designated for ---------------------
@@ -916,183 +1044,330 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
       for (int p = tid; p < k; p += NT) out[p] = p < nr ? p : -1;
       continue;
     }
-    const bool all_mode = nr <= ALL_MAX;
-    const uint32_t* svrow = sv + (int64_t)grow * a.meta_stride;
     const float* srow = a.scores + (int64_t)grow * a.ld;
     __amdgpu_buffer_rsrc_t rs = make_rsrc(srow, (int64_t)nr * 4);
     bool ok = true, done = false;
-    if (all_mode) {
-      if (do_score) ok = wait_tags(svrow, wact, 1, tag[i], spin_limit);
-      if (ok) {
-        // ---- every score of the row into LDS (positions implicit)
-#pragma unroll 1
-        for (int base = 0; base < nr; base += NT * 16) {
-          uint32_t v[16];
+    if (all_mode(nr)) {
+      // ---- every key of the row in registers: thread t holds positions [t S, t S + S).
+      // Slot offsets past the row (or past S) point outside the buffer resource, where
+      // loads return 0 and stores are dropped.
+      constexpr int SA = ALL_MAX / NT;
+      constexpr int OOB = 0x7FFFFFF0;
+      const int S = (nr + NT - 1) / NT;
+      const int p0 = tid * S;
+      uint32_t kr[SA];
+      int offs[SA];
 #pragma unroll
-          for (int j = 0; j < 16; j++)
-            v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (base + j * NT + tid) * 4, 0, CP_COHERENT);
+      for (int j = 0; j < SA; j++) {
+        kr[j] = 0u;
+        offs[j] = (j < S && p0 + j < nr) ? (p0 + j) * 4 : OOB;
+      }
+      if (do_score) {
+        uint32_t* krow = allk + (int64_t)grow * a.all_stride;
+        __amdgpu_buffer_rsrc_t rk = make_rsrc(krow, (int64_t)nr * 4);
 #pragma unroll
-          for (int j = 0; j < 16; j++) {
-            const int p = base + j * NT + tid;
-            if (p < nr) FK[p] = radix_key(__uint_as_float(v[j]));
+        for (int g = 0; g < SA / 8; g++) {
+          if (g * 8 >= S) break;
+#pragma unroll
+          for (int jj = 0; jj < 8; jj++)
+            kr[g * 8 + jj] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, offs[g * 8 + jj], 0, CP_COHERENT);
+        }
+        int spins = 0;
+        while (true) {
+          bool miss = false;
+#pragma unroll
+          for (int g = 0; g < SA / 8; g++) {
+            if (g * 8 >= S) break;
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++) miss |= kr[g * 8 + jj] == 0u && offs[g * 8 + jj] != OOB;
+          }
+          if (!__syncthreads_or(miss)) break;
+          if (++spins >= spin_limit) { ok = false; break; }
+          __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+          for (int g = 0; g < SA / 8; g++) {
+            if (g * 8 >= S) break;
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++)
+              if (kr[g * 8 + jj] == 0u)
+                kr[g * 8 + jj] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, offs[g * 8 + jj], 0, CP_COHERENT);
           }
         }
-        __syncthreads();
-        int rem, ceq;
-        const uint32_t T = block_kth_lds(FK, nr, k, hist, misc, &rem, &ceq);
-        const int got = select_implicit(FK, nr, k, T, rem, ceq, bm, misc, out);
+        if (ok) {
+#pragma unroll
+          for (int g = 0; g < SA / 8; g++) {
+            if (g * 8 >= S) break;
+#pragma unroll
+            for (int jj = 0; jj < 8; jj++)
+              __builtin_amdgcn_raw_buffer_store_b32(0u, rk, offs[g * 8 + jj], 0, CP_COHERENT);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < SA / 8; g++) {
+          if (g * 8 >= S) break;
+#pragma unroll
+          for (int jj = 0; jj < 8; jj++) {
+            const int j = g * 8 + jj;
+            const uint32_t v = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, offs[j], 0, 0);
+            kr[j] = offs[j] != OOB ? radix_key(__uint_as_float(v)) : 0u;
+          }
+        }
+      }
+      if (ok) {
+        uint32_t T;
+        int rem;
+        int got = 0;
+        if (kth_regs<SA>(kr, S, 0u, k, hist, misc, &T, &rem))
+          got = emit_segments<SA>(kr, S, T, rem, out, k, misc, [&](int j) { return p0 + j; });
         if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
         done = true;
       }
-    } else {
-      const uint64_t* mrow = meta + (int64_t)grow * a.meta_stride;
-      ok = wait_tags(reinterpret_cast<const uint32_t*>(mrow) + 1, wact, 2, tag[i], spin_limit);
-      if (ok && nr <= BITMAP_KEYS && wact <= 4 * NT) {
-        __amdgpu_buffer_rsrc_t rmeta = make_rsrc(mrow, (int64_t)wact * 8);
-        __amdgpu_buffer_rsrc_t rtw = make_rsrc(twv + (int64_t)grow * a.meta_stride, (int64_t)wact * 4);
-        __amdgpu_buffer_rsrc_t rent =
-            make_rsrc(ent + (int64_t)grow * CAP_MAX * a.meta_stride, (int64_t)CAP_MAX * a.meta_stride * 8);
-        // ---- candidate counts (chunk w = tid + NT*u), thresholds, offsets
-        int cnt[4], offv[4];
-        uint32_t tw[4];
-        bool ov[4];
-        int E = 0;
+    } else if (thr_mode(nr)) {
+      // ---- chunk words: thread t reads the words of chunks t + NT u (u < upt)
+      const int upt = (wact + NT - 1) / NT;
+      const uint64_t* mrow = meta + (int64_t)grow * ms;
+      uint64_t* erow = ent + (int64_t)grow * es * CAP_MAX;
+      __amdgpu_buffer_rsrc_t rmeta = make_rsrc(mrow, (int64_t)wact * 8);
+      __amdgpu_buffer_rsrc_t rent = make_rsrc(erow, (int64_t)wact * CAP_MAX * 8);
+      uint64_t mv[4] = {0, 0, 0, 0};
+      {
+        int spins = 0;
+        while (true) {
+          bool miss = false;
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-          const int w = tid + NT * u;
-          uint32_t cwv = 0, t = 0;
-          if (w < wact) {
-            cwv = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rmeta, w * 8, 0, CP_COHERENT);
-            t = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rtw, w * 4, 0, CP_COHERENT);
+          for (int u = 0; u < 4; u++)
+            if (u < upt && tid + NT * u < wact && mv[u] == 0) {
+              mv[u] = __builtin_bit_cast(uint64_t,
+                                         __builtin_amdgcn_raw_buffer_load_b64(rmeta, (tid + NT * u) * 8, 0, CP_COHERENT));
+              miss |= mv[u] == 0;
+            }
+          if (!__syncthreads_or(miss)) break;
+          if (++spins >= spin_limit) { ok = false; break; }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      // per chunk (offset << 8 | count) into LDS; offsets in chunk order; t* = max t_w
+      uint32_t* co = LDS_PTR(uint32_t, L_CO);
+      bool any_ov = false;
+      uint32_t tmax = 0;
+      int E = 0;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        if (u >= upt) break;
+        const uint32_t lo = (uint32_t)mv[u];
+        const bool ov = (lo >> 16) & 1u;
+        const int cu = ov ? 0 : (int)(lo & 0xFFFFu);
+        any_ov |= ov;
+        const uint32_t twu = ov ? 0u : (uint32_t)(mv[u] >> 32);
+        int tot;
+        uint32_t mxu;
+        const int off = E + block_scan_max(cu, twu, misc, &tot, &mxu);
+        if (tid + NT * u < wact) co[tid + NT * u] = ((uint32_t)off << 8) | (uint32_t)cu;
+        E += tot;
+        tmax = tmax > mxu ? tmax : mxu;
+      }
+      any_ov = __syncthreads_or(any_ov);
+      if (ok) {
+        // ---- candidates into LDS in position order: wave v gathers chunks v + 8 i, one
+        // load per lane and chunk; a candidate still zero has not landed yet
+        bool late = false;
+#pragma unroll 1
+        for (int w0 = wv; w0 < wact; w0 += 4 * NWAVE) {
+          uint64_t e[4];
+          int2 cw[4];
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int w = w0 + q * NWAVE;
+            const uint32_t cv = (w < wact) ? co[w] : 0u;
+            cw[q] = make_int2((int)(cv & 0xFFu), (int)(cv >> 8));
+            e[q] = 0;
+            if (lane < cw[q].x)
+              e[q] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                                      rent, (w * CAP_MAX + lane) * 8, 0, CP_COHERENT));
           }
-          ov[u] = (cwv >> 16) & 1u;
-          cnt[u] = ov[u] ? 0 : (int)(cwv & 0xFFFFu);
-          tw[u] = t;
-        }
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-          int tot;
-          offv[u] = E + block_excl_scan(cnt[u], misc, &tot);
-          E += tot;
-        }
-        if (E <= FIN_ENT) {
-          // ---- gather every candidate, LOAD_BATCH loads in flight per thread
+          for (int q = 0; q < 4; q++) {
+            const int w = w0 + q * NWAVE;
+            int spins = 0;
+            while (__ballot(lane < cw[q].x && e[q] == 0) != 0) {
+              if (++spins >= spin_limit) { late = true; break; }
+              __builtin_amdgcn_s_sleep(1);
+              if (lane < cw[q].x && e[q] == 0)
+                e[q] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                                        rent, (w * CAP_MAX + lane) * 8, 0, CP_COHERENT));
+            }
+            if (lane < cw[q].x && cw[q].y + lane < FIN_ENT) {
+              FK[cw[q].y + lane] = (uint32_t)(e[q] >> 32);
+              FP[cw[q].y + lane] = (uint32_t)e[q];
+            }
+            // counts above 64 (large candidate caps): the rest of the chunk, slot by slot
 #pragma unroll 1
-          for (int u = 0; u < 4; u++) {
-            const int w = tid + NT * u;
-            const int cu = (w < wact) ? cnt[u] : 0;
-#pragma unroll 1
-            for (int j0 = 0; j0 < cu; j0 += LOAD_BATCH) {
-              v2i_t v[LOAD_BATCH];
-#pragma unroll
-              for (int j = 0; j < LOAD_BATCH; j++)
-                v[j] = (j0 + j < cu)
-                           ? __builtin_amdgcn_raw_buffer_load_b64(rent, ((j0 + j) * a.meta_stride + w) * 8, 0, CP_COHERENT)
-                           : v2i_t{0, 0};
-#pragma unroll
-              for (int j = 0; j < LOAD_BATCH; j++)
-                if (j0 + j < cu) {
-                  FK[offv[u] + j0 + j] = (uint32_t)v[j][1];
-                  FP[offv[u] + j0 + j] = (uint32_t)v[j][0];
-                }
+            for (int s0 = 64; s0 < cw[q].x; s0 += 64) {
+              const int sl = s0 + lane;
+              uint64_t x = 0;
+              int sp = 0;
+              while (true) {
+                if (sl < cw[q].x && x == 0)
+                  x = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                                       rent, (w * CAP_MAX + sl) * 8, 0, CP_COHERENT));
+                if (__ballot(sl < cw[q].x && x == 0) == 0) break;
+                if (++sp >= spin_limit) { late = true; break; }
+                __builtin_amdgcn_s_sleep(1);
+              }
+              if (sl < cw[q].x && cw[q].y + sl < FIN_ENT) {
+                FK[cw[q].y + sl] = (uint32_t)(x >> 32);
+                FP[cw[q].y + sl] = (uint32_t)x;
+              }
             }
           }
-          __syncthreads();
-          int rem = 0, ceq = 0;
-          uint32_t T = 0;
-          if (E >= k) T = block_kth_lds(FK, E, k, hist, misc, &rem, &ceq);
-          // ---- certificate: a chunk whose local threshold is above T may hold unseen
-          // keys >= T; list such chunks (with the threshold below which nothing was
-          // published) in the bitmap area, which is free until the emission
+        }
+        if (__syncthreads_or(late)) ok = false;
+      }
+      if (ok && !sv_done) { publish_sv(); sv_done = true; }
+      if (ok && E <= FIN_ENT) {
+        // ---- keys >= t* are all published (t* is at least every chunk's t_w), so if
+        // k of them are here the threshold is among them and no chunk can hide a key
+        // of the top k.  Thread t takes candidates [t S, t S + S), in position order.
+        constexpr int SE = FIN_ENT / NT;
+        const int S = (E + NT - 1) / NT;
+        const int e0 = tid * S;
+        uint32_t kr[SE];
+#pragma unroll
+        for (int j = 0; j < SE; j++) {
+          const uint32_t key = (j < S && e0 + j < E) ? FK[e0 + j] : 0u;
+          kr[j] = key >= tmax ? key : 0u;
+        }
+        uint32_t T;
+        int rem;
+        if (!any_ov && kth_regs<SE>(kr, S, tmax, k, hist, misc, &T, &rem)) {
+          const int got = emit_segments<SE>(kr, S, T, rem, out, k, misc, [&](int j) { return (int)FP[e0 + j]; });
+          if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
+          done = true;
+        } else if (nr <= BITMAP_KEYS) {
+          // ---- some chunk may hide keys of the top k: T0 = the k-th candidate (if
+          // there are k); a chunk with t_w above it (or that overflowed) is re-read for
+          // its unpublished keys >= T0
+#pragma unroll
+          for (int j = 0; j < SE; j++) kr[j] = (j < S && e0 + j < E) ? FK[e0 + j] : 0u;
+          const bool full = E >= k && kth_regs<SE>(kr, S, 0u, k, hist, misc, &T, &rem);
+          const uint32_t lowT = full ? (rem > 0 ? T : T + 1u) : 0u;
           int nfail = 0;
           {
-            int base = 0;
+            // the failing chunks, listed in the bitmap area after the (count, offset)
+            // pairs (which are no longer needed)
+            bool fail[4];
+            int fl = 0;
 #pragma unroll
             for (int u = 0; u < 4; u++) {
               const int w = tid + NT * u;
-              const bool fail = (w < wact) && ((E < k) || ov[u] || tw[u] > T);
-              int tot;
-              const int fo = base + block_excl_scan(fail ? 1 : 0, misc, &tot);
-              if (fail) {
-                bm[2 * fo] = (uint32_t)w;
-                bm[2 * fo + 1] = ov[u] ? 0xFFFFFFFFu : tw[u];
-              }
-              base += tot;
+              const bool ov = ((uint32_t)mv[u] >> 16) & 1u;
+              fail[u] = u < upt && w < wact && (!full || ov || (uint32_t)(mv[u] >> 32) > lowT);
+              fl += fail[u] ? 1 : 0;
             }
-            nfail = base;
+            __syncthreads();
+            uint32_t dummy;
+            int fo = block_scan_max(fl, 0u, misc, &nfail, &dummy);
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+              if (fail[u]) {
+                const bool ov = ((uint32_t)mv[u] >> 16) & 1u;
+                bm[2 * fo] = (uint32_t)(tid + NT * u);
+                bm[2 * fo + 1] = ov ? 0xFFFFFFFFu : (uint32_t)(mv[u] >> 32);
+                fo++;
+              }
             __syncthreads();
           }
-          if (nfail > 0) {
-            // ---- re-read failing chunks (once their scores are out): add their keys >= T
-            // that were not published
-            bool sv_ok = true;
-            if (do_score) {
-              int spins = 0;
-              while (true) {
-                bool mine = true;
-                for (int f = tid; f < nfail; f += NT) mine &= ld_co32(svrow + bm[2 * f]) == tag[i];
-                if (__syncthreads_and(mine)) break;
-                if (++spins >= spin_limit) { sv_ok = false; break; }
-                __builtin_amdgcn_s_sleep(1);
-              }
-            }
-            if (!sv_ok) {
-              ok = false;
-            } else {
-              const uint32_t lowT = (E >= k) ? T : 0u;
-              int Ecur = E;
-              bool overflow = false;
-#pragma unroll 1
-              for (int f = 0; f < nfail && !overflow; f++) {
-                const uint32_t w = bm[2 * f];
-                const uint32_t twf = bm[2 * f + 1];
-                const int p0 = (int)w * C;
-#pragma unroll 1
-                for (int base = 0; base < C; base += NT) {
-                  const int p = p0 + base + tid;
-                  bool take = false;
-                  uint32_t key = 0;
-                  if (base + tid < C && p < nr) {
-                    key = radix_key(__uint_as_float(
-                        (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, p * 4, 0, CP_COHERENT)));
-                    take = key >= lowT && (twf == 0xFFFFFFFFu || key < twf);
-                  }
-                  int tot;
-                  const int o = block_excl_scan(take ? 1 : 0, misc, &tot);
-                  if (Ecur + tot > FIN_ENT) { overflow = true; break; }
-                  if (take) { FK[Ecur + o] = key; FP[Ecur + o] = (uint32_t)p; }
-                  Ecur += tot;
-                }
-              }
-              __syncthreads();
-              if (!overflow && Ecur >= k) {
-                T = block_kth_lds(FK, Ecur, k, hist, misc, &rem, &ceq);
-                E = Ecur;
-                nfail = 0;
-              }
+          bool sv_ok = true;
+          if (do_score) {
+            // the failing chunks' scores must have reached memory
+            int spins = 0;
+            while (true) {
+              bool mine_ok = true;
+              for (int f = tid; f < nfail; f += NT) mine_ok &= ld_co32(sv + (int64_t)grow * ms + bm[2 * f]) != 0u;
+              if (__syncthreads_and(mine_ok)) break;
+              if (++spins >= spin_limit) { sv_ok = false; break; }
+              __builtin_amdgcn_s_sleep(1);
             }
           }
-          if (ok && nfail == 0) {
-            const int got = select_explicit(FK, FP, E, nr, k, T, rem, ceq, bm, misc, out);
-            if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
-            done = true;
+          if (!sv_ok) {
+            ok = false;
+          } else {
+            int Ecur = E;
+            bool overflow = false;
+#pragma unroll 1
+            for (int f = 0; f < nfail && !overflow; f++) {
+              const uint32_t w = bm[2 * f];
+              const uint32_t twf = bm[2 * f + 1];
+              const int p0 = (int)w * C;
+#pragma unroll 1
+              for (int base = 0; base < C; base += NT) {
+                const int p = p0 + base + tid;
+                bool take = false;
+                uint32_t key = 0;
+                if (base + tid < C && p < nr) {
+                  key = radix_key(__uint_as_float(
+                      (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, p * 4, 0, CP_COHERENT)));
+                  take = key >= lowT && (twf == 0xFFFFFFFFu || key < twf);
+                }
+                int tot;
+                const int oo = block_excl_scan(take ? 1 : 0, misc, &tot);
+                if (Ecur + tot > FIN_ENT) { overflow = true; break; }
+                if (take) { FK[Ecur + oo] = key; FP[Ecur + oo] = (uint32_t)p; }
+                Ecur += tot;
+              }
+            }
+            __syncthreads();
+            if (!overflow && Ecur >= k) {
+              const int S2 = (Ecur + NT - 1) / NT;
+              const int f0 = tid * S2;
+#pragma unroll
+              for (int j = 0; j < SE; j++) kr[j] = (j < S2 && f0 + j < Ecur) ? FK[f0 + j] : 0u;
+              if (kth_regs<SE>(kr, S2, 0u, k, hist, misc, &T, &rem)) {
+                const int got = select_explicit(FK, FP, Ecur, nr, k, T, rem, bm, misc, out);
+                if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
+                done = true;
+              }
+            }
           }
         }
       }
-      if (ok && !done && do_score) ok = wait_tags(svrow, wact, 1, tag[i], spin_limit);
+      // ---- clear this row's chunk words and candidates: wave v clears chunks v + 8 i
+      if (ok) {
+        __syncthreads();
+#pragma unroll 1
+        for (int w = wv; w < wact; w += NWAVE) {
+          const int cu = (int)(co[w] & 0xFFu);
+          for (int sl = lane; sl < cu; sl += 64) st_co64(erow + (int64_t)w * CAP_MAX + sl, 0ull);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+          if (u < upt && tid + NT * u < wact) st_co64(meta + (int64_t)grow * ms + tid + NT * u, 0ull);
+      }
+    }
+    if (ok && !sv_done) { publish_sv(); sv_done = true; }
+    if (ok && !done) {
+      // ---- exact multi-pass select over the row's scores in memory (all-mode rows
+      // are always done above, so sv_row(nr) holds when scoring)
+      if (do_score) ok = wait_nonzero(sv + (int64_t)grow * ms, wact, spin_limit);
+      if (ok) {
+        __syncthreads();
+        global_select_row(srow, nr, k, out, hist, misc);
+      }
+    }
+    if (ok && sv_row(nr)) {
+      // every chunk's "scores visible" word has been written: clear them
+      ok = wait_nonzero(sv + (int64_t)grow * ms, wact, spin_limit);
+      if (ok)
+        for (int w = tid; w < wact; w += NT) st_co32(sv + (int64_t)grow * ms + w, 0u);
     }
     if (!ok) {
       if (tid == 0) raise_error(ws, IDX_DERR_TIMEOUT);
       for (int p = tid; p < k; p += NT) out[p] = -1;
-    } else if (!done) {
-      __syncthreads();
-      global_select_row(srow, nr, k, out, hist, misc);
     }
     __syncthreads();
-    // a fresh tag for the next call on this row (also after a timeout, so that
-    // late arrival words of this call can never pass for the next call's)
-    if (tid == 0 && (do_score || !all_mode)) st_co32(epochs + grow, tag[i]);
   }
+  if (!sv_done) publish_sv();
 }
 
 __global__ void fill_kernel(uint32_t* p, int64_t words, uint32_t magic) {
@@ -1142,8 +1417,8 @@ Plan plan_topk(int max_keys) {
 }
 
 struct WsLayout {
-  uint64_t off_epoch, off_meta, off_tw, off_sv, off_ent, total;
-  int meta_stride;
+  uint64_t off_meta, off_sv, off_ent, off_allk, total;
+  int meta_stride, ent_stride, all_stride;
 };
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -1153,12 +1428,14 @@ WsLayout layout_for(int rows, int max_keys) {
   const int stride = (a.wg > b.wg ? a.wg : b.wg);
   WsLayout L;
   L.meta_stride = stride;
-  L.off_epoch = WS_HDR;
-  L.off_meta = align256(L.off_epoch + (uint64_t)rows * 4);
-  L.off_tw = align256(L.off_meta + (uint64_t)rows * stride * 8);
-  L.off_sv = align256(L.off_tw + (uint64_t)rows * stride * 4);
+  L.ent_stride = stride < 4 * NT ? stride : 4 * NT;
+  L.all_stride = (max_keys < ALL_MAX ? max_keys : ALL_MAX);
+  L.all_stride = L.all_stride < 4 ? 4 : (L.all_stride + 3) & ~3;
+  L.off_meta = WS_HDR;
+  L.off_sv = align256(L.off_meta + (uint64_t)rows * stride * 8);
   L.off_ent = align256(L.off_sv + (uint64_t)rows * stride * 4);
-  L.total = align256(L.off_ent + (uint64_t)rows * stride * CAP_MAX * 8);
+  L.off_allk = align256(L.off_ent + (uint64_t)rows * L.ent_stride * CAP_MAX * 8);
+  L.total = align256(L.off_allk + (uint64_t)rows * L.all_stride * 4);
   return L;
 }
 
@@ -1220,11 +1497,12 @@ void fill_common(KArgs& args, const WsLayout& L, void* ws, size_t ws_bytes) {
   args.spin_limit = g_spin_limit;
   args.skip_chunk = g_skip_chunk;
   args.meta_stride = L.meta_stride;
-  args.off_epoch = L.off_epoch;
+  args.ent_stride = L.ent_stride;
+  args.all_stride = L.all_stride;
   args.off_meta = L.off_meta;
-  args.off_tw = L.off_tw;
   args.off_ent = L.off_ent;
   args.off_sv = L.off_sv;
+  args.off_allk = L.off_allk;
 }
 
 int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int32_t* topk, void* ws,
@@ -1353,9 +1631,17 @@ int idx_device_status(void* ws, size_t ws_bytes, void* stream, uint32_t* detail)
   const uint32_t err = (hdr[0] != WS_MAGIC) ? (hdr[1] | IDX_DERR_WS) : hdr[1];
   if (detail) *detail = err;
   if (err) {
-    uint32_t zero = 0;
-    e = hipMemcpy(static_cast<uint8_t*>(ws) + WS_ERR_OFF, &zero, 4, hipMemcpyHostToDevice);
-    if (e != hipSuccess) return hip_fail(e);
+    if ((err & IDX_DERR_TIMEOUT) && hdr[0] == WS_MAGIC) {
+      // a timed-out exchange leaves words behind: start the workspace afresh
+      const int rc = idx_workspace_init(ws, ws_bytes & ~(size_t)255, stream);
+      if (rc) return rc;
+      e = hipStreamSynchronize(st);
+      if (e != hipSuccess) return hip_fail(e);
+    } else {
+      uint32_t zero = 0;
+      e = hipMemcpy(static_cast<uint8_t*>(ws) + WS_ERR_OFF, &zero, 4, hipMemcpyHostToDevice);
+      if (e != hipSuccess) return hip_fail(e);
+    }
     return IDX_EDEVICE;
   }
   return IDX_OK;
