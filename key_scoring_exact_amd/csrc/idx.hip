@@ -56,7 +56,7 @@ constexpr int LOOKAHEAD = 3;            // pages in flight ahead of the page bei
 constexpr int ALL_MAX = 24576;          // rows up to this many keys select from all scores at once
 constexpr int FIN_ENT = 12288;          // candidate capacity of a finishing workgroup
 constexpr int BITMAP_KEYS = 131072;     // positions covered by the finisher's LDS bitmap
-constexpr int CAP_MAX = 144;            // candidate slots per chunk and row
+constexpr int CAP_MAX = 128;            // candidate slots per chunk and row
 constexpr int LOAD_BATCH = 32;          // candidate loads in flight per thread
 constexpr uint32_t WS_MAGIC = 0x1D5C0DE5u;
 constexpr int DEFAULT_SPIN = 1 << 20;   // polls before a wait gives up (about a second)
@@ -75,14 +75,14 @@ constexpr int L_SCORE_END = L_W + GR * H * 2;
 constexpr int L_FK = 0;                                     // candidate keys: FIN_ENT
 constexpr int L_FP = FIN_ENT * 4;                           // positions: FIN_ENT
 constexpr int L_BM = FIN_ENT * 8;                           // bitmap: BITMAP_KEYS / 32 words
-constexpr int L_HIST = L_BM + BITMAP_KEYS / 8;              // 2 x 4096 u32 histograms
-constexpr int L_MISC = L_HIST + 2 * 4096 * 4;               // 64 u32 scratch
-constexpr int L_CO = L_MISC + 64 * 4;                       // per chunk: offset << 8 | count (4 NT)
-constexpr int L_FIN_END = L_CO + 4 * NT * 4;
+constexpr int HIST_WORDS = 4096 + 64;                       // one histogram: 4096 bins + 64 per-lane dummies
+constexpr int L_HIST = L_BM + BITMAP_KEYS / 8;              // 2 histograms
+constexpr int L_MISC = L_HIST + 2 * HIST_WORDS * 4;         // 64 u32 scratch
+constexpr int L_FIN_END = L_MISC + 64 * 4;
 constexpr int LDS_BYTES = (L_FIN_END > L_SCORE_END ? L_FIN_END : L_SCORE_END);
 static_assert(BITMAP_KEYS / 8 >= 4 * NT * 8, "the failing-chunk list (2 words a chunk) fits the bitmap");
 static_assert(ALL_MAX % NT == 0 && FIN_ENT % NT == 0, "register segments");
-static_assert(CAP_MAX < 256, "a chunk's candidate count is packed in 8 bits");
+static_assert(CAP_MAX <= 128, "a chunk's candidates are gathered in at most two 64-slot groups");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
 // workspace header (bytes)
@@ -190,49 +190,84 @@ __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int m) {
   return t;
 }
 
-__device__ inline int wave_incl_scan(int x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (l >= o) x += y;
-  }
-  return x;
+// ---------------------------------------------------------------------------
+// wave and workgroup primitives on DPP (VALU lane moves; no LDS round trips)
+// ---------------------------------------------------------------------------
+// DPP controls: row_shr:n = 0x110 + n (within rows of 16 lanes), row_bcast:15 = 0x142
+// (lane 15 of each row to the next row), row_bcast:31 = 0x143 (lane 31 to rows 2, 3).
+// A lane whose source is outside its row, or whose row is masked off, keeps `old`.
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROWMASK, 0xF, false);
 }
 
-// Exclusive scan over the workgroup; `tmp` is NWAVE ints of LDS.  Every thread must call.
-__device__ inline int block_excl_scan(int v, int* tmp, int* total) {
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  uint32_t v = (uint32_t)x;
+  v += dpp<0x111>(0u, v);
+  v += dpp<0x112>(0u, v);
+  v += dpp<0x114>(0u, v);
+  v += dpp<0x118>(0u, v);
+  v += dpp<0x142, 0xA>(0u, v);
+  v += dpp<0x143, 0xC>(0u, v);
+  return (int)v;
+}
+
+// within each row of 16 lanes, lane 15 ends up holding the row's max / min / sum
+__device__ __forceinline__ uint32_t row_max(uint32_t v) {
+  v = max(v, dpp<0x111>(v, v));
+  v = max(v, dpp<0x112>(v, v));
+  v = max(v, dpp<0x114>(v, v));
+  v = max(v, dpp<0x118>(v, v));
+  return v;
+}
+__device__ __forceinline__ uint32_t row_min(uint32_t v) {
+  v = min(v, dpp<0x111>(v, v));
+  v = min(v, dpp<0x112>(v, v));
+  v = min(v, dpp<0x114>(v, v));
+  v = min(v, dpp<0x118>(v, v));
+  return v;
+}
+__device__ __forceinline__ uint32_t row_sum(uint32_t v) {
+  v += dpp<0x111>(0u, v);
+  v += dpp<0x112>(0u, v);
+  v += dpp<0x114>(0u, v);
+  v += dpp<0x118>(0u, v);
+  return v;
+}
+__device__ __forceinline__ uint32_t rl(uint32_t v, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)v, l); }
+// wave-uniform results
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = row_max(v);
+  return max(max(rl(v, 15), rl(v, 31)), max(rl(v, 47), rl(v, 63)));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = row_min(v);
+  return min(min(rl(v, 15), rl(v, 31)), min(rl(v, 47), rl(v, 63)));
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v = row_sum(v);
+  return rl(v, 15) + rl(v, 31) + rl(v, 47) + rl(v, 63);
+}
+
+// Exclusive scan over the workgroup; `tmp` is NWAVE ints of LDS (16-byte aligned).
+// Every thread must call.
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   const int l = lane_id(), wv = threadIdx.x >> 6;
-  int x = wave_incl_scan(v);
+  const int x = wave_incl_scan(v);
   if (l == 63) tmp[wv] = x;
   __syncthreads();
+  const v4i a = reinterpret_cast<const v4i*>(tmp)[0];
+  const v4i b = reinterpret_cast<const v4i*>(tmp)[1];
+  const int t[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   int before = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < NWAVE; i++) {
-    int s = tmp[i];
-    before += (i < wv) ? s : 0;
-    tot += s;
+    before += (i < wv) ? t[i] : 0;
+    tot += t[i];
   }
   __syncthreads();
   if (total) *total = tot;
   return x - v + before;
-}
-
-__device__ inline uint32_t wave_min_u32(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t y = (uint32_t)__shfl_xor((int)x, o);
-    x = x < y ? x : y;
-  }
-  return x;
-}
-__device__ inline uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t y = (uint32_t)__shfl_xor((int)x, o);
-    x = x > y ? x : y;
-  }
-  return x;
 }
 
 // Histogram increment of one key per lane (when `m`), aggregated over the wave for
@@ -242,101 +277,108 @@ __device__ inline void hist_add(uint32_t* hist, bool m, uint32_t bin) {
   const uint64_t mb = __ballot(m);
   if (mb == 0) return;
   const int first = __ffsll((unsigned long long)mb) - 1;
-  const uint32_t lb = (uint32_t)__shfl((int)bin, first);
+  const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, first);
   const bool same = m && bin == lb;
   const uint64_t sb = __ballot(same);
   if (lane_id() == first) atomicAdd(&hist[lb], (uint32_t)__popcll(sb));
   if (m && !same) atomicAdd(&hist[bin], 1u);
 }
 
-// Radix digit search, part of kth_regs: the digit d of hist[0 .. nbins) (nbins a power
-// of two, <= 4096) holding the rem-th largest remaining key, counting from the top bin.
-// Writes misc[8] = d, misc[9] = rem left within d, misc[10] = count of d.  Every thread
-// must call; two barriers.
-__device__ inline void find_digit(const uint32_t* hist, int nbins, int rem, int* misc) {
+// Radix digit search: the digit d of hist[0 .. nbins) (nbins a power of two, <= 4096)
+// holding the rem-th largest remaining key, counting from the top bin.  Thread t scans
+// bins [nbins - 8 t - 8, nbins - 8 t).  Writes misc[8] = d, misc[9] = rem left within
+// d, misc[10] = count of d.  Every thread must call; two barriers.
+__device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, int rem, int* misc) {
   const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
-  const int bpt = nbins > NT ? nbins / NT : 1;        // bins per thread, from the top
-  const int hi = nbins - 1 - tid * bpt;               // this thread's highest bin
+  const int base = nbins - 8 * (tid + 1);
+  uint32_t h[8];
+  if (base >= 0) {
+    const v4i a = *reinterpret_cast<const v4i*>(hist + base);
+    const v4i b = *reinterpret_cast<const v4i*>(hist + base + 4);
+    h[0] = a[0]; h[1] = a[1]; h[2] = a[2]; h[3] = a[3];
+    h[4] = b[0]; h[5] = b[1]; h[6] = b[2]; h[7] = b[3];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; i++) h[i] = (base + i >= 0) ? hist[base + i] : 0u;
+  }
   int c = 0;
-  if (hi >= 0)
-    for (int i = 0; i < bpt; i++) c += (int)hist[hi - i];
+#pragma unroll
+  for (int i = 0; i < 8; i++) c += (int)h[i];
   const int incl = wave_incl_scan(c);
   if (lane == 63) misc[wv] = incl;
   __syncthreads();
+  const v4i ta = reinterpret_cast<const v4i*>(misc)[0];
+  const v4i tb = reinterpret_cast<const v4i*>(misc)[1];
+  const int t[8] = {ta[0], ta[1], ta[2], ta[3], tb[0], tb[1], tb[2], tb[3]};
   int before = incl - c;
 #pragma unroll
-  for (int i = 0; i < NWAVE; i++) before += (i < wv) ? misc[i] : 0;
+  for (int i = 0; i < NWAVE; i++) before += (i < wv) ? t[i] : 0;
   if (c > 0 && before < rem && rem <= before + c) {
-    int b = hi, r = rem - before;
-    for (int i = 0; i < bpt; i++, b--) {
-      const int h = (int)hist[b];
-      if (r <= h) break;
-      r -= h;
+    int r = rem - before, d = base + 7, dc = (int)h[7];
+#pragma unroll
+    for (int i = 7; i >= 0; i--) {
+      if (r <= (int)h[i]) { d = base + i; dc = (int)h[i]; break; }
+      r -= (int)h[i];
     }
-    misc[8] = b;
+    misc[8] = d;
     misc[9] = r;
-    misc[10] = (int)hist[b];
+    misc[10] = dc;
   }
   __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
 // Exact k-th largest of the keys held in registers across the workgroup: thread t
-// holds kr[0 .. S) (slots past S hold 0), a zero key is absent, and only keys >= lo
-// count.  Radix select over the bits below the common prefix of the smallest and
-// largest counted key, in digits of up to 12 bits from the top, histograms in LDS
-// (hist: 2 x 4096 words).  Returns false if fewer than k keys count.  Otherwise the
-// top k of the counted keys (score descending, then position) are exactly: every key
-// > *T, then the first *rem keys equal to *T in position order (*rem may be 0).
-// Slots are visited in groups of 8, skipping whole groups past S.  Every thread must
-// call.
+// holds kr[0 .. S) (slots past S hold 0); a zero key is absent.  Radix select over the
+// bits below the common prefix of the smallest and largest key, in digits of up to 12
+// bits from the top, histograms in LDS (hist: 2 x HIST_WORDS words).  Returns false
+// if fewer than k keys are present.  Otherwise the top k (score descending, then
+// position) are exactly: every key > *T, then the first *rem keys equal to *T in
+// position order (*rem may be 0).  Slots are visited in groups of 8, skipping whole
+// groups past S.  Every thread must call.
 // ---------------------------------------------------------------------------
 template <int SMAX>
-__device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, uint32_t lo, int k, uint32_t* hist,
-                                         int* misc, uint32_t* T_out, int* rem_out) {
+__device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, int k, uint32_t* hist, int* misc,
+                                         uint32_t* T_out, int* rem_out) {
   static_assert(SMAX % 8 == 0, "slot groups of 8");
   const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
-  lo = lo > 1u ? lo : 1u;
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  int cnt = 0;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u, cnt = 0;
 #pragma unroll
   for (int g = 0; g < SMAX / 8; g++) {
     if (g * 8 >= S) break;
 #pragma unroll
     for (int jj = 0; jj < 8; jj++) {
       const uint32_t key = kr[g * 8 + jj];
-      const bool v = key >= lo;
-      mn = (v && key < mn) ? key : mn;
-      mx = (v && key > mx) ? key : mx;
-      cnt += v ? 1 : 0;
+      mn = min(mn, key == 0u ? 0xFFFFFFFFu : key);
+      mx = max(mx, key);
+      cnt += key != 0u ? 1u : 0u;
     }
   }
   mn = wave_min_u32(mn);
   mx = wave_max_u32(mx);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+  cnt = wave_sum_u32(cnt);
   uint32_t* red = reinterpret_cast<uint32_t*>(misc) + 16;
   if (lane == 0) {
     red[wv] = mn;
     red[NWAVE + wv] = mx;
-    red[2 * NWAVE + wv] = (uint32_t)cnt;
+    red[2 * NWAVE + wv] = cnt;
   }
   {
-    v4i z = {0, 0, 0, 0};
+    const v4i z = {0, 0, 0, 0};
     v4i* h4 = reinterpret_cast<v4i*>(hist);
-    h4[tid] = z;                                        // first histogram buffer (4096 words)
+    h4[tid] = z;                                        // bins of the first buffer
     h4[tid + NT] = z;
   }
   __syncthreads();
   cnt = 0;
 #pragma unroll
   for (int i = 0; i < NWAVE; i++) {
-    mn = mn < red[i] ? mn : red[i];
-    mx = mx > red[NWAVE + i] ? mx : red[NWAVE + i];
-    cnt += (int)red[2 * NWAVE + i];
+    mn = min(mn, red[i]);
+    mx = max(mx, red[NWAVE + i]);
+    cnt += red[2 * NWAVE + i];
   }
-  if (cnt < k) return false;
-  if (mn == mx) {  // every counted key equal: the first k of them
+  if ((int)cnt < k) return false;
+  if (mn == mx) {  // every key equal: the first k of them
     *T_out = mn;
     *rem_out = k;
     return true;
@@ -348,24 +390,26 @@ __device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, uint
   const int npass = (nb + 11) / 12;
   const int wdef = (nb + npass - 1) / npass;
   int rem = k, shift = nb, buf = 0;
+  const uint32_t dummy = 4096u + (uint32_t)lane;
   while (true) {
     const int width = wdef < shift ? wdef : shift;
     shift -= width;
     const uint32_t dmask = (1u << width) - 1u;
-    uint32_t* h = hist + buf * 4096;
+    uint32_t* h = hist + buf * HIST_WORDS;
 #pragma unroll
     for (int g = 0; g < SMAX / 8; g++) {
       if (g * 8 >= S) break;
 #pragma unroll
       for (int jj = 0; jj < 8; jj++) {
         const uint32_t key = kr[g * 8 + jj];
-        if (key >= lo && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & dmask], 1u);
+        const bool m = key != 0u && (key & mask) == prefix;
+        atomicAdd(&h[m ? (key >> shift) & dmask : dummy], 1u);
       }
     }
     {
       // the other buffer is free: clear it for the next pass
-      v4i z = {0, 0, 0, 0};
-      v4i* h4 = reinterpret_cast<v4i*>(hist + (buf ^ 1) * 4096);
+      const v4i z = {0, 0, 0, 0};
+      v4i* h4 = reinterpret_cast<v4i*>(hist + (buf ^ 1) * HIST_WORDS);
       h4[tid] = z;
       h4[tid + NT] = z;
     }
@@ -393,13 +437,15 @@ __device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, uint
 }
 
 // Emission of the top k in segment order (thread t's slots j < S precede thread t + 1's;
-// the caller lays positions out ascending in that order; slots past S hold 0): a key
-// is selected when key > T, or key == T and it is among the first rem such keys.
-// out[0 .. k) receives the selected positions (pos_of(j)).  Returns the number
-// selected.  Every thread must call.
+// the caller lays positions out ascending in that order; absent slots hold key 0): a
+// key is selected when key > T, or key == T and it is among the first rem such keys.
+// out[0 .. k) receives the selected positions pos_of(j) (stores of unselected slots go
+// outside the buffer resource and are dropped).  Returns the number selected.  Every
+// thread must call.
 template <int SMAX, typename PosF>
 __device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], int S, uint32_t T, int rem, int32_t* out,
                                              int k, int* misc, PosF pos_of) {
+  constexpr int OOB = 0x7FFFFFF0;
   int gt = 0, eq = 0;
 #pragma unroll
   for (int g = 0; g < SMAX / 8; g++) {
@@ -414,22 +460,20 @@ __device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], int S, 
   int tot;
   const int packed = block_excl_scan(gt | (eq << 16), misc, &tot);
   const int before_gt = packed & 0xFFFF, before_eq = packed >> 16;
-  if (gt + (eq > 0 ? 1 : 0) > 0) {
-    int o = before_gt + (before_eq < rem ? before_eq : rem);
-    int er = before_eq;
+  __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (int64_t)k * 4);
+  int o = before_gt + (before_eq < rem ? before_eq : rem);
+  int er = before_eq;
 #pragma unroll
-    for (int g = 0; g < SMAX / 8; g++) {
-      if (g * 8 >= S) break;
+  for (int g = 0; g < SMAX / 8; g++) {
+    if (g * 8 >= S) break;
 #pragma unroll
-      for (int jj = 0; jj < 8; jj++) {
-        const uint32_t key = kr[g * 8 + jj];
-        bool sel = key > T;
-        if (key == T) sel = er++ < rem;
-        if (sel) {
-          if (o < k) out[o] = pos_of(g * 8 + jj);
-          o++;
-        }
-      }
+    for (int jj = 0; jj < 8; jj++) {
+      const uint32_t key = kr[g * 8 + jj];
+      const bool e = key == T;
+      const bool sel = key > T || (e && er < rem);
+      er += e ? 1 : 0;
+      __builtin_amdgcn_raw_buffer_store_b32(pos_of(g * 8 + jj), ro, (sel && o < k) ? o * 4 : OOB, 0, 0);
+      o += sel ? 1 : 0;
     }
   }
   const int tg = tot & 0xFFFF, te = tot >> 16;
@@ -776,6 +820,193 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
+// Sum over the workgroup (wave-uniform result).  Every thread must call.
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, int* misc) {
+  v = wave_sum_u32(v);
+  if (lane_id() == 0) misc[threadIdx.x >> 6] = (int)v;
+  __syncthreads();
+  const v4i a = reinterpret_cast<const v4i*>(misc)[0];
+  const v4i b = reinterpret_cast<const v4i*>(misc)[1];
+  __syncthreads();
+  return (uint32_t)(a[0] + a[1] + a[2] + a[3] + b[0] + b[1] + b[2] + b[3]);
+}
+
+// t[0] and t[2] summed, t[1] maxed over the workgroup.  Every thread must call.
+__device__ __forceinline__ void block_sum_max_sum(uint32_t (&t)[3], int* misc) {
+  const uint32_t a = wave_sum_u32(t[0]), b = wave_max_u32(t[1]), c = wave_sum_u32(t[2]);
+  const int wv = threadIdx.x >> 6;
+  if (lane_id() == 0) {
+    misc[wv] = (int)a;
+    misc[NWAVE + wv] = (int)b;
+    misc[2 * NWAVE + wv] = (int)c;
+  }
+  __syncthreads();
+  uint32_t sa = 0, mb = 0, sc = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; i++) {
+    sa += (uint32_t)misc[i];
+    mb = max(mb, (uint32_t)misc[NWAVE + i]);
+    sc += (uint32_t)misc[2 * NWAVE + i];
+  }
+  __syncthreads();
+  t[0] = sa;
+  t[1] = mb;
+  t[2] = sc;
+}
+
+// The row's published candidates into LDS in position order: FK[e] = key, FP[e] =
+// position for e < *E (entries past FIN_ENT are counted, not stored).  Chunk w's
+// candidates sit at erow[w * CAP_MAX + s], s < its count <= 64 SLOTS (slots past the
+// count are zero); rcount[r] is the sum of the counts of the chunks of round r, NWAVE *
+// CPW chunks a round.  In round r wave v reads chunks r NWAVE CPW + v CPW + q (q < CPW),
+// SLOTS loads per lane and chunk, all in flight together.  A zero slot is past its
+// chunk's count or not landed yet, so a round is complete once its nonzero slots add
+// up to rcount[r].  Each candidate read is cleared behind.  Returns false on a
+// timeout.  Every thread must call.
+template <int SLOTS>
+__device__ __forceinline__ bool gather_candidates(uint64_t* erow, int wact, const int* rcount, int spin_limit,
+                                                  uint32_t* FK, uint32_t* FP, int* misc, int* E_out) {
+  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  constexpr int CPW = 32 / SLOTS;
+  constexpr int L = CPW * SLOTS;
+  __amdgpu_buffer_rsrc_t rent = make_rsrc(erow, (int64_t)wact * CAP_MAX * 8);
+  const int rounds = (wact + NWAVE * CPW - 1) / (NWAVE * CPW);
+  auto soff = [&](int wbase, int i) { return ((wbase + i / SLOTS) * CAP_MAX + (i % SLOTS) * 64) * 8; };
+  int base = 0;
+#pragma unroll 1
+  for (int r = 0; r < rounds; r++) {
+    const int wbase = r * NWAVE * CPW + wv * CPW;
+    const int expect = rcount[r];
+    uint64_t e[L];
+#pragma unroll
+    for (int i = 0; i < L; i++)
+      e[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rent, lane * 8, soff(wbase, i), CP_COHERENT));
+    int spins = 0;
+    while (true) {
+      uint32_t nz = 0;
+#pragma unroll
+      for (int i = 0; i < L; i++) nz += (uint32_t)__popcll(__ballot(e[i] != 0));
+      if ((int)block_sum(lane == 0 ? nz : 0u, misc) == expect) break;
+      if (++spins >= spin_limit) return false;
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int i = 0; i < L; i++)
+        if (e[i] == 0)
+          e[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rent, lane * 8, soff(wbase, i), CP_COHERENT));
+    }
+    // compaction in position order: wave-local offsets by ballot, then wave bases
+    uint32_t tot = 0;
+#pragma unroll
+    for (int i = 0; i < L; i++) tot += (uint32_t)__popcll(__ballot(e[i] != 0));
+    if (lane == 0) misc[16 + wv] = (int)tot;
+    __syncthreads();
+    int o = base;
+#pragma unroll
+    for (int i = 0; i < NWAVE; i++) o += (i < wv) ? misc[16 + i] : 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < L; i++) {
+      const uint64_t bal = __ballot(e[i] != 0);
+      if (e[i] != 0) {
+        const int slot = o + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        if (slot < FIN_ENT) {
+          FK[slot] = (uint32_t)(e[i] >> 32);
+          FP[slot] = (uint32_t)e[i];
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(v2i_t{0, 0}, rent, lane * 8, soff(wbase, i), CP_COHERENT);
+      }
+      o += (int)__popcll(bal);
+    }
+    base += expect;
+  }
+  __syncthreads();
+  *E_out = base;
+  return true;
+}
+
+// Candidate path when the certificate fails.  T0 = the k-th candidate (if there are
+// k); every chunk whose local threshold t_w (tw[w], 0xFFFFFFFF when it published
+// nothing) is above T0 is re-read from the row's scores for its unpublished keys >= T0,
+// after which every key >= T0 of the row is a candidate, and the top k is taken from
+// that set through a position bitmap.  Returns 1 when it selected, 0 to fall back to the
+// multi-pass select over memory, -1 on a timeout.  Every thread must call.
+__device__ __forceinline__ int rare_select(const KArgs& a, int grow, int nr, int k, int wact, int E, int C,
+                                        __amdgpu_buffer_rsrc_t rs, const uint32_t* svrow, bool do_score,
+                                        int spin_limit, uint32_t* FK, uint32_t* FP, uint32_t* bm, uint32_t* hist,
+                                        int* misc, int32_t* out) {
+  (void)a;
+  (void)grow;
+  const int tid = threadIdx.x;
+  constexpr int SR = 32;
+  uint32_t kr[SR];
+  auto load_keys = [&](int n_ent) {
+    int S = (n_ent + NT - 1) / NT;
+    S |= 1;
+    const int e0 = tid * S;
+#pragma unroll
+    for (int j = 0; j < SR; j++) kr[j] = (j < S && e0 + j < n_ent) ? FK[e0 + j] : 0u;
+    return S;
+  };
+  uint32_t T = 0;
+  int rem = 0;
+  const int S0 = load_keys(E);
+  const bool full = E >= k && kth_regs<SR>(kr, S0, k, hist, misc, &T, &rem);
+  const uint32_t lowT = full ? (rem > 0 ? T : T + 1u) : 0u;
+  // failing chunks listed in bm[4 NT ...] (tw[] occupies bm[0 .. 4 NT))
+  uint32_t* fl = bm + 4 * NT;
+  int nfail = 0;
+  for (int w0 = 0; w0 < wact; w0 += NT) {
+    const int w = w0 + tid;
+    const bool f = w < wact && (!full || bm[w] > lowT);
+    int tot;
+    const int o = block_excl_scan(f ? 1 : 0, misc, &tot);
+    if (f) fl[nfail + o] = (uint32_t)w;
+    nfail += tot;
+  }
+  __syncthreads();
+  if (do_score) {
+    // the failing chunks' scores must have reached memory
+    int spins = 0;
+    while (true) {
+      bool mine_ok = true;
+      for (int f = tid; f < nfail; f += NT) mine_ok &= ld_co32(svrow + fl[f]) != 0u;
+      if (__syncthreads_and(mine_ok)) break;
+      if (++spins >= spin_limit) return -1;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  int Ecur = E;
+#pragma unroll 1
+  for (int f = 0; f < nfail; f++) {
+    const uint32_t w = fl[f];
+    const uint32_t twf = bm[w];
+    const int p0 = (int)w * C;
+#pragma unroll 1
+    for (int base = 0; base < C; base += NT) {
+      const int p = p0 + base + tid;
+      bool take = false;
+      uint32_t key = 0;
+      if (base + tid < C && p < nr) {
+        key = radix_key(__uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, p * 4, 0, CP_COHERENT)));
+        take = key >= lowT && key < twf;
+      }
+      int tot;
+      const int oo = block_excl_scan(take ? 1 : 0, misc, &tot);
+      if (Ecur + tot > FIN_ENT) return 0;
+      if (take) { FK[Ecur + oo] = key; FP[Ecur + oo] = (uint32_t)p; }
+      Ecur += tot;
+    }
+  }
+  __syncthreads();
+  if (Ecur < k) return 0;
+  const int S1 = load_keys(Ecur);
+  if (!kth_regs<SR>(kr, S1, k, hist, misc, &T, &rem)) return 0;
+  const int got = select_explicit(FK, FP, Ecur, nr, k, T, rem, bm, misc, out);
+  if (got != k && tid == 0) raise_error(a.ws, IDX_DERR_SELECT);
+  return 1;
+}
+
 // x[u] for a runtime u < 4 without indexing registers
 __device__ inline int pick4(const int (&x)[4], int u) {
   return u == 0 ? x[0] : u == 1 ? x[1] : u == 2 ? x[2] : x[3];
@@ -791,13 +1022,15 @@ __device__ inline int block_scan_max(int v, uint32_t m, int* misc, int* total, u
   __syncthreads();
   int before = 0, tot = 0;
   uint32_t mx = 0;
+  const v4i* m4 = reinterpret_cast<const v4i*>(misc);
+  const v4i s0 = m4[0], s1 = m4[1], x0 = m4[2], x1 = m4[3];
+  const int sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  const int xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
 #pragma unroll
   for (int i = 0; i < NWAVE; i++) {
-    const int s = misc[i];
-    before += (i < wv) ? s : 0;
-    tot += s;
-    const uint32_t mi = (uint32_t)misc[NWAVE + i];
-    mx = mx > mi ? mx : mi;
+    before += (i < wv) ? sv[i] : 0;
+    tot += sv[i];
+    mx = mx > (uint32_t)xv[i] ? mx : (uint32_t)xv[i];
   }
   __syncthreads();
   *total = tot;
@@ -1046,91 +1279,71 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
     }
     const float* srow = a.scores + (int64_t)grow * a.ld;
     __amdgpu_buffer_rsrc_t rs = make_rsrc(srow, (int64_t)nr * 4);
-    bool ok = true, done = false;
+    bool ok = true, done = false, implicit = false, cert = false;
+    int E = 0;                 // candidates in LDS, in position order
+    uint32_t lo = 0;           // candidates below lo do not count
+    const uint64_t* mrow = meta + (int64_t)grow * ms;
+    uint64_t* erow = ent + (int64_t)grow * es * CAP_MAX;
     if (all_mode(nr)) {
-      // ---- every key of the row in registers: thread t holds positions [t S, t S + S).
-      // Slot offsets past the row (or past S) point outside the buffer resource, where
-      // loads return 0 and stores are dropped.
-      constexpr int SA = ALL_MAX / NT;
-      constexpr int OOB = 0x7FFFFFF0;
-      const int S = (nr + NT - 1) / NT;
-      const int p0 = tid * S;
-      uint32_t kr[SA];
-      int offs[SA];
-#pragma unroll
-      for (int j = 0; j < SA; j++) {
-        kr[j] = 0u;
-        offs[j] = (j < S && p0 + j < nr) ? (p0 + j) * 4 : OOB;
-      }
+      // ---- every key of the row into LDS (FK[p] for position p), coalesced: thread t
+      // reads positions t + NT j.  Positions past the row are outside the buffer
+      // resource: their loads return 0 and their stores are dropped.
+      constexpr int JA = ALL_MAX / NT;
+      const int J = (nr + NT - 1) / NT;
       if (do_score) {
         uint32_t* krow = allk + (int64_t)grow * a.all_stride;
         __amdgpu_buffer_rsrc_t rk = make_rsrc(krow, (int64_t)nr * 4);
+        uint32_t kv[JA];
 #pragma unroll
-        for (int g = 0; g < SA / 8; g++) {
-          if (g * 8 >= S) break;
-#pragma unroll
-          for (int jj = 0; jj < 8; jj++)
-            kr[g * 8 + jj] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, offs[g * 8 + jj], 0, CP_COHERENT);
-        }
+        for (int j = 0; j < JA; j++)
+          kv[j] = j < J ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, tid * 4, j * NT * 4, CP_COHERENT) : 0u;
+        // every key has landed once nr of them are nonzero
         int spins = 0;
         while (true) {
-          bool miss = false;
+          uint32_t nz = 0;
 #pragma unroll
-          for (int g = 0; g < SA / 8; g++) {
-            if (g * 8 >= S) break;
-#pragma unroll
-            for (int jj = 0; jj < 8; jj++) miss |= kr[g * 8 + jj] == 0u && offs[g * 8 + jj] != OOB;
-          }
-          if (!__syncthreads_or(miss)) break;
+          for (int j = 0; j < JA; j++) nz += kv[j] != 0u ? 1u : 0u;
+          if (block_sum(nz, misc) == (uint32_t)nr) break;
           if (++spins >= spin_limit) { ok = false; break; }
           __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-          for (int g = 0; g < SA / 8; g++) {
-            if (g * 8 >= S) break;
-#pragma unroll
-            for (int jj = 0; jj < 8; jj++)
-              if (kr[g * 8 + jj] == 0u)
-                kr[g * 8 + jj] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, offs[g * 8 + jj], 0, CP_COHERENT);
-          }
+          for (int j = 0; j < JA; j++)
+            if (j < J && kv[j] == 0u)
+              kv[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, tid * 4, j * NT * 4, CP_COHERENT);
         }
+#pragma unroll
+        for (int j = 0; j < JA; j++)
+          if (j < J) FK[j * NT + tid] = kv[j];
         if (ok) {
 #pragma unroll
-          for (int g = 0; g < SA / 8; g++) {
-            if (g * 8 >= S) break;
-#pragma unroll
-            for (int jj = 0; jj < 8; jj++)
-              __builtin_amdgcn_raw_buffer_store_b32(0u, rk, offs[g * 8 + jj], 0, CP_COHERENT);
-          }
+          for (int j = 0; j < JA; j++)
+            if (j < J) __builtin_amdgcn_raw_buffer_store_b32(0u, rk, tid * 4, j * NT * 4, CP_COHERENT);
         }
       } else {
+        uint32_t kv[JA];
 #pragma unroll
-        for (int g = 0; g < SA / 8; g++) {
-          if (g * 8 >= S) break;
+        for (int j = 0; j < JA; j++)
+          kv[j] = j < J ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, tid * 4, j * NT * 4, 0) : 0u;
 #pragma unroll
-          for (int jj = 0; jj < 8; jj++) {
-            const int j = g * 8 + jj;
-            const uint32_t v = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, offs[j], 0, 0);
-            kr[j] = offs[j] != OOB ? radix_key(__uint_as_float(v)) : 0u;
-          }
-        }
+        for (int j = 0; j < JA; j++)
+          if (j < J) FK[j * NT + tid] = radix_key(__uint_as_float(kv[j]));
       }
-      if (ok) {
-        uint32_t T;
-        int rem;
-        int got = 0;
-        if (kth_regs<SA>(kr, S, 0u, k, hist, misc, &T, &rem))
-          got = emit_segments<SA>(kr, S, T, rem, out, k, misc, [&](int j) { return p0 + j; });
-        if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
-        done = true;
-      }
+      __syncthreads();
+      E = nr;
+      implicit = true;
+      cert = true;
     } else if (thr_mode(nr)) {
       // ---- chunk words: thread t reads the words of chunks t + NT u (u < upt)
       const int upt = (wact + NT - 1) / NT;
-      const uint64_t* mrow = meta + (int64_t)grow * ms;
-      uint64_t* erow = ent + (int64_t)grow * es * CAP_MAX;
       __amdgpu_buffer_rsrc_t rmeta = make_rsrc(mrow, (int64_t)wact * 8);
-      __amdgpu_buffer_rsrc_t rent = make_rsrc(erow, (int64_t)wact * CAP_MAX * 8);
       uint64_t mv[4] = {0, 0, 0, 0};
+      // candidates per gather round (256 chunks a round, or 128 when a chunk may post
+      // more than 64)
+      int m_unused, cap;
+      candidate_params(nr, C, k, &m_unused, &cap);
+      const int rshift = cap > 64 ? 7 : 8;
+      int* rcount = misc + 40;
+      if (tid < 16) rcount[tid] = 0;
       {
         int spins = 0;
         while (true) {
@@ -1147,208 +1360,76 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
           __builtin_amdgcn_s_sleep(1);
         }
       }
-      // per chunk (offset << 8 | count) into LDS; offsets in chunk order; t* = max t_w
-      uint32_t* co = LDS_PTR(uint32_t, L_CO);
-      bool any_ov = false;
-      uint32_t tmax = 0;
-      int E = 0;
+      // E = candidates published, t* = the largest t_w, whether any chunk overflowed;
+      // bm[w] = t_w (0xFFFFFFFF: overflowed, published nothing) for the rare path
+      uint32_t pub = 0, tmax = 0, ovs = 0;
 #pragma unroll
       for (int u = 0; u < 4; u++) {
-        if (u >= upt) break;
-        const uint32_t lo = (uint32_t)mv[u];
-        const bool ov = (lo >> 16) & 1u;
-        const int cu = ov ? 0 : (int)(lo & 0xFFFFu);
-        any_ov |= ov;
-        const uint32_t twu = ov ? 0u : (uint32_t)(mv[u] >> 32);
-        int tot;
-        uint32_t mxu;
-        const int off = E + block_scan_max(cu, twu, misc, &tot, &mxu);
-        if (tid + NT * u < wact) co[tid + NT * u] = ((uint32_t)off << 8) | (uint32_t)cu;
-        E += tot;
-        tmax = tmax > mxu ? tmax : mxu;
+        if (u >= upt || tid + NT * u >= wact) break;
+        const uint32_t lw = (uint32_t)mv[u];
+        const bool ov = (lw >> 16) & 1u;
+        const uint32_t twu = (uint32_t)(mv[u] >> 32);
+        pub += ov ? 0u : (lw & 0xFFFFu);
+        if (!ov) atomicAdd(&rcount[(tid + NT * u) >> rshift], (int)(lw & 0xFFFFu));
+        ovs += ov ? 1u : 0u;
+        if (!ov) tmax = max(tmax, twu);
+        bm[tid + NT * u] = ov ? 0xFFFFFFFFu : twu;
       }
-      any_ov = __syncthreads_or(any_ov);
+      uint32_t t3[3] = {pub, tmax, ovs};
+      block_sum_max_sum(t3, misc);
+      pub = t3[0];
+      tmax = t3[1];
+      ovs = t3[2];
+      // keys >= t* are all published (t* is at least every chunk's t_w): if k of them
+      // are here, the k-th is among them and no chunk hides a key of the top k
+      lo = tmax;
       if (ok) {
-        // ---- candidates into LDS in position order: wave v gathers chunks v + 8 i, one
-        // load per lane and chunk; a candidate still zero has not landed yet
-        bool late = false;
-#pragma unroll 1
-        for (int w0 = wv; w0 < wact; w0 += 4 * NWAVE) {
-          uint64_t e[4];
-          int2 cw[4];
-#pragma unroll
-          for (int q = 0; q < 4; q++) {
-            const int w = w0 + q * NWAVE;
-            const uint32_t cv = (w < wact) ? co[w] : 0u;
-            cw[q] = make_int2((int)(cv & 0xFFu), (int)(cv >> 8));
-            e[q] = 0;
-            if (lane < cw[q].x)
-              e[q] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
-                                                      rent, (w * CAP_MAX + lane) * 8, 0, CP_COHERENT));
-          }
-#pragma unroll
-          for (int q = 0; q < 4; q++) {
-            const int w = w0 + q * NWAVE;
-            int spins = 0;
-            while (__ballot(lane < cw[q].x && e[q] == 0) != 0) {
-              if (++spins >= spin_limit) { late = true; break; }
-              __builtin_amdgcn_s_sleep(1);
-              if (lane < cw[q].x && e[q] == 0)
-                e[q] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
-                                                        rent, (w * CAP_MAX + lane) * 8, 0, CP_COHERENT));
-            }
-            if (lane < cw[q].x && cw[q].y + lane < FIN_ENT) {
-              FK[cw[q].y + lane] = (uint32_t)(e[q] >> 32);
-              FP[cw[q].y + lane] = (uint32_t)e[q];
-            }
-            // counts above 64 (large candidate caps): the rest of the chunk, slot by slot
-#pragma unroll 1
-            for (int s0 = 64; s0 < cw[q].x; s0 += 64) {
-              const int sl = s0 + lane;
-              uint64_t x = 0;
-              int sp = 0;
-              while (true) {
-                if (sl < cw[q].x && x == 0)
-                  x = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(
-                                                       rent, (w * CAP_MAX + sl) * 8, 0, CP_COHERENT));
-                if (__ballot(sl < cw[q].x && x == 0) == 0) break;
-                if (++sp >= spin_limit) { late = true; break; }
-                __builtin_amdgcn_s_sleep(1);
-              }
-              if (sl < cw[q].x && cw[q].y + sl < FIN_ENT) {
-                FK[cw[q].y + sl] = (uint32_t)(x >> 32);
-                FP[cw[q].y + sl] = (uint32_t)x;
-              }
-            }
-          }
-        }
-        if (__syncthreads_or(late)) ok = false;
+        if (cap > 64) ok = gather_candidates<2>(erow, wact, rcount, spin_limit, FK, FP, misc, &E);
+        else ok = gather_candidates<1>(erow, wact, rcount, spin_limit, FK, FP, misc, &E);
       }
-      if (ok && !sv_done) { publish_sv(); sv_done = true; }
-      if (ok && E <= FIN_ENT) {
-        // ---- keys >= t* are all published (t* is at least every chunk's t_w), so if
-        // k of them are here the threshold is among them and no chunk can hide a key
-        // of the top k.  Thread t takes candidates [t S, t S + S), in position order.
-        constexpr int SE = FIN_ENT / NT;
-        const int S = (E + NT - 1) / NT;
-        const int e0 = tid * S;
-        uint32_t kr[SE];
-#pragma unroll
-        for (int j = 0; j < SE; j++) {
-          const uint32_t key = (j < S && e0 + j < E) ? FK[e0 + j] : 0u;
-          kr[j] = key >= tmax ? key : 0u;
-        }
-        uint32_t T;
-        int rem;
-        if (!any_ov && kth_regs<SE>(kr, S, tmax, k, hist, misc, &T, &rem)) {
-          const int got = emit_segments<SE>(kr, S, T, rem, out, k, misc, [&](int j) { return (int)FP[e0 + j]; });
-          if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
-          done = true;
-        } else if (nr <= BITMAP_KEYS) {
-          // ---- some chunk may hide keys of the top k: T0 = the k-th candidate (if
-          // there are k); a chunk with t_w above it (or that overflowed) is re-read for
-          // its unpublished keys >= T0
-#pragma unroll
-          for (int j = 0; j < SE; j++) kr[j] = (j < S && e0 + j < E) ? FK[e0 + j] : 0u;
-          const bool full = E >= k && kth_regs<SE>(kr, S, 0u, k, hist, misc, &T, &rem);
-          const uint32_t lowT = full ? (rem > 0 ? T : T + 1u) : 0u;
-          int nfail = 0;
-          {
-            // the failing chunks, listed in the bitmap area after the (count, offset)
-            // pairs (which are no longer needed)
-            bool fail[4];
-            int fl = 0;
-#pragma unroll
-            for (int u = 0; u < 4; u++) {
-              const int w = tid + NT * u;
-              const bool ov = ((uint32_t)mv[u] >> 16) & 1u;
-              fail[u] = u < upt && w < wact && (!full || ov || (uint32_t)(mv[u] >> 32) > lowT);
-              fl += fail[u] ? 1 : 0;
-            }
-            __syncthreads();
-            uint32_t dummy;
-            int fo = block_scan_max(fl, 0u, misc, &nfail, &dummy);
-#pragma unroll
-            for (int u = 0; u < 4; u++)
-              if (fail[u]) {
-                const bool ov = ((uint32_t)mv[u] >> 16) & 1u;
-                bm[2 * fo] = (uint32_t)(tid + NT * u);
-                bm[2 * fo + 1] = ov ? 0xFFFFFFFFu : (uint32_t)(mv[u] >> 32);
-                fo++;
-              }
-            __syncthreads();
-          }
-          bool sv_ok = true;
-          if (do_score) {
-            // the failing chunks' scores must have reached memory
-            int spins = 0;
-            while (true) {
-              bool mine_ok = true;
-              for (int f = tid; f < nfail; f += NT) mine_ok &= ld_co32(sv + (int64_t)grow * ms + bm[2 * f]) != 0u;
-              if (__syncthreads_and(mine_ok)) break;
-              if (++spins >= spin_limit) { sv_ok = false; break; }
-              __builtin_amdgcn_s_sleep(1);
-            }
-          }
-          if (!sv_ok) {
-            ok = false;
-          } else {
-            int Ecur = E;
-            bool overflow = false;
-#pragma unroll 1
-            for (int f = 0; f < nfail && !overflow; f++) {
-              const uint32_t w = bm[2 * f];
-              const uint32_t twf = bm[2 * f + 1];
-              const int p0 = (int)w * C;
-#pragma unroll 1
-              for (int base = 0; base < C; base += NT) {
-                const int p = p0 + base + tid;
-                bool take = false;
-                uint32_t key = 0;
-                if (base + tid < C && p < nr) {
-                  key = radix_key(__uint_as_float(
-                      (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, p * 4, 0, CP_COHERENT)));
-                  take = key >= lowT && (twf == 0xFFFFFFFFu || key < twf);
-                }
-                int tot;
-                const int oo = block_excl_scan(take ? 1 : 0, misc, &tot);
-                if (Ecur + tot > FIN_ENT) { overflow = true; break; }
-                if (take) { FK[Ecur + oo] = key; FP[Ecur + oo] = (uint32_t)p; }
-                Ecur += tot;
-              }
-            }
-            __syncthreads();
-            if (!overflow && Ecur >= k) {
-              const int S2 = (Ecur + NT - 1) / NT;
-              const int f0 = tid * S2;
-#pragma unroll
-              for (int j = 0; j < SE; j++) kr[j] = (j < S2 && f0 + j < Ecur) ? FK[f0 + j] : 0u;
-              if (kth_regs<SE>(kr, S2, 0u, k, hist, misc, &T, &rem)) {
-                const int got = select_explicit(FK, FP, Ecur, nr, k, T, rem, bm, misc, out);
-                if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
-                done = true;
-              }
-            }
-          }
-        }
-      }
-      // ---- clear this row's chunk words and candidates: wave v clears chunks v + 8 i
-      if (ok) {
-        __syncthreads();
-#pragma unroll 1
-        for (int w = wv; w < wact; w += NWAVE) {
-          const int cu = (int)(co[w] & 0xFFu);
-          for (int sl = lane; sl < cu; sl += 64) st_co64(erow + (int64_t)w * CAP_MAX + sl, 0ull);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; u++)
-          if (u < upt && tid + NT * u < wact) st_co64(meta + (int64_t)grow * ms + tid + NT * u, 0ull);
-      }
+      cert = ovs == 0 && E <= FIN_ENT;
     }
     if (ok && !sv_done) { publish_sv(); sv_done = true; }
+    if (ok && cert) {
+      // ---- select from the E candidates in LDS: thread t holds [t S, t S + S) (S odd,
+      // so the strided LDS reads are free of bank conflicts)
+      constexpr int SS = 56;
+      int S = (E + NT - 1) / NT;
+      S |= 1;
+      const int e0 = tid * S;
+      uint32_t kr[SS];
+#pragma unroll
+      for (int j = 0; j < SS; j++) kr[j] = 0u;
+#pragma unroll
+      for (int g = 0; g < SS / 8; g++) {
+        if (g * 8 >= S) break;
+#pragma unroll
+        for (int jj = 0; jj < 8; jj++) {
+          const int j = g * 8 + jj, e = e0 + j;
+          const uint32_t key = (j < S && e < E) ? FK[e] : 0u;
+          kr[j] = key >= lo ? key : 0u;
+        }
+      }
+      uint32_t T;
+      int rem;
+      if (kth_regs<SS>(kr, S, k, hist, misc, &T, &rem)) {
+        const int got = emit_segments<SS>(kr, S, T, rem, out, k, misc, [&](int j) {
+          return implicit ? (uint32_t)(e0 + j) : FP[e0 + j];
+        });
+        if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
+        done = true;
+      }
+    }
+    if (ok && !done && thr_mode(nr) && E <= FIN_ENT && nr <= BITMAP_KEYS) {
+      const int st = rare_select(a, grow, nr, k, wact, E, C, rs, sv + (int64_t)grow * ms, do_score, spin_limit,
+                                 FK, FP, bm, hist, misc, out);
+      if (st < 0) ok = false;
+      done = st > 0;
+    }
+    if (thr_mode(nr) && ok)
+      for (int w = tid; w < wact; w += NT) st_co64(meta + (int64_t)grow * ms + w, 0ull);
     if (ok && !done) {
-      // ---- exact multi-pass select over the row's scores in memory (all-mode rows
-      // are always done above, so sv_row(nr) holds when scoring)
+      // ---- exact multi-pass select over the row's scores in memory
       if (do_score) ok = wait_nonzero(sv + (int64_t)grow * ms, wact, spin_limit);
       if (ok) {
         __syncthreads();
