@@ -10,13 +10,13 @@
 //
 // One kernel template covers the three entry points.
 //
-// Scoring.  A workgroup (4 waves, one per SIMD) owns a chunk of P pages of one
+// Scoring.  A workgroup (8 waves, two per SIMD) owns a chunk of P pages of one
 // request.  It DMAs the group's bf16 queries and head weights into LDS, then the
 // chunk's pages (16-byte global->LDS loads, three pages ahead of the compute, each
 // key's 16-byte chunks XOR-swizzled so the operand reads below hit distinct banks).
-// Each wave holds the A operands of up to two rows (64 heads each) in registers and
-// runs bf16 MFMA 32x32x16 over its tiles of 32 keys, the E4M3 codes widened to bf16
-// in registers (exact: every finite E4M3 value is a bf16 value).  FP8 MFMA is not
+// Each wave holds the A operands of one row (64 heads) in registers and runs bf16
+// MFMA 32x32x16 over its tiles of 32 keys, the E4M3 codes widened to bf16 in
+// registers (exact: every finite E4M3 value is a bf16 value).  FP8 MFMA is not
 // used: on gfx950 it accumulates with an error near 1e-4 of the sum of |terms|,
 // which would spend the whole score tolerance.  The tile loop is software
 // pipelined: the MFMAs of one tile are issued, then the epilogue of the previous
@@ -24,15 +24,17 @@
 // tile run on the VALU while the matrix core works.
 //
 // Selection.  Each workgroup publishes, per row, every key of its chunk at or above
-// a local threshold t_w (the m-th largest of its 64 lane maxima), write-through, then
-// a tagged arrival word; its scores are stored afterwards, followed by a second
-// tagged word.  One designated workgroup per row gathers the candidates, finds the
-// exact k-th key T by radix select in LDS and checks t_w <= T for every chunk (then
-// no key left behind can reach the top k); chunks that fail are re-read in full.
-// The selected positions are marked in an LDS bitmap (ties at T resolved by lowest
-// position) and emitted in ascending order.  Rows of up to ALL_MAX keys select from
-// all their scores directly; anything beyond the LDS capacities takes an exact
-// multi-pass radix select over the row's scores in global memory.
+// a local threshold t_w (the m-th largest of its 64 lane maxima), in position
+// order, then a header word; rows of at most ALL_MAX keys publish every key.  Every
+// exchanged word is nonzero once written; one designated workgroup per row polls
+// until it reads nonzero and clears what it read, so the exchange areas are all zero
+// between calls.  The finisher gathers the candidates in position order, finds the
+// exact k-th key T by radix select over the candidates at or above t* = max t_w
+// (every such key is published, so when k of them are present no chunk can hide a
+// key of the top k), and emits the selected positions in ascending order by one
+// block scan, ties at T resolved by lowest position.  When that certificate fails,
+// the chunks that may hide keys are re-read from the scores; anything beyond the
+// LDS capacities takes an exact multi-pass radix select over the row's scores.
 //
 // All waits between workgroups are bounded polls; a timeout sets a sticky error bit.
 #include <hip/hip_runtime.h>
