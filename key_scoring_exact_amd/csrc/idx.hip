@@ -56,7 +56,8 @@ constexpr int PMAX = 8;                 // pages per workgroup at most
 constexpr int CMAX = PMAX * PS;         // keys per chunk at most (512)
 constexpr int LOOKAHEAD = 3;            // pages in flight ahead of the page being scored
 constexpr int ALL_MAX = 24576;          // rows up to this many keys select from all scores at once
-constexpr int FIN_ENT = 12288;          // candidate capacity of a finishing workgroup
+constexpr int FIN_ENT = 12288;          // candidate capacity of a finishing workgroup (the last 64
+                                        // slots take the writes of empty lanes)
 constexpr int BITMAP_KEYS = 131072;     // positions covered by the finisher's LDS bitmap
 constexpr int CAP_MAX = 128;            // candidate slots per chunk and row
 constexpr int LOAD_BATCH = 32;          // candidate loads in flight per thread
@@ -80,7 +81,9 @@ constexpr int L_BM = FIN_ENT * 8;                           // bitmap: BITMAP_KE
 constexpr int HIST_WORDS = 4096 + 64;                       // one histogram: 4096 bins + 64 per-lane dummies
 constexpr int L_HIST = L_BM + BITMAP_KEYS / 8;              // 2 histograms
 constexpr int L_MISC = L_HIST + 2 * HIST_WORDS * 4;         // 64 u32 scratch
-constexpr int L_FIN_END = L_MISC + 64 * 4;
+constexpr int L_CO = L_MISC + 64 * 4;                       // per chunk: candidate count (u8, 4 NT)
+constexpr int L_GRP = L_CO + 4 * NT;                        // per group of 8 chunks: count, then base (2 x 256 u32)
+constexpr int L_FIN_END = L_GRP + 2 * 256 * 4;
 constexpr int LDS_BYTES = (L_FIN_END > L_SCORE_END ? L_FIN_END : L_SCORE_END);
 static_assert(BITMAP_KEYS / 8 >= 4 * NT * 8, "the failing-chunk list (2 words a chunk) fits the bitmap");
 static_assert(ALL_MAX % NT == 0 && FIN_ENT % NT == 0, "register segments");
@@ -105,6 +108,7 @@ struct KArgs {
   int64_t ld;
   int32_t rows, max_pages, max_keys, num_pages, k;
   int32_t chunk;            // keys per workgroup chunk (P * 64)
+  int32_t chunk_shift;      // log2(chunk)
   int32_t mode;
   int32_t spin_limit;
   int32_t skip_chunk;       // test hook: this chunk publishes nothing (-1 = off)
@@ -176,6 +180,8 @@ __device__ inline uint32_t radix_key(float f) {
 }
 
 __device__ inline int lane_id() { return (int)(threadIdx.x & 63); }
+// the wave's index in the workgroup, as a wave-uniform (scalar) value
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 // max(x, 0) of a float as one integer max of its bits: every negative float (and -0)
 // is a negative int32, every positive float a positive one
@@ -254,7 +260,7 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 // Exclusive scan over the workgroup; `tmp` is NWAVE ints of LDS (16-byte aligned).
 // Every thread must call.
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
-  const int l = lane_id(), wv = threadIdx.x >> 6;
+  const int l = lane_id(), wv = wave_id();
   const int x = wave_incl_scan(v);
   if (l == 63) tmp[wv] = x;
   __syncthreads();
@@ -291,7 +297,7 @@ __device__ inline void hist_add(uint32_t* hist, bool m, uint32_t bin) {
 // bins [nbins - 8 t - 8, nbins - 8 t).  Writes misc[8] = d, misc[9] = rem left within
 // d, misc[10] = count of d.  Every thread must call; two barriers.
 __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, int rem, int* misc) {
-  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
   const int base = nbins - 8 * (tid + 1);
   uint32_t h[8];
   if (base >= 0) {
@@ -330,20 +336,23 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, int 
 }
 
 // ---------------------------------------------------------------------------
-// Exact k-th largest of the keys held in registers across the workgroup: thread t
+// Exact top-k threshold of the keys held in registers across the workgroup: thread t
 // holds kr[0 .. S) (slots past S hold 0); a zero key is absent.  Radix select over the
 // bits below the common prefix of the smallest and largest key, in digits of up to 12
 // bits from the top, histograms in LDS (hist: 2 x HIST_WORDS words).  Returns false
 // if fewer than k keys are present.  Otherwise the top k (score descending, then
-// position) are exactly: every key > *T, then the first *rem keys equal to *T in
-// position order (*rem may be 0).  Slots are visited in groups of 8, skipping whole
-// groups past S.  Every thread must call.
+// position) are exactly: every key >= *Tge, and, when *rem > 0, also the first *rem
+// keys equal to *T = *Tge - 1 in position order.  Absent keys never match a prefix
+// once the first digit is fixed, and in the first pass they fall into bin 0, below
+// every present key (a present key is >= 2^23 and the first digit starts at bit 21 or
+// lower), so they are neither counted nor selected.  Slots are visited in groups of
+// 8, skipping whole groups past S.  Every thread must call.
 // ---------------------------------------------------------------------------
 template <int SMAX>
 __device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, int k, uint32_t* hist, int* misc,
-                                         uint32_t* T_out, int* rem_out) {
+                                         uint32_t* Tge_out, int* rem_out) {
   static_assert(SMAX % 8 == 0, "slot groups of 8");
-  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
   uint32_t mn = 0xFFFFFFFFu, mx = 0u, cnt = 0;
 #pragma unroll
   for (int g = 0; g < SMAX / 8; g++) {
@@ -351,12 +360,12 @@ __device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, int 
 #pragma unroll
     for (int jj = 0; jj < 8; jj++) {
       const uint32_t key = kr[g * 8 + jj];
-      mn = min(mn, key == 0u ? 0xFFFFFFFFu : key);
+      mn = min(mn, key - 1u);                         // absent keys wrap to 0xFFFFFFFF
       mx = max(mx, key);
       cnt += key != 0u ? 1u : 0u;
     }
   }
-  mn = wave_min_u32(mn);
+  mn = wave_min_u32(mn);                              // still key - 1 (absent: 0xFFFFFFFF)
   mx = wave_max_u32(mx);
   cnt = wave_sum_u32(cnt);
   uint32_t* red = reinterpret_cast<uint32_t*>(misc) + 16;
@@ -380,9 +389,10 @@ __device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, int 
     cnt += red[2 * NWAVE + i];
   }
   if ((int)cnt < k) return false;
-  if (mn == mx) {  // every key equal: the first k of them
-    *T_out = mn;
-    *rem_out = k;
+  mn += 1u;                                           // the smallest present key
+  if (mn == mx) {  // every key equal: the first k of them (all of them when cnt == k)
+    *Tge_out = (int)cnt == k ? mn : mn + 1u;
+    *rem_out = (int)cnt == k ? 0 : k;
     return true;
   }
   const int top = 31 - __clz(mn ^ mx);               // highest bit that differs
@@ -396,7 +406,6 @@ __device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, int 
   while (true) {
     const int width = wdef < shift ? wdef : shift;
     shift -= width;
-    const uint32_t dmask = (1u << width) - 1u;
     uint32_t* h = hist + buf * HIST_WORDS;
 #pragma unroll
     for (int g = 0; g < SMAX / 8; g++) {
@@ -404,8 +413,8 @@ __device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, int 
 #pragma unroll
       for (int jj = 0; jj < 8; jj++) {
         const uint32_t key = kr[g * 8 + jj];
-        const bool m = key != 0u && (key & mask) == prefix;
-        atomicAdd(&h[m ? (key >> shift) & dmask : dummy], 1u);
+        const uint32_t dg = __builtin_amdgcn_ubfe(key, (uint32_t)shift, (uint32_t)width);
+        atomicAdd(&h[((key & mask) == prefix) ? dg : dummy], 1u);
       }
     }
     {
@@ -420,17 +429,19 @@ __device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, int 
     const uint32_t d = (uint32_t)misc[8];
     const int r = misc[9];
     const int c = misc[10];
+    const uint32_t dmask = (1u << width) - 1u;
     prefix |= d << shift;
     mask |= dmask << shift;
-    if (shift == 0) {
-      *T_out = prefix;
-      *rem_out = r;
+    if (c == r && (shift == 0 || prefix != 0u)) {
+      // every key of this digit is selected: the top k are exactly the keys >= prefix
+      *Tge_out = prefix;
+      *rem_out = 0;
       return true;
     }
-    if (c == r && prefix != 0u) {
-      // every key of this digit is selected: the top k are exactly the keys >= prefix
-      *T_out = prefix - 1u;
-      *rem_out = 0;
+    if (shift == 0) {
+      // r of the c keys equal to prefix, in position order
+      *Tge_out = prefix + 1u;
+      *rem_out = r;
       return true;
     }
     rem = r;
@@ -440,42 +451,61 @@ __device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, int 
 
 // Emission of the top k in segment order (thread t's slots j < S precede thread t + 1's;
 // the caller lays positions out ascending in that order; absent slots hold key 0): a
-// key is selected when key > T, or key == T and it is among the first rem such keys.
-// out[0 .. k) receives the selected positions pos_of(j) (stores of unselected slots go
-// outside the buffer resource and are dropped).  Returns the number selected.  Every
-// thread must call.
-template <int SMAX, typename PosF>
-__device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], int S, uint32_t T, int rem, int32_t* out,
-                                             int k, int* misc, PosF pos_of) {
+// key is selected when key >= Tge, or, when rem > 0, key == Tge - 1 and it is among
+// the first rem such keys.  out[0 .. k) receives the selected positions pr[j] (stores
+// of unselected slots go outside the buffer resource and are dropped).  Returns the
+// number selected.  Every thread must call.
+template <int SMAX>
+__device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], const uint32_t (&pr)[SMAX], int S,
+                                             uint32_t Tge, int rem, int32_t* out, int k, int* misc) {
   constexpr int OOB = 0x7FFFFFF0;
+  const uint32_t T = Tge - 1u;
   int gt = 0, eq = 0;
 #pragma unroll
   for (int g = 0; g < SMAX / 8; g++) {
     if (g * 8 >= S) break;
 #pragma unroll
-    for (int jj = 0; jj < 8; jj++) {
-      const uint32_t key = kr[g * 8 + jj];
-      gt += key > T ? 1 : 0;
-      eq += key == T ? 1 : 0;
+    for (int jj = 0; jj < 8; jj++) gt += kr[g * 8 + jj] >= Tge ? 1 : 0;
+  }
+  if (rem > 0) {
+#pragma unroll
+    for (int g = 0; g < SMAX / 8; g++) {
+      if (g * 8 >= S) break;
+#pragma unroll
+      for (int jj = 0; jj < 8; jj++) eq += kr[g * 8 + jj] == T ? 1 : 0;
     }
   }
   int tot;
   const int packed = block_excl_scan(gt | (eq << 16), misc, &tot);
   const int before_gt = packed & 0xFFFF, before_eq = packed >> 16;
   __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (int64_t)k * 4);
-  int o = before_gt + (before_eq < rem ? before_eq : rem);
-  int er = before_eq;
+  if (rem == 0) {
+    int o4 = before_gt * 4;
 #pragma unroll
-  for (int g = 0; g < SMAX / 8; g++) {
-    if (g * 8 >= S) break;
+    for (int g = 0; g < SMAX / 8; g++) {
+      if (g * 8 >= S) break;
 #pragma unroll
-    for (int jj = 0; jj < 8; jj++) {
-      const uint32_t key = kr[g * 8 + jj];
-      const bool e = key == T;
-      const bool sel = key > T || (e && er < rem);
-      er += e ? 1 : 0;
-      __builtin_amdgcn_raw_buffer_store_b32(pos_of(g * 8 + jj), ro, (sel && o < k) ? o * 4 : OOB, 0, 0);
-      o += sel ? 1 : 0;
+      for (int jj = 0; jj < 8; jj++) {
+        const bool sel = kr[g * 8 + jj] >= Tge;
+        __builtin_amdgcn_raw_buffer_store_b32(pr[g * 8 + jj], ro, sel ? o4 : OOB, 0, 0);
+        o4 += sel ? 4 : 0;
+      }
+    }
+  } else {
+    int o = before_gt + (before_eq < rem ? before_eq : rem);
+    int er = before_eq;
+#pragma unroll
+    for (int g = 0; g < SMAX / 8; g++) {
+      if (g * 8 >= S) break;
+#pragma unroll
+      for (int jj = 0; jj < 8; jj++) {
+        const uint32_t key = kr[g * 8 + jj];
+        const bool e = key == T;
+        const bool sel = key >= Tge || (e && er < rem);
+        er += e ? 1 : 0;
+        __builtin_amdgcn_raw_buffer_store_b32(pr[g * 8 + jj], ro, (sel && o < k) ? o * 4 : OOB, 0, 0);
+        o += sel ? 1 : 0;
+      }
     }
   }
   const int tg = tot & 0xFFFF, te = tot >> 16;
@@ -632,8 +662,9 @@ __device__ void global_select_row(const float* row, int n, int k, int32_t* out, 
 // m (lane-maximum rank used as the local threshold) and the candidate cap, from the
 // row length n, chunk size C and k.  About k*C/n keys of a chunk reach the top k.
 __device__ inline void candidate_params(int n, int C, int k, int* m, int* cap) {
-  int64_t lam = ((int64_t)k * C + n - 1) / n;
-  int mm = (int)(lam + lam / 4 + 12);
+  // k * C <= 2^20 and n >= 1: 32-bit arithmetic is exact
+  const uint32_t lam = ((uint32_t)(k * C) + (uint32_t)n - 1u) / (uint32_t)n;
+  int mm = (int)(lam + lam / 4u + 12u);
   mm = mm > 64 ? 64 : mm;
   int cc = 2 * mm + 16;
   cc = cc > C ? C : cc;
@@ -642,9 +673,22 @@ __device__ inline void candidate_params(int n, int C, int k, int* m, int* cap) {
   *cap = cc;
 }
 
+// Whether any / every thread of the workgroup holds p (misc[48 .. 56) as scratch).
+// Every thread must call; two barriers.
+__device__ __forceinline__ bool block_any(bool p, int* misc) {
+  const int w = __ballot(p) != 0 ? 1 : 0;
+  if (lane_id() == 0) misc[48 + wave_id()] = w;
+  __syncthreads();
+  const v4i a = reinterpret_cast<const v4i*>(misc)[12];
+  const v4i b = reinterpret_cast<const v4i*>(misc)[13];
+  __syncthreads();
+  return (a[0] | a[1] | a[2] | a[3] | b[0] | b[1] | b[2] | b[3]) != 0;
+}
+__device__ __forceinline__ bool block_all(bool p, int* misc) { return !block_any(!p, misc); }
+
 // Bounded poll until words[w] != 0 for every w < count (coherent loads).  Every thread
 // must call.  Returns false on timeout.
-__device__ __forceinline__ bool wait_nonzero(const uint32_t* words, int count, int spin_limit) {
+__device__ __forceinline__ bool wait_nonzero(const uint32_t* words, int count, int spin_limit, int* misc) {
   const int tid = threadIdx.x;
   __amdgpu_buffer_rsrc_t r = make_rsrc(words, (int64_t)count * 4);
   int spins = 0;
@@ -652,7 +696,7 @@ __device__ __forceinline__ bool wait_nonzero(const uint32_t* words, int count, i
     bool mine = true;
     for (int w = tid; w < count; w += NT)
       mine &= __builtin_amdgcn_raw_buffer_load_b32(r, w * 4, 0, CP_COHERENT) != 0;
-    if (__syncthreads_and(mine)) return true;
+    if (block_all(mine, misc)) return true;
     if (++spins >= spin_limit) return false;
     __builtin_amdgcn_s_sleep(1);
   }
@@ -678,7 +722,7 @@ __device__ inline void wait_pages_through(int x, int issued) {
 // ---------------------------------------------------------------------------
 template <int P, int TS>
 __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R, int c, const int* phys) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   float* const sc_lds = LDS_PTR(float, L_SC);
   constexpr int T = (2 * P + TS - 1) / TS;      // tiles of 32 keys per wave
@@ -825,7 +869,7 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
 // Sum over the workgroup (wave-uniform result).  Every thread must call.
 __device__ __forceinline__ uint32_t block_sum(uint32_t v, int* misc) {
   v = wave_sum_u32(v);
-  if (lane_id() == 0) misc[threadIdx.x >> 6] = (int)v;
+  if (lane_id() == 0) misc[wave_id()] = (int)v;
   __syncthreads();
   const v4i a = reinterpret_cast<const v4i*>(misc)[0];
   const v4i b = reinterpret_cast<const v4i*>(misc)[1];
@@ -836,7 +880,7 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, int* misc) {
 // t[0] and t[2] summed, t[1] maxed over the workgroup.  Every thread must call.
 __device__ __forceinline__ void block_sum_max_sum(uint32_t (&t)[3], int* misc) {
   const uint32_t a = wave_sum_u32(t[0]), b = wave_max_u32(t[1]), c = wave_sum_u32(t[2]);
-  const int wv = threadIdx.x >> 6;
+  const int wv = wave_id();
   if (lane_id() == 0) {
     misc[wv] = (int)a;
     misc[NWAVE + wv] = (int)b;
@@ -857,73 +901,119 @@ __device__ __forceinline__ void block_sum_max_sum(uint32_t (&t)[3], int* misc) {
 }
 
 // The row's published candidates into LDS in position order: FK[e] = key, FP[e] =
-// position for e < *E (entries past FIN_ENT are counted, not stored).  Chunk w's
-// candidates sit at erow[w * CAP_MAX + s], s < its count <= 64 SLOTS (slots past the
-// count are zero); rcount[r] is the sum of the counts of the chunks of round r, NWAVE *
-// CPW chunks a round.  In round r wave v reads chunks r NWAVE CPW + v CPW + q (q < CPW),
-// SLOTS loads per lane and chunk, all in flight together.  A zero slot is past its
-// chunk's count or not landed yet, so a round is complete once its nonzero slots add
-// up to rcount[r].  Each candidate read is cleared behind.  Returns false on a
-// timeout.  Every thread must call.
-template <int SLOTS>
-__device__ __forceinline__ bool gather_candidates(uint64_t* erow, int wact, const int* rcount, int spin_limit,
-                                                  uint32_t* FK, uint32_t* FP, int* misc, int* E_out) {
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
-  constexpr int CPW = 32 / SLOTS;
-  constexpr int L = CPW * SLOTS;
+// position for e < E.  Chunk w's candidates sit at erow[w * CAP_MAX + s] for s < its
+// count cnt8[w] <= 64 SLOTS, all nonzero once landed.  Chunks come in groups of 8:
+// group g starts at position-ordered offset gbase[g], so candidate s of chunk w goes to
+// slot gbase[w / 8] + (counts of the chunks before w in its group) + s, known before
+// anything is loaded.  In batch b wave v takes the GPB groups b NWAVE GPB + v GPB + j
+// (j < GPB), issuing one 64-slot load per lane and chunk for all of them before
+// waiting; slots past a count point outside the buffer resource (no traffic, zero
+// result, dropped stores) and write into the last 64 LDS slots, which E <= FIN_ENT - 64
+// leaves free.  A candidate still zero has not landed yet and is loaded again.  Each
+// candidate read is cleared behind; without KEEP the candidates are only awaited and
+// cleared.  No barrier inside; returns false on a timeout.
+template <int SLOTS, bool KEEP>
+__device__ __forceinline__ bool gather_candidates(uint64_t* erow, int wact, const uint8_t* cnt8, const uint32_t* gbase,
+                                                  int spin_limit, uint32_t* FK, uint32_t* FP) {
+  constexpr int OOB = 0x7FFFFFF0;
+  constexpr int GPB = 4 / SLOTS;                        // groups a wave and batch
+  constexpr int L = GPB * 8 * SLOTS;                    // loads a lane and batch (32)
+  const int lane = lane_id(), wv = wave_id();
   __amdgpu_buffer_rsrc_t rent = make_rsrc(erow, (int64_t)wact * CAP_MAX * 8);
-  const int rounds = (wact + NWAVE * CPW - 1) / (NWAVE * CPW);
-  auto soff = [&](int wbase, int i) { return ((wbase + i / SLOTS) * CAP_MAX + (i % SLOTS) * 64) * 8; };
-  int base = 0;
+  const int groups = (wact + 7) / 8;
+  const int dummy = FIN_ENT - 64 + lane;
+  bool ok = true;
 #pragma unroll 1
-  for (int r = 0; r < rounds; r++) {
-    const int wbase = r * NWAVE * CPW + wv * CPW;
-    const int expect = rcount[r];
+  for (int gb = wv * GPB; gb < groups; gb += NWAVE * GPB) {
+    int off[L], at[L];
+#pragma unroll
+    for (int j = 0; j < GPB; j++) {
+      const int g = gb + j;
+      const int w0 = g * 8;
+      // group g's 8 chunk counts (one byte a chunk; bytes past wact are 0) and its base,
+      // as wave-uniform values
+      const bool live = g < groups;
+      const v2i_t cq = live ? *reinterpret_cast<const v2i_t*>(cnt8 + w0) : v2i_t{0, 0};
+      const uint32_t c0 = (uint32_t)__builtin_amdgcn_readfirstlane(cq[0]);
+      const uint32_t c1 = (uint32_t)__builtin_amdgcn_readfirstlane(cq[1]);
+      int base = live ? __builtin_amdgcn_readfirstlane((int)gbase[g]) : 0;
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        const int cu = (int)(((q < 4 ? c0 : c1) >> ((q & 3) * 8)) & 0xFFu);
+#pragma unroll
+        for (int s2 = 0; s2 < SLOTS; s2++) {
+          const int sl = s2 * 64 + lane;
+          const bool v = sl < cu;
+          off[(j * 8 + q) * SLOTS + s2] = v ? ((w0 + q) * CAP_MAX + sl) * 8 : OOB;
+          at[(j * 8 + q) * SLOTS + s2] = v ? base + sl : dummy;
+        }
+        base += cu;
+      }
+    }
     uint64_t e[L];
 #pragma unroll
     for (int i = 0; i < L; i++)
-      e[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rent, lane * 8, soff(wbase, i), CP_COHERENT));
+      e[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rent, off[i], 0, CP_COHERENT));
     int spins = 0;
     while (true) {
-      uint32_t nz = 0;
+      bool miss = false;
 #pragma unroll
-      for (int i = 0; i < L; i++) nz += (uint32_t)__popcll(__ballot(e[i] != 0));
-      if ((int)block_sum(lane == 0 ? nz : 0u, misc) == expect) break;
-      if (++spins >= spin_limit) return false;
+      for (int i = 0; i < L; i++) miss |= (e[i] == 0) & (off[i] != OOB);
+      if (__ballot(miss) == 0) break;
+      if (++spins >= spin_limit) { ok = false; break; }
       __builtin_amdgcn_s_sleep(1);
 #pragma unroll
       for (int i = 0; i < L; i++)
-        if (e[i] == 0)
-          e[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rent, lane * 8, soff(wbase, i), CP_COHERENT));
+        if (e[i] == 0 && off[i] != OOB)
+          e[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rent, off[i], 0, CP_COHERENT));
     }
-    // compaction in position order: wave-local offsets by ballot, then wave bases
-    uint32_t tot = 0;
+    if (!ok) break;
+    if (KEEP) {
 #pragma unroll
-    for (int i = 0; i < L; i++) tot += (uint32_t)__popcll(__ballot(e[i] != 0));
-    if (lane == 0) misc[16 + wv] = (int)tot;
-    __syncthreads();
-    int o = base;
-#pragma unroll
-    for (int i = 0; i < NWAVE; i++) o += (i < wv) ? misc[16 + i] : 0;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < L; i++) {
-      const uint64_t bal = __ballot(e[i] != 0);
-      if (e[i] != 0) {
-        const int slot = o + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-        if (slot < FIN_ENT) {
-          FK[slot] = (uint32_t)(e[i] >> 32);
-          FP[slot] = (uint32_t)e[i];
-        }
-        __builtin_amdgcn_raw_buffer_store_b64(v2i_t{0, 0}, rent, lane * 8, soff(wbase, i), CP_COHERENT);
+      for (int i = 0; i < L; i++) {
+        FK[at[i]] = (uint32_t)(e[i] >> 32);
+        FP[at[i]] = (uint32_t)e[i];
       }
-      o += (int)__popcll(bal);
     }
-    base += expect;
+    // clear what was read
+#pragma unroll
+    for (int i = 0; i < L; i++) __builtin_amdgcn_raw_buffer_store_b64(v2i_t{0, 0}, rent, off[i], 0, CP_COHERENT);
   }
-  __syncthreads();
-  *E_out = base;
+  return ok;
+}
+
+// Top k of the E candidates FK[0 .. E) (with positions FP[e], or e itself when
+// IMPLICIT), laid out in position order; candidates below lo do not count.  Thread t
+// holds candidates [t S, t S + S), S odd so that the strided LDS reads are free of
+// bank conflicts.  Returns false (writing nothing) when fewer than k candidates count.
+// Every thread must call.
+template <int SMAX, bool IMPLICIT>
+__device__ __forceinline__ bool select_emit(const uint32_t* FK, const uint32_t* FP, int E, uint32_t lo, int k,
+                                            uint32_t* hist, int* misc, int32_t* out, int* got) {
+  const int S = ((E + NT - 1) / NT) | 1;
+  const int e0 = threadIdx.x * S;
+  uint32_t kr[SMAX], pr[SMAX];
+#pragma unroll
+  for (int j = 0; j < SMAX; j++) {
+    kr[j] = 0u;
+    pr[j] = 0u;
+  }
+#pragma unroll
+  for (int g = 0; g < SMAX / 8; g++) {
+    if (g * 8 >= S) break;
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++) {
+      const int j = g * 8 + jj, e = e0 + j;
+      const bool v = j < S && e < E;
+      const uint32_t key = v ? FK[e] : 0u;
+      kr[j] = key >= lo ? key : 0u;
+      pr[j] = IMPLICIT ? (uint32_t)e : (v ? FP[e] : 0u);
+    }
+  }
+  uint32_t Tge;
+  int rem;
+  if (!kth_regs<SMAX>(kr, S, k, hist, misc, &Tge, &rem)) return false;
+  *got = emit_segments<SMAX>(kr, pr, S, Tge, rem, out, k, misc);
   return true;
 }
 
@@ -954,7 +1044,8 @@ __device__ __forceinline__ int rare_select(const KArgs& a, int grow, int nr, int
   int rem = 0;
   const int S0 = load_keys(E);
   const bool full = E >= k && kth_regs<SR>(kr, S0, k, hist, misc, &T, &rem);
-  const uint32_t lowT = full ? (rem > 0 ? T : T + 1u) : 0u;
+  // the k-th largest candidate is Tge - 1 when ties are cut, else at least Tge
+  const uint32_t lowT = full ? (rem > 0 ? T - 1u : T) : 0u;
   // failing chunks listed in bm[4 NT ...] (tw[] occupies bm[0 .. 4 NT))
   uint32_t* fl = bm + 4 * NT;
   int nfail = 0;
@@ -973,7 +1064,7 @@ __device__ __forceinline__ int rare_select(const KArgs& a, int grow, int nr, int
     while (true) {
       bool mine_ok = true;
       for (int f = tid; f < nfail; f += NT) mine_ok &= ld_co32(svrow + fl[f]) != 0u;
-      if (__syncthreads_and(mine_ok)) break;
+      if (block_all(mine_ok, misc)) break;
       if (++spins >= spin_limit) return -1;
       __builtin_amdgcn_s_sleep(1);
     }
@@ -1004,7 +1095,8 @@ __device__ __forceinline__ int rare_select(const KArgs& a, int grow, int nr, int
   if (Ecur < k) return 0;
   const int S1 = load_keys(Ecur);
   if (!kth_regs<SR>(kr, S1, k, hist, misc, &T, &rem)) return 0;
-  const int got = select_explicit(FK, FP, Ecur, nr, k, T, rem, bm, misc, out);
+  // select_explicit takes keys > T - 1 (>= Tge) and the first rem keys equal to Tge - 1
+  const int got = select_explicit(FK, FP, Ecur, nr, k, T - 1u, rem, bm, misc, out);
   if (got != k && tid == 0) raise_error(a.ws, IDX_DERR_SELECT);
   return 1;
 }
@@ -1016,7 +1108,7 @@ __device__ inline int pick4(const int (&x)[4], int u) {
 
 // Exclusive scan of v and maximum of m over the workgroup.  Every thread must call.
 __device__ inline int block_scan_max(int v, uint32_t m, int* misc, int* total, uint32_t* mall) {
-  const int lane = lane_id(), wv = threadIdx.x >> 6;
+  const int lane = lane_id(), wv = wave_id();
   const int x = wave_incl_scan(v);
   m = wave_max_u32(m);
   if (lane == 63) misc[wv] = x;
@@ -1045,7 +1137,7 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = wave_id();
   const int c = blockIdx.x;
   const int g = blockIdx.y;
   const uint32_t ge = a.grp[g];
@@ -1121,7 +1213,7 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
     return;
   }
   if (chunk_base >= nmax) return;                 // nothing of this group here
-  const int wact = (nmax + C - 1) / C;            // chunks holding keys of this group
+  const int wact = (nmax + C - 1) >> a.chunk_shift;   // chunks holding keys of this group (C = 2^shift)
   const int k = a.k;
   // how row i selects: nothing to select (n <= k), from all its keys at once (n <=
   // ALL_MAX), from per-chunk candidates (up to 4 chunks per finishing thread), or by
@@ -1133,7 +1225,7 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
   // finisher of row i: chunk wact - 1 - (i % wact)
   bool is_fin = false;
 #pragma unroll
-  for (int i = 0; i < GR; i++) is_fin |= (i < R) && (c == wact - 1 - (i % wact));
+  for (int i = 0; i < GR; i++) is_fin |= (i < R) && (c == wact - 1 - (i < wact ? i : i % wact));
   if (given && !is_fin) {
     // over given scores, only rows selecting from candidates need this chunk
     bool needed = false;
@@ -1270,7 +1362,7 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
   uint32_t* bm = LDS_PTR(uint32_t, L_BM);
 #pragma unroll 1
   for (int i = 0; i < R; i++) {
-    const int fin = wact - 1 - (i % wact);
+    const int fin = wact - 1 - (i < wact ? i : i % wact);
     if (c != fin) continue;
     const int grow = row0 + i;
     const int nr = n[i];
@@ -1339,13 +1431,12 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
       const int upt = (wact + NT - 1) / NT;
       __amdgpu_buffer_rsrc_t rmeta = make_rsrc(mrow, (int64_t)wact * 8);
       uint64_t mv[4] = {0, 0, 0, 0};
-      // candidates per gather round (256 chunks a round, or 128 when a chunk may post
-      // more than 64)
       int m_unused, cap;
       candidate_params(nr, C, k, &m_unused, &cap);
-      const int rshift = cap > 64 ? 7 : 8;
-      int* rcount = misc + 40;
-      if (tid < 16) rcount[tid] = 0;
+      uint8_t* cnt8 = LDS_PTR(uint8_t, L_CO);
+      uint32_t* gcnt = LDS_PTR(uint32_t, L_GRP);
+      uint32_t* gbase = gcnt + 256;
+      if (tid < 256) gcnt[tid] = 0;
       {
         int spins = 0;
         while (true) {
@@ -1357,72 +1448,69 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
                                          __builtin_amdgcn_raw_buffer_load_b64(rmeta, (tid + NT * u) * 8, 0, CP_COHERENT));
               miss |= mv[u] == 0;
             }
-          if (!__syncthreads_or(miss)) break;
+          if (!block_any(miss, misc)) break;
           if (++spins >= spin_limit) { ok = false; break; }
           __builtin_amdgcn_s_sleep(1);
         }
       }
-      // E = candidates published, t* = the largest t_w, whether any chunk overflowed;
-      // bm[w] = t_w (0xFFFFFFFF: overflowed, published nothing) for the rare path
+      // per chunk: its count (cnt8), per group of 8 chunks: the count (gcnt); bm[w] =
+      // t_w (0xFFFFFFFF: overflowed, published nothing) for the rare path; E = the
+      // candidates published, t* = the largest t_w, whether any chunk overflowed
       uint32_t pub = 0, tmax = 0, ovs = 0;
 #pragma unroll
       for (int u = 0; u < 4; u++) {
-        if (u >= upt || tid + NT * u >= wact) break;
+        const int w = tid + NT * u;
+        if (u >= upt) break;
         const uint32_t lw = (uint32_t)mv[u];
-        const bool ov = (lw >> 16) & 1u;
+        const bool live = w < wact;
+        const bool ov = live && ((lw >> 16) & 1u);
+        const uint32_t cu = (live && !ov) ? (lw & 0xFFFFu) : 0u;
         const uint32_t twu = (uint32_t)(mv[u] >> 32);
-        pub += ov ? 0u : (lw & 0xFFFFu);
-        if (!ov) atomicAdd(&rcount[(tid + NT * u) >> rshift], (int)(lw & 0xFFFFu));
+        cnt8[w] = (uint8_t)cu;                       // w < 4 NT: bytes past wact read as 0
+        if (cu) atomicAdd(&gcnt[w >> 3], cu);
+        pub += cu;
         ovs += ov ? 1u : 0u;
-        if (!ov) tmax = max(tmax, twu);
-        bm[tid + NT * u] = ov ? 0xFFFFFFFFu : twu;
+        if (live && !ov) tmax = max(tmax, twu);
+        if (live) bm[w] = ov ? 0xFFFFFFFFu : twu;
       }
       uint32_t t3[3] = {pub, tmax, ovs};
       block_sum_max_sum(t3, misc);
       pub = t3[0];
       tmax = t3[1];
       ovs = t3[2];
+      // group bases: an exclusive scan of the 256 group counts (wave 0, 4 a lane)
+      if (wv == 0) {
+        const v4i c4 = reinterpret_cast<const v4i*>(gcnt)[lane];
+        const int t = c4[0] + c4[1] + c4[2] + c4[3];
+        const int b = wave_incl_scan(t) - t;
+        reinterpret_cast<v4i*>(gbase)[lane] = v4i{b, b + c4[0], b + c4[0] + c4[1], b + c4[0] + c4[1] + c4[2]};
+      }
+      __syncthreads();
+      E = (int)pub;
       // keys >= t* are all published (t* is at least every chunk's t_w): if k of them
       // are here, the k-th is among them and no chunk hides a key of the top k
       lo = tmax;
-      if (ok) {
-        if (cap > 64) ok = gather_candidates<2>(erow, wact, rcount, spin_limit, FK, FP, misc, &E);
-        else ok = gather_candidates<1>(erow, wact, rcount, spin_limit, FK, FP, misc, &E);
+      if (ok && E <= FIN_ENT - 64) {
+        if (cap > 64) ok = gather_candidates<2, true>(erow, wact, cnt8, gbase, spin_limit, FK, FP);
+        else ok = gather_candidates<1, true>(erow, wact, cnt8, gbase, spin_limit, FK, FP);
+        ok = !block_any(!ok, misc);
+      } else if (ok) {
+        // too many candidates for the LDS: await and clear them without keeping any
+        if (cap > 64) ok = gather_candidates<2, false>(erow, wact, cnt8, gbase, spin_limit, FK, FP);
+        else ok = gather_candidates<1, false>(erow, wact, cnt8, gbase, spin_limit, FK, FP);
+        ok = !block_any(!ok, misc);
       }
-      cert = ovs == 0 && E <= FIN_ENT;
+      cert = ovs == 0 && E <= FIN_ENT - 64;
     }
     if (ok && !sv_done) { publish_sv(); sv_done = true; }
     if (ok && cert) {
-      // ---- select from the E candidates in LDS: thread t holds [t S, t S + S) (S odd,
-      // so the strided LDS reads are free of bank conflicts)
-      constexpr int SS = 56;
-      int S = (E + NT - 1) / NT;
-      S |= 1;
-      const int e0 = tid * S;
-      uint32_t kr[SS];
-#pragma unroll
-      for (int j = 0; j < SS; j++) kr[j] = 0u;
-#pragma unroll
-      for (int g = 0; g < SS / 8; g++) {
-        if (g * 8 >= S) break;
-#pragma unroll
-        for (int jj = 0; jj < 8; jj++) {
-          const int j = g * 8 + jj, e = e0 + j;
-          const uint32_t key = (j < S && e < E) ? FK[e] : 0u;
-          kr[j] = key >= lo ? key : 0u;
-        }
-      }
-      uint32_t T;
-      int rem;
-      if (kth_regs<SS>(kr, S, k, hist, misc, &T, &rem)) {
-        const int got = emit_segments<SS>(kr, S, T, rem, out, k, misc, [&](int j) {
-          return implicit ? (uint32_t)(e0 + j) : FP[e0 + j];
-        });
-        if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
-        done = true;
-      }
+      // ---- select from the E candidates in LDS (position order)
+      int got = -1;
+      if (implicit) done = select_emit<56, true>(FK, FP, E, lo, k, hist, misc, out, &got);
+      else done = select_emit<32, false>(FK, FP, E, lo, k, hist, misc, out, &got);
+      if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
     }
-    if (ok && !done && thr_mode(nr) && E <= FIN_ENT && nr <= BITMAP_KEYS) {
+    if (ok && !done && thr_mode(nr) && E <= FIN_ENT - 64 && nr <= BITMAP_KEYS) {
       const int st = rare_select(a, grow, nr, k, wact, E, C, rs, sv + (int64_t)grow * ms, do_score, spin_limit,
                                  FK, FP, bm, hist, misc, out);
       if (st < 0) ok = false;
@@ -1432,7 +1520,7 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
       for (int w = tid; w < wact; w += NT) st_co64(meta + (int64_t)grow * ms + w, 0ull);
     if (ok && !done) {
       // ---- exact multi-pass select over the row's scores in memory
-      if (do_score) ok = wait_nonzero(sv + (int64_t)grow * ms, wact, spin_limit);
+      if (do_score) ok = wait_nonzero(sv + (int64_t)grow * ms, wact, spin_limit, misc);
       if (ok) {
         __syncthreads();
         global_select_row(srow, nr, k, out, hist, misc);
@@ -1440,7 +1528,7 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
     }
     if (ok && sv_row(nr)) {
       // every chunk's "scores visible" word has been written: clear them
-      ok = wait_nonzero(sv + (int64_t)grow * ms, wact, spin_limit);
+      ok = wait_nonzero(sv + (int64_t)grow * ms, wact, spin_limit, misc);
       if (ok)
         for (int w = tid; w < wact; w += NT) st_co32(sv + (int64_t)grow * ms + w, 0u);
     }
@@ -1620,6 +1708,7 @@ int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int3
   args.num_pages = p->num_pages;
   args.k = k;
   args.chunk = pl.chunk;
+  args.chunk_shift = 31 - __builtin_clz((unsigned)pl.chunk);
   args.mode = mode;
   fill_common(args, L, ws, ws_bytes);
   for (int j = 0; j < p->num_req; j++) {
@@ -1689,6 +1778,7 @@ int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys, int3
     args.max_keys = max_keys;
     args.k = k;
     args.chunk = pl.chunk;
+    args.chunk_shift = 31 - __builtin_clz((unsigned)pl.chunk);
     args.mode = MODE_SELECT;
     fill_common(args, L, ws, ws_bytes);
     for (int gi = 0; gi < groups; gi++) {
