@@ -32,7 +32,7 @@
  *    error bit in the workspace, read back with idx_device_status().
  *  - A workspace is used by one stream at a time; calls on distinct
  *    workspaces are independent.  It must be initialised once with
- *    idx_workspace_init() (and again after a device error).
+ *    idx_workspace_init(); a call leaves it usable by the next one.
  */
 #ifndef IDX_H
 #define IDX_H
@@ -53,7 +53,7 @@ extern "C" {
 #define IDX_KMAX 2048
 #define IDX_GROUP_ROWS 4
 #define IDX_MAX_REQ 256
-#define IDX_ABI_VERSION 1
+#define IDX_ABI_VERSION 2
 
 /* Return codes. */
 #define IDX_OK 0
@@ -67,7 +67,6 @@ extern "C" {
 #define IDX_DERR_NKEYS 0x1u       /* an n_keys entry was outside [0, max_keys] */
 #define IDX_DERR_PAGE 0x2u        /* a page id was outside [0, num_pages) */
 #define IDX_DERR_WS 0x4u          /* the workspace was not initialised */
-#define IDX_DERR_TIMEOUT 0x8u     /* a bounded wait between workgroups ran out */
 #define IDX_DERR_SELECT 0x10u     /* internal selection invariant failed (list count != k) */
 
 typedef struct idx_problem {
@@ -122,8 +121,10 @@ int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys,
              int32_t rows, int32_t max_keys, int32_t k, int32_t* topk,
              void* ws, size_t ws_bytes, void* stream);
 
-/* Fused scoring and exact top-k in one launch: writes the scores exactly as
- * idx_score() does and the lists exactly as idx_topk() over those scores. */
+/* Scoring and exact top-k in one call (two launches on `stream`: scoring with
+ * candidate publication, then one selection workgroup per row): writes the
+ * scores exactly as idx_score() does and the lists exactly as idx_topk() over
+ * those scores. */
 int idx_score_topk(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores,
                    int32_t* topk, void* ws, size_t ws_bytes, void* stream);
 
@@ -137,12 +138,6 @@ const char* idx_strerror(int code);
 
 /* The last HIP error string seen by this thread (empty if none). */
 const char* idx_last_hip_error(void);
-
-/* Test hook for the failure paths, not for production use: key 1 sets the
- * bound (in polls) of every wait between workgroups (0 = the default);
- * key 2 makes the workgroup with this chunk index skip publishing its
- * candidates (-1 = off).  Returns IDX_OK or IDX_EINVAL. */
-int idx_debug_set(int32_t key, int32_t value);
 
 #ifdef __cplusplus
 }

@@ -184,7 +184,3 @@ def device_status(ws: Workspace, stream=None):
                                    ctypes.byref(detail))
     return int(code), int(detail.value)
 
-
-def debug_set(key: int, value: int):
-    """Test hook of the failure paths (see idx_debug_set in include/idx.h)."""
-    _check(lib().idx_debug_set(int(key), int(value)), "idx_debug_set")

@@ -24,7 +24,6 @@ IDX_EDEVICE = 5
 IDX_DERR_NKEYS = 0x1
 IDX_DERR_PAGE = 0x2
 IDX_DERR_WS = 0x4
-IDX_DERR_TIMEOUT = 0x8
 IDX_DERR_SELECT = 0x10
 
 # every function the header declares, with its ctypes signature
@@ -62,7 +61,6 @@ SIGNATURES = {
     "idx_device_status": (ctypes.c_int, [_vp, _sz, _vp, ctypes.POINTER(ctypes.c_uint32)]),
     "idx_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "idx_last_hip_error": (ctypes.c_char_p, []),
-    "idx_debug_set": (ctypes.c_int, [_i32, _i32]),
 }
 
 _lib = None

@@ -8,10 +8,10 @@
 //
 //   score[r][p] = sum_h w[r][h] * ReLU( s[p] * <q[r][h][:], k8[p][:]> )
 //
-// One kernel template covers the three entry points.
+// Two launches on the caller's stream cover the three entry points.
 //
-// Scoring.  A workgroup (8 waves, two per SIMD) owns a chunk of P pages of one
-// request.  It DMAs the group's bf16 queries and head weights into LDS, then the
+// Launch 1, scoring.  A workgroup (8 waves, two per SIMD) owns a chunk of P pages of
+// one request.  It DMAs the group's bf16 queries and head weights into LDS, then the
 // chunk's pages (16-byte global->LDS loads, three pages ahead of the compute, each
 // key's 16-byte chunks XOR-swizzled so the operand reads below hit distinct banks).
 // Each wave holds the A operands of one row (64 heads) in registers and runs bf16
@@ -21,22 +21,21 @@
 // which would spend the whole score tolerance.  The tile loop is software
 // pipelined: the MFMAs of one tile are issued, then the epilogue of the previous
 // tile (ReLU, head weights, f32 head sum, key scale) and the widening of the next
-// tile run on the VALU while the matrix core works.
+// tile run on the VALU while the matrix core works.  For each row longer than
+// ALL_MAX keys, the workgroup also publishes every key of its chunk at or above a
+// local threshold t_w (the m-th largest of its 64 lane maxima), in position order,
+// with a header word (t_w, count, overflow flag).
 //
-// Selection.  Each workgroup publishes, per row, every key of its chunk at or above
-// a local threshold t_w (the m-th largest of its 64 lane maxima), in position
-// order, then a header word; rows of at most ALL_MAX keys publish every key.  Every
-// exchanged word is nonzero once written; one designated workgroup per row polls
-// until it reads nonzero and clears what it read, so the exchange areas are all zero
-// between calls.  The finisher gathers the candidates in position order, finds the
-// exact k-th key T by radix select over the candidates at or above t* = max t_w
-// (every such key is published, so when k of them are present no chunk can hide a
-// key of the top k), and emits the selected positions in ascending order by one
-// block scan, ties at T resolved by lowest position.  When that certificate fails,
-// the chunks that may hide keys are re-read from the scores; anything beyond the
-// LDS capacities takes an exact multi-pass radix select over the row's scores.
-//
-// All waits between workgroups are bounded polls; a timeout sets a sticky error bit.
+// Launch 2, selection: one workgroup per row.  A row of at most ALL_MAX keys loads
+// all its scores into LDS.  A longer row gathers its chunks' candidates in position
+// order and finds the exact k-th key T by radix select over the candidates at or
+// above t* = max t_w: every such key is published, so when k of them are present no
+// chunk can hide a key of the top k.  The selected positions are emitted in ascending
+// order by one block scan, ties at T resolved by lowest position.  When that
+// certificate fails, the chunks that may hide keys are re-read from the scores;
+// anything beyond the LDS capacities takes an exact multi-pass radix select over the
+// row's scores.  The kernel boundary orders the two launches: no workgroup waits on
+// another.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -62,10 +61,9 @@ constexpr int BITMAP_KEYS = 131072;     // positions covered by the finisher's L
 constexpr int CAP_MAX = 128;            // candidate slots per chunk and row
 constexpr int LOAD_BATCH = 32;          // candidate loads in flight per thread
 constexpr uint32_t WS_MAGIC = 0x1D5C0DE5u;
-constexpr int DEFAULT_SPIN = 1 << 20;   // polls before a wait gives up (about a second)
 
 constexpr int MODE_SCORE = 1;           // compute scores (else read them from args.scores)
-constexpr int MODE_SELECT = 2;          // select the top k
+constexpr int MODE_PUBLISH = 2;         // publish each chunk's candidates for the selection launch
 
 // LDS layout, scoring phase (bytes)
 constexpr int L_KEYS = 0;                                   // [PMAX][64 keys][128 B], swizzled
@@ -84,11 +82,10 @@ constexpr int L_MISC = L_HIST + 2 * HIST_WORDS * 4;         // 64 u32 scratch
 constexpr int L_CO = L_MISC + 64 * 4;                       // per chunk: candidate count (u8, 4 NT)
 constexpr int L_GRP = L_CO + 4 * NT;                        // per group of 8 chunks: count, then base (2 x 256 u32)
 constexpr int L_FIN_END = L_GRP + 2 * 256 * 4;
-constexpr int LDS_BYTES = (L_FIN_END > L_SCORE_END ? L_FIN_END : L_SCORE_END);
 static_assert(BITMAP_KEYS / 8 >= 4 * NT * 8, "the failing-chunk list (2 words a chunk) fits the bitmap");
 static_assert(ALL_MAX % NT == 0 && FIN_ENT % NT == 0, "register segments");
 static_assert(CAP_MAX <= 128, "a chunk's candidates are gathered in at most two 64-slot groups");
-static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(L_SCORE_END <= 160 * 1024 && L_FIN_END <= 160 * 1024, "LDS budget");
 
 // workspace header (bytes)
 constexpr int WS_MAGIC_OFF = 0;
@@ -110,12 +107,9 @@ struct KArgs {
   int32_t chunk;            // keys per workgroup chunk (P * 64)
   int32_t chunk_shift;      // log2(chunk)
   int32_t mode;
-  int32_t spin_limit;
-  int32_t skip_chunk;       // test hook: this chunk publishes nothing (-1 = off)
-  int32_t meta_stride;      // chunk slots per row (>= gridDim.x)
-  int32_t ent_stride;       // chunk slots per row and candidate slot (min(meta_stride, 4 NT))
-  int32_t all_stride;       // keys per row of the all-keys area
-  uint64_t off_meta, off_ent, off_sv, off_allk;
+  int32_t meta_stride;      // chunk slots per row (>= chunks of the longest row)
+  int32_t ent_stride;       // chunk slots per row of the candidate area (min(meta_stride, 4 NT))
+  uint64_t off_meta, off_ent;
   uint32_t grp[IDX_MAX_REQ];// row0 | nrows << 24
   int32_t gmax[IDX_MAX_REQ];// host bound on the keys of each group's rows
 };
@@ -132,11 +126,6 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 // memory helpers
 // ---------------------------------------------------------------------------
-// Cache policy bits of buffer instructions on gfx950: sc0 = 1, nt = 2, sc1 = 16.
-// sc0|sc1 reads miss the non-coherent caches and writes go through to memory, so
-// data handed between workgroups on different XCDs needs no cache-wide fence.
-constexpr int CP_COHERENT = 1 | 16;
-
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   int64_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : (bytes < 0 ? 0 : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
@@ -154,16 +143,6 @@ __device__ inline void wait_vmcnt() {
 __device__ inline void dma16(const void* gptr, uint32_t lds_wave_base) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base))
                : "memory");
-}
-
-__device__ inline uint32_t ld_co32(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void st_co32(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void st_co64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ inline void raise_error(uint8_t* ws, uint32_t bits) {
@@ -604,7 +583,7 @@ __device__ void global_select_row(const float* row, int n, int k, int32_t* out, 
       uint32_t v[8];
 #pragma unroll
       for (int j = 0; j < 8; j++)
-        v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (base + j * NT + tid) * 4, 0, CP_COHERENT);
+        v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (base + j * NT + tid) * 4, 0, 0);
 #pragma unroll
       for (int j = 0; j < 8; j++) {
         const int p = base + j * NT + tid;
@@ -627,7 +606,7 @@ __device__ void global_select_row(const float* row, int n, int k, int32_t* out, 
 #pragma unroll
     for (int j = 0; j < 8; j++)
       key[j] = radix_key(__uint_as_float(
-          (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (p0 + j) * 4, 0, CP_COHERENT)));
+          (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (p0 + j) * 4, 0, 0)));
     int ceq = 0;
 #pragma unroll
     for (int j = 0; j < 8; j++) ceq += (p0 + j < n && key[j] == T) ? 1 : 0;
@@ -683,23 +662,6 @@ __device__ __forceinline__ bool block_any(bool p, int* misc) {
   const v4i b = reinterpret_cast<const v4i*>(misc)[13];
   __syncthreads();
   return (a[0] | a[1] | a[2] | a[3] | b[0] | b[1] | b[2] | b[3]) != 0;
-}
-__device__ __forceinline__ bool block_all(bool p, int* misc) { return !block_any(!p, misc); }
-
-// Bounded poll until words[w] != 0 for every w < count (coherent loads).  Every thread
-// must call.  Returns false on timeout.
-__device__ __forceinline__ bool wait_nonzero(const uint32_t* words, int count, int spin_limit, int* misc) {
-  const int tid = threadIdx.x;
-  __amdgpu_buffer_rsrc_t r = make_rsrc(words, (int64_t)count * 4);
-  int spins = 0;
-  while (true) {
-    bool mine = true;
-    for (int w = tid; w < count; w += NT)
-      mine &= __builtin_amdgcn_raw_buffer_load_b32(r, w * 4, 0, CP_COHERENT) != 0;
-    if (block_all(mine, misc)) return true;
-    if (++spins >= spin_limit) return false;
-    __builtin_amdgcn_s_sleep(1);
-  }
 }
 
 // wait until this wave's DMAs of pages [0, x] are done, pages [0, issued) having
@@ -902,19 +864,16 @@ __device__ __forceinline__ void block_sum_max_sum(uint32_t (&t)[3], int* misc) {
 
 // The row's published candidates into LDS in position order: FK[e] = key, FP[e] =
 // position for e < E.  Chunk w's candidates sit at erow[w * CAP_MAX + s] for s < its
-// count cnt8[w] <= 64 SLOTS, all nonzero once landed.  Chunks come in groups of 8:
-// group g starts at position-ordered offset gbase[g], so candidate s of chunk w goes to
-// slot gbase[w / 8] + (counts of the chunks before w in its group) + s, known before
-// anything is loaded.  In batch b wave v takes the GPB groups b NWAVE GPB + v GPB + j
-// (j < GPB), issuing one 64-slot load per lane and chunk for all of them before
-// waiting; slots past a count point outside the buffer resource (no traffic, zero
-// result, dropped stores) and write into the last 64 LDS slots, which E <= FIN_ENT - 64
-// leaves free.  A candidate still zero has not landed yet and is loaded again.  Each
-// candidate read is cleared behind; without KEEP the candidates are only awaited and
-// cleared.  No barrier inside; returns false on a timeout.
-template <int SLOTS, bool KEEP>
-__device__ __forceinline__ bool gather_candidates(uint64_t* erow, int wact, const uint8_t* cnt8, const uint32_t* gbase,
-                                                  int spin_limit, uint32_t* FK, uint32_t* FP) {
+// count cnt8[w] <= 64 SLOTS.  Chunks come in groups of 8: group g starts at position-
+// ordered offset gbase[g], so candidate s of chunk w goes to slot gbase[w / 8] + (counts
+// of the chunks before w in its group) + s, known before anything is loaded.  In batch
+// b wave v takes the GPB groups b NWAVE GPB + v GPB + j (j < GPB), issuing one 64-slot
+// load per lane and chunk for all of them before the first use; slots past a count
+// point outside the buffer resource (no traffic, zero result) and write into the last
+// 64 LDS slots, which E <= FIN_ENT - 64 leaves free.  No barrier inside.
+template <int SLOTS>
+__device__ __forceinline__ void gather_candidates(const uint64_t* erow, int wact, const uint8_t* cnt8,
+                                                  const uint32_t* gbase, uint32_t* FK, uint32_t* FP) {
   constexpr int OOB = 0x7FFFFFF0;
   constexpr int GPB = 4 / SLOTS;                        // groups a wave and batch
   constexpr int L = GPB * 8 * SLOTS;                    // loads a lane and batch (32)
@@ -922,7 +881,6 @@ __device__ __forceinline__ bool gather_candidates(uint64_t* erow, int wact, cons
   __amdgpu_buffer_rsrc_t rent = make_rsrc(erow, (int64_t)wact * CAP_MAX * 8);
   const int groups = (wact + 7) / 8;
   const int dummy = FIN_ENT - 64 + lane;
-  bool ok = true;
 #pragma unroll 1
   for (int gb = wv * GPB; gb < groups; gb += NWAVE * GPB) {
     int off[L], at[L];
@@ -953,33 +911,13 @@ __device__ __forceinline__ bool gather_candidates(uint64_t* erow, int wact, cons
     uint64_t e[L];
 #pragma unroll
     for (int i = 0; i < L; i++)
-      e[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rent, off[i], 0, CP_COHERENT));
-    int spins = 0;
-    while (true) {
-      bool miss = false;
+      e[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rent, off[i], 0, 0));
 #pragma unroll
-      for (int i = 0; i < L; i++) miss |= (e[i] == 0) & (off[i] != OOB);
-      if (__ballot(miss) == 0) break;
-      if (++spins >= spin_limit) { ok = false; break; }
-      __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-      for (int i = 0; i < L; i++)
-        if (e[i] == 0 && off[i] != OOB)
-          e[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rent, off[i], 0, CP_COHERENT));
+    for (int i = 0; i < L; i++) {
+      FK[at[i]] = (uint32_t)(e[i] >> 32);
+      FP[at[i]] = (uint32_t)e[i];
     }
-    if (!ok) break;
-    if (KEEP) {
-#pragma unroll
-      for (int i = 0; i < L; i++) {
-        FK[at[i]] = (uint32_t)(e[i] >> 32);
-        FP[at[i]] = (uint32_t)e[i];
-      }
-    }
-    // clear what was read
-#pragma unroll
-    for (int i = 0; i < L; i++) __builtin_amdgcn_raw_buffer_store_b64(v2i_t{0, 0}, rent, off[i], 0, CP_COHERENT);
   }
-  return ok;
 }
 
 // Top k of the E candidates FK[0 .. E) (with positions FP[e], or e itself when
@@ -1021,14 +959,11 @@ __device__ __forceinline__ bool select_emit(const uint32_t* FK, const uint32_t* 
 // k); every chunk whose local threshold t_w (tw[w], 0xFFFFFFFF when it published
 // nothing) is above T0 is re-read from the row's scores for its unpublished keys >= T0,
 // after which every key >= T0 of the row is a candidate, and the top k is taken from
-// that set through a position bitmap.  Returns 1 when it selected, 0 to fall back to the
-// multi-pass select over memory, -1 on a timeout.  Every thread must call.
-__device__ __forceinline__ int rare_select(const KArgs& a, int grow, int nr, int k, int wact, int E, int C,
-                                        __amdgpu_buffer_rsrc_t rs, const uint32_t* svrow, bool do_score,
-                                        int spin_limit, uint32_t* FK, uint32_t* FP, uint32_t* bm, uint32_t* hist,
-                                        int* misc, int32_t* out) {
-  (void)a;
-  (void)grow;
+// that set through a position bitmap.  Returns true when it selected, false to fall
+// back to the multi-pass select over memory.  Every thread must call.
+__device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact, int E, int C,
+                                            __amdgpu_buffer_rsrc_t rs, uint32_t* FK, uint32_t* FP, uint32_t* bm,
+                                            uint32_t* hist, int* misc, int32_t* out) {
   const int tid = threadIdx.x;
   constexpr int SR = 32;
   uint32_t kr[SR];
@@ -1058,17 +993,6 @@ __device__ __forceinline__ int rare_select(const KArgs& a, int grow, int nr, int
     nfail += tot;
   }
   __syncthreads();
-  if (do_score) {
-    // the failing chunks' scores must have reached memory
-    int spins = 0;
-    while (true) {
-      bool mine_ok = true;
-      for (int f = tid; f < nfail; f += NT) mine_ok &= ld_co32(svrow + fl[f]) != 0u;
-      if (block_all(mine_ok, misc)) break;
-      if (++spins >= spin_limit) return -1;
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
   int Ecur = E;
 #pragma unroll 1
   for (int f = 0; f < nfail; f++) {
@@ -1081,24 +1005,24 @@ __device__ __forceinline__ int rare_select(const KArgs& a, int grow, int nr, int
       bool take = false;
       uint32_t key = 0;
       if (base + tid < C && p < nr) {
-        key = radix_key(__uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, p * 4, 0, CP_COHERENT)));
+        key = radix_key(__uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, p * 4, 0, 0)));
         take = key >= lowT && key < twf;
       }
       int tot;
       const int oo = block_excl_scan(take ? 1 : 0, misc, &tot);
-      if (Ecur + tot > FIN_ENT) return 0;
+      if (Ecur + tot > FIN_ENT) return false;
       if (take) { FK[Ecur + oo] = key; FP[Ecur + oo] = (uint32_t)p; }
       Ecur += tot;
     }
   }
   __syncthreads();
-  if (Ecur < k) return 0;
+  if (Ecur < k) return false;
   const int S1 = load_keys(Ecur);
-  if (!kth_regs<SR>(kr, S1, k, hist, misc, &T, &rem)) return 0;
+  if (!kth_regs<SR>(kr, S1, k, hist, misc, &T, &rem)) return false;
   // select_explicit takes keys > T - 1 (>= Tge) and the first rem keys equal to Tge - 1
   const int got = select_explicit(FK, FP, Ecur, nr, k, T - 1u, rem, bm, misc, out);
-  if (got != k && tid == 0) raise_error(a.ws, IDX_DERR_SELECT);
-  return 1;
+  if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
+  return true;
 }
 
 // x[u] for a runtime u < 4 without indexing registers
@@ -1132,8 +1056,22 @@ __device__ inline int block_scan_max(int v, uint32_t m, int* misc, int* total, u
   return x - v + before;
 }
 
+// How a row of n keys selects (the same decision in both launches): nothing to select
+// (n <= k), from all its scores at once (n <= ALL_MAX), from the candidates its chunks of
+// 2^shift keys publish (at most 4 NT chunks), or by a multi-pass select over its scores.
+constexpr int PATH_NONE = 0, PATH_ALL = 1, PATH_CAND = 2, PATH_MULTI = 3;
+__host__ __device__ inline int row_path(int n, int k, int shift) {
+  if (n <= k) return PATH_NONE;
+  if (n <= ALL_MAX) return PATH_ALL;
+  return ((n - 1) >> shift) < 4 * NT ? PATH_CAND : PATH_MULTI;
+}
+
+// ---------------------------------------------------------------------------
+// Launch 1: workgroup (c, g) scores chunk c (keys [c C, c C + C)) of request g's rows
+// and, per row that selects from candidates, publishes the chunk's candidates.
+// ---------------------------------------------------------------------------
 template <int P>
-__global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
+__global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1150,18 +1088,10 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
   const int gbound = a.gmax[g];
   if (c > 0 && chunk_base >= gbound) return;      // beyond every row of this group
   const bool do_score = (a.mode & MODE_SCORE) != 0;
-  const bool do_select = (a.mode & MODE_SELECT) != 0;
-  const bool given = !do_score;
-  {
-    // magic word and sticky error word in one load.  The exchange areas are clean
-    // (all zero) between calls unless a wait timed out; such a workspace is refused
-    // for selection until idx_device_status() has read the error and re-initialised it.
-    const uint64_t hdr = *reinterpret_cast<const uint64_t*>(ws + WS_MAGIC_OFF);
-    if ((uint32_t)hdr != WS_MAGIC) {
-      if (tid == 0 && c == 0 && g == 0) raise_error(ws, IDX_DERR_WS);
-      return;
-    }
-    if (do_select && ((uint32_t)(hdr >> 32) & IDX_DERR_TIMEOUT)) return;
+  const bool do_pub = (a.mode & MODE_PUBLISH) != 0;
+  if (*reinterpret_cast<const uint32_t*>(ws + WS_MAGIC_OFF) != WS_MAGIC) {
+    if (tid == 0 && c == 0 && g == 0) raise_error(ws, IDX_DERR_WS);
+    return;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   if (do_score) {
@@ -1206,41 +1136,20 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
     if (v > nmax) { nmax = v; rmax = i; }
   }
   if (err && tid == 0) raise_error(ws, err);
-  if (nmax == 0) {                                // every row of the group is empty
-    if (c == 0 && do_select)
-      for (int i = 0; i < R; i++)
-        for (int p = tid; p < a.k; p += NT) a.topk[(int64_t)(row0 + i) * a.k + p] = -1;
-    return;
-  }
   if (chunk_base >= nmax) return;                 // nothing of this group here
-  const int wact = (nmax + C - 1) >> a.chunk_shift;   // chunks holding keys of this group (C = 2^shift)
   const int k = a.k;
-  // how row i selects: nothing to select (n <= k), from all its keys at once (n <=
-  // ALL_MAX), from per-chunk candidates (up to 4 chunks per finishing thread), or by
-  // a multi-pass select over its scores in memory
-  auto thr_mode = [&](int nr) { return nr > k && nr > ALL_MAX && wact <= 4 * NT; };
-  auto all_mode = [&](int nr) { return nr > k && nr <= ALL_MAX; };
-  // rows whose finisher may read scores back from memory (after "scores visible")
-  auto sv_row = [&](int nr) { return do_score && nr > k && nr > ALL_MAX; };
-  // finisher of row i: chunk wact - 1 - (i % wact)
-  bool is_fin = false;
-#pragma unroll
-  for (int i = 0; i < GR; i++) is_fin |= (i < R) && (c == wact - 1 - (i < wact ? i : i % wact));
-  if (given && !is_fin) {
+  const int shift = a.chunk_shift;
+  if (!do_score) {
     // over given scores, only rows selecting from candidates need this chunk
     bool needed = false;
 #pragma unroll
-    for (int i = 0; i < GR; i++) needed |= (i < R) && thr_mode(n[i]);
+    for (int i = 0; i < GR; i++) needed |= (i < R) && chunk_base < n[i] && row_path(n[i], k, shift) == PATH_CAND;
     if (!needed) return;
   }
 
   float* const sc_lds = LDS_PTR(float, L_SC);
-  const int64_t ms = a.meta_stride;
-  const int64_t es = a.ent_stride;      // chunk slots of the candidate area (<= 4 NT)
   uint64_t* const meta = reinterpret_cast<uint64_t*>(ws + a.off_meta);
   uint64_t* const ent = reinterpret_cast<uint64_t*>(ws + a.off_ent);
-  uint32_t* const sv = reinterpret_cast<uint32_t*>(ws + a.off_sv);
-  uint32_t* const allk = reinterpret_cast<uint32_t*>(ws + a.off_allk);
 
   if (do_score) {
     int phys[P];
@@ -1269,21 +1178,17 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
     }
     __syncthreads();
   }
-  int* misc = LDS_PTR(int, L_MISC);
-  const bool skip_me = (c == a.skip_chunk);
 
-  // ---------------- publish (wave i handles row i); no waits ------------------------
-  // Every exchange word is written through to memory and is nonzero once written; the
-  // finisher polls until it reads nonzero, then clears it, so the areas are all zero
-  // again when the call ends.
-  if (do_select && wv < R && !skip_me) {
+  // ---------------- publish (wave i handles row i) -----------------------------------
+  if (do_pub && wv < R) {
     const int i = wv;
     const int nr = n[i];
-    const int grow = row0 + i;
     const int nv = nr - chunk_base;
-    if (thr_mode(nr)) {
+    if (nv > 0 && row_path(nr, k, shift) == PATH_CAND) {
       // candidates: every key of the chunk >= t_w (the m-th largest of the 64 lane
-      // maxima), as (key << 32 | position), in ascending position order
+      // maxima), as (key << 32 | position), in ascending position order; a chunk with
+      // more than cap of them publishes none and is flagged
+      const int grow = row0 + i;
       int m, cap;
       candidate_params(nr, C, k, &m, &cap);
       uint32_t key[8];
@@ -1302,31 +1207,23 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
       const int total = __shfl(incl, 63);
       uint32_t cw;
       if (total > cap) {
-        cw = 1u << 16;  // overflow: nothing published, the finisher re-reads this chunk
+        cw = 1u << 16;
       } else {
         int o = incl - cnt;
-        uint64_t* dst = ent + ((int64_t)grow * es + c) * CAP_MAX;
+        uint64_t* dst = ent + ((int64_t)grow * a.ent_stride + c) * CAP_MAX;
 #pragma unroll
         for (int j = 0; j < 8; j++)
           if (key[j] != 0u && key[j] >= thr) {
-            st_co64(dst + o, ((uint64_t)key[j] << 32) | (uint32_t)(chunk_base + lane * 8 + j));
+            dst[o] = ((uint64_t)key[j] << 32) | (uint32_t)(chunk_base + lane * 8 + j);
             o++;
           }
         cw = (uint32_t)total;
       }
-      if (lane == 0) st_co64(meta + (int64_t)grow * ms + c, ((uint64_t)thr << 32) | 0x80000000u | cw);
-    } else if (all_mode(nr) && do_score) {
-      // every key of the chunk, at its position (finite scores have nonzero keys)
-      uint32_t* dst = allk + (int64_t)grow * a.all_stride + chunk_base;
-#pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const int p = j * 64 + lane;
-        if (p < nv && p < C) st_co32(dst + p, radix_key(sc_lds[i * CMAX + p]));
-      }
+      if (lane == 0) meta[(int64_t)grow * a.meta_stride + c] = ((uint64_t)thr << 32) | cw;
     }
   }
 
-  // ---------------- scores out (write-through: a finisher may re-read them) ----------
+  // ---------------- scores out -------------------------------------------------------
   if (do_score) {
 #pragma unroll
     for (int i = 0; i < GR; i++) {
@@ -1335,149 +1232,114 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
       float* dst = a.scores + (int64_t)(row0 + i) * a.ld + chunk_base;
       __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, (int64_t)(nv > 0 ? (nv < C ? nv : C) : 0) * 4);
       for (int p = tid; p < C; p += NT)
-        if (p < nv)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_lds[i * CMAX + p]), rs, p * 4, 0, CP_COHERENT);
+        if (p < nv) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_lds[i * CMAX + p]), rs, p * 4, 0, 0);
     }
   }
-  // "scores visible" words of rows selecting from candidates, once this chunk's scores
-  // have reached memory.  A finisher writes its own later, when it next waits anyway.
-  auto publish_sv = [&]() {
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (tid < R && !skip_me && sv_row(n[tid])) st_co32(sv + (int64_t)(row0 + tid) * ms + c, 1u);
-  };
-  if (!do_select) return;
-  if (!is_fin) {
-    if (do_score) publish_sv();
+}
+
+// ---------------------------------------------------------------------------
+// Launch 2: workgroup (i, g) selects row i of request g.  Launch 1 has ended, so its
+// scores and candidates are in memory.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = wave_id();
+  const uint32_t ge = a.grp[blockIdx.y];
+  const int R = (int)(ge >> 24);
+  const int i = blockIdx.x;
+  if (i >= R) return;
+  const int grow = (int)(ge & 0xFFFFFFu) + i;
+  uint8_t* const ws = a.ws;
+  if (*reinterpret_cast<const uint32_t*>(ws + WS_MAGIC_OFF) != WS_MAGIC) {
+    if (tid == 0 && i == 0 && blockIdx.y == 0) raise_error(ws, IDX_DERR_WS);
     return;
   }
-  bool sv_done = !do_score;
-  __syncthreads();
-
-  // ---------------- finish the rows this chunk is designated for ---------------------
-  const int spin_limit = a.spin_limit > 0 ? a.spin_limit : DEFAULT_SPIN;
+  const int gbound = a.gmax[blockIdx.y];
+  int nr = __builtin_amdgcn_readfirstlane(a.nk[grow]);
+  if (nr < 0 || nr > gbound) {
+    if (tid == 0) raise_error(ws, IDX_DERR_NKEYS);
+    nr = nr < 0 ? 0 : gbound;
+  }
+  const int k = a.k, C = a.chunk;
+  int32_t* out = a.topk + (int64_t)grow * k;
+  const int path = row_path(nr, k, a.chunk_shift);
+  if (path == PATH_NONE) {
+    for (int p = tid; p < k; p += NT) out[p] = p < nr ? p : -1;
+    return;
+  }
+  int* misc = LDS_PTR(int, L_MISC);
   uint32_t* hist = LDS_PTR(uint32_t, L_HIST);
   uint32_t* FK = LDS_PTR(uint32_t, L_FK);
   uint32_t* FP = LDS_PTR(uint32_t, L_FP);
   uint32_t* bm = LDS_PTR(uint32_t, L_BM);
-#pragma unroll 1
-  for (int i = 0; i < R; i++) {
-    const int fin = wact - 1 - (i < wact ? i : i % wact);
-    if (c != fin) continue;
-    const int grow = row0 + i;
-    const int nr = n[i];
-    int32_t* out = a.topk + (int64_t)grow * k;
-    if (nr <= k) {
-      for (int p = tid; p < k; p += NT) out[p] = p < nr ? p : -1;
-      continue;
+  const float* srow = a.scores + (int64_t)grow * a.ld;
+  __amdgpu_buffer_rsrc_t rs = make_rsrc(srow, (int64_t)nr * 4);
+  bool done = false;
+  if (path == PATH_ALL) {
+    // every key of the row into LDS (FK[p] for position p), coalesced: thread t reads
+    // positions t + NT j
+    constexpr int JA = ALL_MAX / NT;
+    const int J = (nr + NT - 1) / NT;
+    uint32_t kv[JA];
+#pragma unroll
+    for (int j = 0; j < JA; j++)
+      kv[j] = j < J ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, tid * 4, j * NT * 4, 0) : 0u;
+#pragma unroll
+    for (int j = 0; j < JA; j++)
+      if (j < J) FK[j * NT + tid] = radix_key(__uint_as_float(kv[j]));
+    __syncthreads();
+    int got = -1;
+    done = select_emit<56, true>(FK, FP, nr, 0u, k, hist, misc, out, &got);
+    if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
+  } else if (path == PATH_CAND) {
+    // ---- chunk words: thread t reads the words of chunks t + NT u (u < upt)
+    const int wact = (nr + C - 1) >> a.chunk_shift;
+    const int upt = (wact + NT - 1) / NT;
+    const uint64_t* mrow = reinterpret_cast<const uint64_t*>(ws + a.off_meta) + (int64_t)grow * a.meta_stride;
+    const uint64_t* erow = reinterpret_cast<const uint64_t*>(ws + a.off_ent) + (int64_t)grow * a.ent_stride * CAP_MAX;
+    __amdgpu_buffer_rsrc_t rmeta = make_rsrc(mrow, (int64_t)wact * 8);
+    uint64_t mv[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+      mv[u] = (u < upt) ? __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rmeta, (tid + NT * u) * 8, 0, 0))
+                        : 0ull;
+    int m_unused, cap;
+    candidate_params(nr, C, k, &m_unused, &cap);
+    uint8_t* cnt8 = LDS_PTR(uint8_t, L_CO);
+    uint32_t* gcnt = LDS_PTR(uint32_t, L_GRP);
+    uint32_t* gbase = gcnt + 256;
+    if (tid < 256) gcnt[tid] = 0;
+    __syncthreads();
+    // per chunk: its count (cnt8), per group of 8 chunks: the count (gcnt); bm[w] =
+    // t_w (0xFFFFFFFF: overflowed, published nothing) for the rare path; E = the
+    // candidates published, t* = the largest t_w, whether any chunk overflowed
+    uint32_t pub = 0, tmax = 0, ovs = 0;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int w = tid + NT * u;
+      if (u >= upt) break;
+      const uint32_t lw = (uint32_t)mv[u];
+      const bool live = w < wact;
+      const bool ov = live && ((lw >> 16) & 1u);
+      const uint32_t cu = (live && !ov) ? (lw & 0xFFFFu) : 0u;
+      const uint32_t twu = (uint32_t)(mv[u] >> 32);
+      cnt8[w] = (uint8_t)cu;                       // w < 4 NT: bytes past wact read as 0
+      if (cu) atomicAdd(&gcnt[w >> 3], cu);
+      pub += cu;
+      ovs += ov ? 1u : 0u;
+      if (live && !ov) tmax = max(tmax, twu);
+      if (live) bm[w] = ov ? 0xFFFFFFFFu : twu;
     }
-    const float* srow = a.scores + (int64_t)grow * a.ld;
-    __amdgpu_buffer_rsrc_t rs = make_rsrc(srow, (int64_t)nr * 4);
-    bool ok = true, done = false, implicit = false, cert = false;
-    int E = 0;                 // candidates in LDS, in position order
-    uint32_t lo = 0;           // candidates below lo do not count
-    const uint64_t* mrow = meta + (int64_t)grow * ms;
-    uint64_t* erow = ent + (int64_t)grow * es * CAP_MAX;
-    if (all_mode(nr)) {
-      // ---- every key of the row into LDS (FK[p] for position p), coalesced: thread t
-      // reads positions t + NT j.  Positions past the row are outside the buffer
-      // resource: their loads return 0 and their stores are dropped.
-      constexpr int JA = ALL_MAX / NT;
-      const int J = (nr + NT - 1) / NT;
-      if (do_score) {
-        uint32_t* krow = allk + (int64_t)grow * a.all_stride;
-        __amdgpu_buffer_rsrc_t rk = make_rsrc(krow, (int64_t)nr * 4);
-        uint32_t kv[JA];
-#pragma unroll
-        for (int j = 0; j < JA; j++)
-          kv[j] = j < J ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, tid * 4, j * NT * 4, CP_COHERENT) : 0u;
-        // every key has landed once nr of them are nonzero
-        int spins = 0;
-        while (true) {
-          uint32_t nz = 0;
-#pragma unroll
-          for (int j = 0; j < JA; j++) nz += kv[j] != 0u ? 1u : 0u;
-          if (block_sum(nz, misc) == (uint32_t)nr) break;
-          if (++spins >= spin_limit) { ok = false; break; }
-          __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-          for (int j = 0; j < JA; j++)
-            if (j < J && kv[j] == 0u)
-              kv[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, tid * 4, j * NT * 4, CP_COHERENT);
-        }
-#pragma unroll
-        for (int j = 0; j < JA; j++)
-          if (j < J) FK[j * NT + tid] = kv[j];
-        if (ok) {
-#pragma unroll
-          for (int j = 0; j < JA; j++)
-            if (j < J) __builtin_amdgcn_raw_buffer_store_b32(0u, rk, tid * 4, j * NT * 4, CP_COHERENT);
-        }
-      } else {
-        uint32_t kv[JA];
-#pragma unroll
-        for (int j = 0; j < JA; j++)
-          kv[j] = j < J ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, tid * 4, j * NT * 4, 0) : 0u;
-#pragma unroll
-        for (int j = 0; j < JA; j++)
-          if (j < J) FK[j * NT + tid] = radix_key(__uint_as_float(kv[j]));
-      }
-      __syncthreads();
-      E = nr;
-      implicit = true;
-      cert = true;
-    } else if (thr_mode(nr)) {
-      // ---- chunk words: thread t reads the words of chunks t + NT u (u < upt)
-      const int upt = (wact + NT - 1) / NT;
-      __amdgpu_buffer_rsrc_t rmeta = make_rsrc(mrow, (int64_t)wact * 8);
-      uint64_t mv[4] = {0, 0, 0, 0};
-      int m_unused, cap;
-      candidate_params(nr, C, k, &m_unused, &cap);
-      uint8_t* cnt8 = LDS_PTR(uint8_t, L_CO);
-      uint32_t* gcnt = LDS_PTR(uint32_t, L_GRP);
-      uint32_t* gbase = gcnt + 256;
-      if (tid < 256) gcnt[tid] = 0;
-      {
-        int spins = 0;
-        while (true) {
-          bool miss = false;
-#pragma unroll
-          for (int u = 0; u < 4; u++)
-            if (u < upt && tid + NT * u < wact && mv[u] == 0) {
-              mv[u] = __builtin_bit_cast(uint64_t,
-                                         __builtin_amdgcn_raw_buffer_load_b64(rmeta, (tid + NT * u) * 8, 0, CP_COHERENT));
-              miss |= mv[u] == 0;
-            }
-          if (!block_any(miss, misc)) break;
-          if (++spins >= spin_limit) { ok = false; break; }
-          __builtin_amdgcn_s_sleep(1);
-        }
-      }
-      // per chunk: its count (cnt8), per group of 8 chunks: the count (gcnt); bm[w] =
-      // t_w (0xFFFFFFFF: overflowed, published nothing) for the rare path; E = the
-      // candidates published, t* = the largest t_w, whether any chunk overflowed
-      uint32_t pub = 0, tmax = 0, ovs = 0;
-#pragma unroll
-      for (int u = 0; u < 4; u++) {
-        const int w = tid + NT * u;
-        if (u >= upt) break;
-        const uint32_t lw = (uint32_t)mv[u];
-        const bool live = w < wact;
-        const bool ov = live && ((lw >> 16) & 1u);
-        const uint32_t cu = (live && !ov) ? (lw & 0xFFFFu) : 0u;
-        const uint32_t twu = (uint32_t)(mv[u] >> 32);
-        cnt8[w] = (uint8_t)cu;                       // w < 4 NT: bytes past wact read as 0
-        if (cu) atomicAdd(&gcnt[w >> 3], cu);
-        pub += cu;
-        ovs += ov ? 1u : 0u;
-        if (live && !ov) tmax = max(tmax, twu);
-        if (live) bm[w] = ov ? 0xFFFFFFFFu : twu;
-      }
-      uint32_t t3[3] = {pub, tmax, ovs};
-      block_sum_max_sum(t3, misc);
-      pub = t3[0];
-      tmax = t3[1];
-      ovs = t3[2];
+    uint32_t t3[3] = {pub, tmax, ovs};
+    block_sum_max_sum(t3, misc);
+    const int E = (int)t3[0];
+    // keys >= t* are all published (t* is at least every chunk's t_w): if k of them are
+    // here, the k-th is among them and no chunk hides a key of the top k
+    const uint32_t lo = t3[1];
+    ovs = t3[2];
+    if (E <= FIN_ENT - 64) {
       // group bases: an exclusive scan of the 256 group counts (wave 0, 4 a lane)
       if (wv == 0) {
         const v4i c4 = reinterpret_cast<const v4i*>(gcnt)[lane];
@@ -1486,59 +1348,22 @@ __global__ __launch_bounds__(NT, 1) void idx_kernel(const KArgs a) {
         reinterpret_cast<v4i*>(gbase)[lane] = v4i{b, b + c4[0], b + c4[0] + c4[1], b + c4[0] + c4[1] + c4[2]};
       }
       __syncthreads();
-      E = (int)pub;
-      // keys >= t* are all published (t* is at least every chunk's t_w): if k of them
-      // are here, the k-th is among them and no chunk hides a key of the top k
-      lo = tmax;
-      if (ok && E <= FIN_ENT - 64) {
-        if (cap > 64) ok = gather_candidates<2, true>(erow, wact, cnt8, gbase, spin_limit, FK, FP);
-        else ok = gather_candidates<1, true>(erow, wact, cnt8, gbase, spin_limit, FK, FP);
-        ok = !block_any(!ok, misc);
-      } else if (ok) {
-        // too many candidates for the LDS: await and clear them without keeping any
-        if (cap > 64) ok = gather_candidates<2, false>(erow, wact, cnt8, gbase, spin_limit, FK, FP);
-        else ok = gather_candidates<1, false>(erow, wact, cnt8, gbase, spin_limit, FK, FP);
-        ok = !block_any(!ok, misc);
+      if (cap > 64) gather_candidates<2>(erow, wact, cnt8, gbase, FK, FP);
+      else gather_candidates<1>(erow, wact, cnt8, gbase, FK, FP);
+      __syncthreads();
+      if (ovs == 0) {
+        int got = -1;
+        done = select_emit<32, false>(FK, FP, E, lo, k, hist, misc, out, &got);
+        if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
       }
-      cert = ovs == 0 && E <= FIN_ENT - 64;
+      if (!done && nr <= BITMAP_KEYS) done = rare_select(ws, nr, k, wact, E, C, rs, FK, FP, bm, hist, misc, out);
     }
-    if (ok && !sv_done) { publish_sv(); sv_done = true; }
-    if (ok && cert) {
-      // ---- select from the E candidates in LDS (position order)
-      int got = -1;
-      if (implicit) done = select_emit<56, true>(FK, FP, E, lo, k, hist, misc, out, &got);
-      else done = select_emit<32, false>(FK, FP, E, lo, k, hist, misc, out, &got);
-      if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
-    }
-    if (ok && !done && thr_mode(nr) && E <= FIN_ENT - 64 && nr <= BITMAP_KEYS) {
-      const int st = rare_select(a, grow, nr, k, wact, E, C, rs, sv + (int64_t)grow * ms, do_score, spin_limit,
-                                 FK, FP, bm, hist, misc, out);
-      if (st < 0) ok = false;
-      done = st > 0;
-    }
-    if (thr_mode(nr) && ok)
-      for (int w = tid; w < wact; w += NT) st_co64(meta + (int64_t)grow * ms + w, 0ull);
-    if (ok && !done) {
-      // ---- exact multi-pass select over the row's scores in memory
-      if (do_score) ok = wait_nonzero(sv + (int64_t)grow * ms, wact, spin_limit, misc);
-      if (ok) {
-        __syncthreads();
-        global_select_row(srow, nr, k, out, hist, misc);
-      }
-    }
-    if (ok && sv_row(nr)) {
-      // every chunk's "scores visible" word has been written: clear them
-      ok = wait_nonzero(sv + (int64_t)grow * ms, wact, spin_limit, misc);
-      if (ok)
-        for (int w = tid; w < wact; w += NT) st_co32(sv + (int64_t)grow * ms + w, 0u);
-    }
-    if (!ok) {
-      if (tid == 0) raise_error(ws, IDX_DERR_TIMEOUT);
-      for (int p = tid; p < k; p += NT) out[p] = -1;
-    }
-    __syncthreads();
   }
-  if (!sv_done) publish_sv();
+  if (!done) {
+    // ---- exact multi-pass select over the row's scores in memory
+    __syncthreads();
+    global_select_row(srow, nr, k, out, hist, misc);
+  }
 }
 
 __global__ void fill_kernel(uint32_t* p, int64_t words, uint32_t magic) {
@@ -1550,8 +1375,6 @@ __global__ void fill_kernel(uint32_t* p, int64_t words, uint32_t magic) {
 // host side
 // ---------------------------------------------------------------------------
 thread_local char g_hip_err[256] = "";
-int g_spin_limit = 0;
-int g_skip_chunk = -1;
 bool g_attr_done = false;
 
 int hip_fail(hipError_t e) {
@@ -1588,8 +1411,8 @@ Plan plan_topk(int max_keys) {
 }
 
 struct WsLayout {
-  uint64_t off_meta, off_sv, off_ent, off_allk, total;
-  int meta_stride, ent_stride, all_stride;
+  uint64_t off_meta, off_ent, total;
+  int meta_stride, ent_stride;
 };
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -1600,13 +1423,9 @@ WsLayout layout_for(int rows, int max_keys) {
   WsLayout L;
   L.meta_stride = stride;
   L.ent_stride = stride < 4 * NT ? stride : 4 * NT;
-  L.all_stride = (max_keys < ALL_MAX ? max_keys : ALL_MAX);
-  L.all_stride = L.all_stride < 4 ? 4 : (L.all_stride + 3) & ~3;
   L.off_meta = WS_HDR;
-  L.off_sv = align256(L.off_meta + (uint64_t)rows * stride * 8);
-  L.off_ent = align256(L.off_sv + (uint64_t)rows * stride * 4);
-  L.off_allk = align256(L.off_ent + (uint64_t)rows * L.ent_stride * CAP_MAX * 8);
-  L.total = align256(L.off_allk + (uint64_t)rows * L.all_stride * 4);
+  L.off_ent = align256(L.off_meta + (uint64_t)rows * stride * 8);
+  L.total = align256(L.off_ent + (uint64_t)rows * L.ent_stride * CAP_MAX * 8);
   return L;
 }
 
@@ -1638,51 +1457,60 @@ int validate_problem(const idx_problem* p) {
   return IDX_OK;
 }
 
+constexpr int SCORE_LDS = L_SCORE_END;
+constexpr int SELECT_LDS = L_FIN_END;
+
 int set_attrs() {
   if (g_attr_done) return IDX_OK;
-  hipError_t e;
-  if ((e = hipFuncSetAttribute((const void*)idx_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES)) != hipSuccess) return hip_fail(e);
-  if ((e = hipFuncSetAttribute((const void*)idx_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES)) != hipSuccess) return hip_fail(e);
-  if ((e = hipFuncSetAttribute((const void*)idx_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES)) != hipSuccess) return hip_fail(e);
-  if ((e = hipFuncSetAttribute((const void*)idx_kernel<8>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES)) != hipSuccess) return hip_fail(e);
+  const void* fs[5] = {(const void*)score_kernel<1>, (const void*)score_kernel<2>, (const void*)score_kernel<4>,
+                       (const void*)score_kernel<8>, (const void*)select_kernel};
+  for (int i = 0; i < 5; i++) {
+    const hipError_t e =
+        hipFuncSetAttribute(fs[i], hipFuncAttributeMaxDynamicSharedMemorySize, i < 4 ? SCORE_LDS : SELECT_LDS);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   g_attr_done = true;
   return IDX_OK;
 }
 
-int launch(const KArgs& args, int P, dim3 grid, hipStream_t st) {
+// Launch 1 (grid: chunks x groups), then, when selecting, launch 2 (grid: rows of a
+// group x groups) on the same stream.
+int launch(const KArgs& args, int P, dim3 grid, bool score_launch, bool select_launch, hipStream_t st) {
   int rc = set_attrs();
   if (rc) return rc;
-  switch (P) {
-    case 1: hipLaunchKernelGGL(idx_kernel<1>, grid, dim3(NT), LDS_BYTES, st, args); break;
-    case 2: hipLaunchKernelGGL(idx_kernel<2>, grid, dim3(NT), LDS_BYTES, st, args); break;
-    case 4: hipLaunchKernelGGL(idx_kernel<4>, grid, dim3(NT), LDS_BYTES, st, args); break;
-    default: hipLaunchKernelGGL(idx_kernel<8>, grid, dim3(NT), LDS_BYTES, st, args); break;
+  if (score_launch) {
+    switch (P) {
+      case 1: hipLaunchKernelGGL(score_kernel<1>, grid, dim3(NT), SCORE_LDS, st, args); break;
+      case 2: hipLaunchKernelGGL(score_kernel<2>, grid, dim3(NT), SCORE_LDS, st, args); break;
+      case 4: hipLaunchKernelGGL(score_kernel<4>, grid, dim3(NT), SCORE_LDS, st, args); break;
+      default: hipLaunchKernelGGL(score_kernel<8>, grid, dim3(NT), SCORE_LDS, st, args); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e);
   }
-  hipError_t e = hipGetLastError();
-  return e == hipSuccess ? IDX_OK : hip_fail(e);
+  if (select_launch) {
+    hipLaunchKernelGGL(select_kernel, dim3(IDX_GROUP_ROWS, grid.y), dim3(NT), SELECT_LDS, st, args);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return IDX_OK;
 }
 
-void fill_common(KArgs& args, const WsLayout& L, void* ws, size_t ws_bytes) {
+void fill_common(KArgs& args, const WsLayout& L, void* ws) {
   args.ws = static_cast<uint8_t*>(ws);
-  (void)ws_bytes;
-  args.spin_limit = g_spin_limit;
-  args.skip_chunk = g_skip_chunk;
   args.meta_stride = L.meta_stride;
   args.ent_stride = L.ent_stride;
-  args.all_stride = L.all_stride;
   args.off_meta = L.off_meta;
   args.off_ent = L.off_ent;
-  args.off_sv = L.off_sv;
-  args.off_allk = L.off_allk;
 }
 
 int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int32_t* topk, void* ws,
-                size_t ws_bytes, void* stream, int mode) {
+                size_t ws_bytes, void* stream, bool select) {
   int rc = validate_problem(p);
   if (rc) return rc;
   if (!scores || ld < 1 || ld < (int64_t)p->max_keys) return IDX_EINVAL;
   if ((int64_t)p->rows > INT64_MAX / ld) return IDX_EINVAL;
-  if (mode & MODE_SELECT) {
+  if (select) {
     if (k < 1 || k > IDX_KMAX || !topk) return IDX_EINVAL;
   } else {
     k = 1;
@@ -1709,14 +1537,14 @@ int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int3
   args.k = k;
   args.chunk = pl.chunk;
   args.chunk_shift = 31 - __builtin_clz((unsigned)pl.chunk);
-  args.mode = mode;
-  fill_common(args, L, ws, ws_bytes);
+  args.mode = select ? (MODE_SCORE | MODE_PUBLISH) : MODE_SCORE;
+  fill_common(args, L, ws);
   for (int j = 0; j < p->num_req; j++) {
     args.grp[j] = (uint32_t)p->req_indptr[j] | ((uint32_t)(p->req_indptr[j + 1] - p->req_indptr[j]) << 24);
     const int bound = p->req_max_keys ? p->req_max_keys[j] : p->max_keys;
     args.gmax[j] = bound;
   }
-  return launch(args, pl.pages_per_wg, dim3(pl.wg, p->num_req), static_cast<hipStream_t>(stream));
+  return launch(args, pl.pages_per_wg, dim3(pl.wg, p->num_req), true, select, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -1743,12 +1571,12 @@ int idx_workspace_init(void* ws, size_t ws_bytes, void* stream) {
 }
 
 int idx_score(const idx_problem* p, float* scores, int64_t ld_scores, void* ws, size_t ws_bytes, void* stream) {
-  return run_problem(p, 1, scores, ld_scores, nullptr, ws, ws_bytes, stream, MODE_SCORE);
+  return run_problem(p, 1, scores, ld_scores, nullptr, ws, ws_bytes, stream, false);
 }
 
 int idx_score_topk(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores, int32_t* topk, void* ws,
                    size_t ws_bytes, void* stream) {
-  return run_problem(p, k, scores, ld_scores, topk, ws, ws_bytes, stream, MODE_SCORE | MODE_SELECT);
+  return run_problem(p, k, scores, ld_scores, topk, ws, ws_bytes, stream, true);
 }
 
 int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys, int32_t rows, int32_t max_keys,
@@ -1779,15 +1607,16 @@ int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys, int3
     args.k = k;
     args.chunk = pl.chunk;
     args.chunk_shift = 31 - __builtin_clz((unsigned)pl.chunk);
-    args.mode = MODE_SELECT;
-    fill_common(args, L, ws, ws_bytes);
+    args.mode = MODE_PUBLISH;
+    fill_common(args, L, ws);
     for (int gi = 0; gi < groups; gi++) {
       const int a0 = r0 + gi * IDX_GROUP_ROWS;
       const int an = (rows - a0) < IDX_GROUP_ROWS ? (rows - a0) : IDX_GROUP_ROWS;
       args.grp[gi] = (uint32_t)a0 | ((uint32_t)an << 24);
       args.gmax[gi] = max_keys;
     }
-    int rc = launch(args, pl.pages_per_wg, dim3(pl.wg, groups), st);
+    // launch 1 only publishes candidates, which no row needs below ALL_MAX keys
+    int rc = launch(args, pl.pages_per_wg, dim3(pl.wg, groups), max_keys > ALL_MAX, true, st);
     if (rc) return rc;
   }
   return IDX_OK;
@@ -1804,17 +1633,9 @@ int idx_device_status(void* ws, size_t ws_bytes, void* stream, uint32_t* detail)
   const uint32_t err = (hdr[0] != WS_MAGIC) ? (hdr[1] | IDX_DERR_WS) : hdr[1];
   if (detail) *detail = err;
   if (err) {
-    if ((err & IDX_DERR_TIMEOUT) && hdr[0] == WS_MAGIC) {
-      // a timed-out exchange leaves words behind: start the workspace afresh
-      const int rc = idx_workspace_init(ws, ws_bytes & ~(size_t)255, stream);
-      if (rc) return rc;
-      e = hipStreamSynchronize(st);
-      if (e != hipSuccess) return hip_fail(e);
-    } else {
-      uint32_t zero = 0;
-      e = hipMemcpy(static_cast<uint8_t*>(ws) + WS_ERR_OFF, &zero, 4, hipMemcpyHostToDevice);
-      if (e != hipSuccess) return hip_fail(e);
-    }
+    uint32_t zero = 0;
+    e = hipMemcpy(static_cast<uint8_t*>(ws) + WS_ERR_OFF, &zero, 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e);
     return IDX_EDEVICE;
   }
   return IDX_OK;
@@ -1833,11 +1654,5 @@ const char* idx_strerror(int code) {
 }
 
 const char* idx_last_hip_error(void) { return g_hip_err; }
-
-int idx_debug_set(int32_t key, int32_t value) {
-  if (key == 1 && value >= 0) { g_spin_limit = value; return IDX_OK; }
-  if (key == 2 && value >= -1) { g_skip_chunk = value; return IDX_OK; }
-  return IDX_EINVAL;
-}
 
 }  // extern "C"

@@ -27,7 +27,7 @@ def header_functions():
 
 def test_exports_every_declared_function(L):
     names = header_functions()
-    assert len(names) >= 10
+    assert len(names) >= 9
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -52,7 +52,7 @@ def test_header_constants_match_binding():
 
 
 def test_abi_version_and_strerror(L):
-    assert L.idx_abi_version() == 1
+    assert L.idx_abi_version() == 2
     for c in range(6):
         assert len(L.idx_strerror(c)) > 0
     assert b"unknown" in L.idx_strerror(99)
@@ -63,7 +63,7 @@ def test_workspace_bytes(L):
     out = ctypes.c_size_t(0)
     assert L.idx_workspace_bytes(4, 131072, 2048, ctypes.byref(out)) == 0
     big = out.value
-    assert big % 256 == 0 and big > 4 * 256 * 144 * 8
+    assert big % 256 == 0 and big >= 4 * 256 * 128 * 8     # candidate slots: rows x chunks x 128 x 8 B
     assert L.idx_workspace_bytes(1, 4096, 2048, ctypes.byref(out)) == 0
     assert 0 < out.value < big
     assert L.idx_workspace_bytes(0, 10, 2048, ctypes.byref(out)) == _lib.IDX_EINVAL
@@ -183,9 +183,3 @@ def test_workspace_init_and_status_validation(L):
     assert L.idx_workspace_init(FAKE, 1000, None) == _lib.IDX_EINVAL
     assert L.idx_device_status(None, 1024, None, None) == _lib.IDX_EINVAL
 
-
-def test_debug_hook_validation(L):
-    assert L.idx_debug_set(1, -5) == _lib.IDX_EINVAL
-    assert L.idx_debug_set(7, 0) == _lib.IDX_EINVAL
-    assert L.idx_debug_set(1, 0) == _lib.IDX_OK
-    assert L.idx_debug_set(2, -1) == _lib.IDX_OK

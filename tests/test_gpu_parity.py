@@ -101,19 +101,17 @@ def test_deterministic_and_layout_invariant():
     assert np.array_equal(a["lists"], c["lists"])
 
 
-def test_exchange_areas_are_left_clean():
-    """Every word a call posts between workgroups is cleared by its reader, so the
-    workspace past its header is all zero again after fused, score-only and top-k
-    calls, over the row kinds (all keys, candidates, short rows, re-read chunks)."""
+def test_stale_workspace_contents_are_ignored():
+    """A call reads back only the candidate words its own scoring launch wrote: a
+    workspace whose body (past its 256-byte header) holds random bytes gives the
+    same results, over the row kinds (all keys, candidates, short rows, re-read
+    chunks)."""
     import key_scoring_exact_amd as idx
-    ws = None
+    ws = idx.Workspace(16, 60000, 2048)
+    gen = torch.Generator(device="cuda").manual_seed(12)
     for prob in [make_problem([60000], [4], seed=9), make_problem([700, 9000, 40000], [2, 4, 3], seed=10),
                  make_problem([40000], [4], seed=11, keys="recent", recent=4096)]:
-        dp = device_problem(prob)
-        if ws is None or ws.nbytes < idx.workspace_bytes(prob.rows, dp.max_keys, prob.k):
-            ws = idx.Workspace(16, 60000, prob.k)
+        body = ws.buf[ws.offset + 256: ws.offset + ws.nbytes]
+        body.copy_(torch.randint(0, 256, body.shape, dtype=torch.uint8, device="cuda", generator=gen))
         res = run_all(prob, ws=ws)
         check_against_oracle(prob, res)
-        torch.cuda.synchronize()
-        body = ws.buf[ws.offset + 256: ws.offset + ws.nbytes]
-        assert int(torch.count_nonzero(body).item()) == 0, prob.name
