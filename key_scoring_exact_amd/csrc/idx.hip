@@ -53,13 +53,11 @@ constexpr int NT = 512;                 // threads per workgroup: 8 waves, two p
 constexpr int NWAVE = NT / 64;
 constexpr int PMAX = 8;                 // pages per workgroup at most
 constexpr int CMAX = PMAX * PS;         // keys per chunk at most (512)
-constexpr int LOOKAHEAD = 3;            // pages in flight ahead of the page being scored
+constexpr int LOOKAHEAD = PMAX - 1;     // pages in flight ahead of the page being scored (all of them)
 constexpr int ALL_MAX = 24576;          // rows up to this many keys select from all scores at once
-constexpr int FIN_ENT = 12288;          // candidate capacity of a finishing workgroup (the last 64
-                                        // slots take the writes of empty lanes)
+constexpr int FIN_ENT = 12288;          // candidate capacity of a selecting workgroup
 constexpr int BITMAP_KEYS = 131072;     // positions covered by the finisher's LDS bitmap
 constexpr int CAP_MAX = 128;            // candidate slots per chunk and row
-constexpr int LOAD_BATCH = 32;          // candidate loads in flight per thread
 constexpr uint32_t WS_MAGIC = 0x1D5C0DE5u;
 
 constexpr int MODE_SCORE = 1;           // compute scores (else read them from args.scores)
@@ -73,18 +71,17 @@ constexpr int L_Q = L_SC + GR * CMAX * 4;                   // [GR][64 heads][25
 constexpr int L_W = L_Q + GR * H * D * 2;                   // [GR][64] bf16 head weights
 constexpr int L_SCORE_END = L_W + GR * H * 2;
 // LDS layout, finishing phase
-constexpr int L_FK = 0;                                     // candidate keys: FIN_ENT
-constexpr int L_FP = FIN_ENT * 4;                           // positions: FIN_ENT
-constexpr int L_BM = FIN_ENT * 8;                           // bitmap: BITMAP_KEYS / 32 words
 constexpr int HIST_WORDS = 4096 + 64;                       // one histogram: 4096 bins + 64 per-lane dummies
-constexpr int L_HIST = L_BM + BITMAP_KEYS / 8;              // 2 histograms
+constexpr int L_HIST = 0;                                   // 2 histograms (low addresses: offsets fold into ds_add)
 constexpr int L_MISC = L_HIST + 2 * HIST_WORDS * 4;         // 64 u32 scratch
-constexpr int L_CO = L_MISC + 64 * 4;                       // per chunk: candidate count (u8, 4 NT)
-constexpr int L_GRP = L_CO + 4 * NT;                        // per group of 8 chunks: count, then base (2 x 256 u32)
-constexpr int L_FIN_END = L_GRP + 2 * 256 * 4;
+constexpr int L_CAND = L_MISC + 64 * 4;                     // FIN_ENT u64 candidates + 64 dummies (or ALL_MAX u32 keys)
+constexpr int L_BM = L_CAND + (FIN_ENT + 64) * 8;           // bitmap: BITMAP_KEYS / 32 words
+constexpr int L_FIN_END = L_BM + BITMAP_KEYS / 8;
 static_assert(BITMAP_KEYS / 8 >= 4 * NT * 8, "the failing-chunk list (2 words a chunk) fits the bitmap");
-static_assert(ALL_MAX % NT == 0 && FIN_ENT % NT == 0, "register segments");
-static_assert(CAP_MAX <= 128, "a chunk's candidates are gathered in at most two 64-slot groups");
+static_assert(ALL_MAX % (4 * NT) == 0 && FIN_ENT % (4 * NT) == 0, "register segments of whole slot groups");
+static_assert(ALL_MAX * 4 <= FIN_ENT * 8, "all-keys rows fit the candidate area");
+static_assert(L_CAND % 16 == 0, "16-byte candidate reads");
+static_assert(CAP_MAX == 128, "a chunk's header and candidates are gathered in at most two 64-slot groups");
 static_assert(L_SCORE_END <= 160 * 1024 && L_FIN_END <= 160 * 1024, "LDS budget");
 
 // workspace header (bytes)
@@ -107,16 +104,17 @@ struct KArgs {
   int32_t chunk;            // keys per workgroup chunk (P * 64)
   int32_t chunk_shift;      // log2(chunk)
   int32_t mode;
-  int32_t meta_stride;      // chunk slots per row (>= chunks of the longest row)
-  int32_t ent_stride;       // chunk slots per row of the candidate area (min(meta_stride, 4 NT))
-  uint64_t off_meta, off_ent;
+  int32_t ent_stride;       // candidate blocks per row (>= chunks of a row that selects from candidates)
+  uint64_t off_ent;
   uint32_t grp[IDX_MAX_REQ];// row0 | nrows << 24
   int32_t gmax[IDX_MAX_REQ];// host bound on the keys of each group's rows
 };
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
@@ -161,6 +159,18 @@ __device__ inline uint32_t radix_key(float f) {
 __device__ inline int lane_id() { return (int)(threadIdx.x & 63); }
 // the wave's index in the workgroup, as a wave-uniform (scalar) value
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Makes the given wave-uniform values live in scalar registers at this point: a kernel
+// calls it on its arguments first, so that their loads go out together instead of one
+// round trip behind each branch that first needs them.
+template <typename T>
+__device__ __forceinline__ void scalar_ready(const T& v) {
+  asm volatile("" ::"s"(v));
+}
+template <typename... T>
+__device__ __forceinline__ void scalars_ready(const T&... v) {
+  (scalar_ready(v), ...);
+}
 
 // max(x, 0) of a float as one integer max of its bits: every negative float (and -0)
 // is a negative int32, every positive float a positive one
@@ -316,84 +326,196 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, int 
 
 // ---------------------------------------------------------------------------
 // Exact top-k threshold of the keys held in registers across the workgroup: thread t
-// holds kr[0 .. S) (slots past S hold 0); a zero key is absent.  Radix select over the
-// bits below the common prefix of the smallest and largest key, in digits of up to 12
-// bits from the top, histograms in LDS (hist: 2 x HIST_WORDS words).  Returns false
-// if fewer than k keys are present.  Otherwise the top k (score descending, then
-// position) are exactly: every key >= *Tge, and, when *rem > 0, also the first *rem
-// keys equal to *T = *Tge - 1 in position order.  Absent keys never match a prefix
-// once the first digit is fixed, and in the first pass they fall into bin 0, below
-// every present key (a present key is >= 2^23 and the first digit starts at bit 21 or
-// lower), so they are neither counted nor selected.  Slots are visited in groups of
-// 8, skipping whole groups past S.  Every thread must call.
+// holds kr[0 .. S) (S a multiple of 4); a zero key is absent, cnt keys are present and
+// all of them lie in [lo, hi].  Both histogram buffers (hist: 2 x HIST_WORDS words) must
+// be clear on entry and are left dirty.  Returns false if cnt < k.  Otherwise the top k
+// (score descending, then position) are exactly: every key >= *Tge, and, when *rem > 0,
+// also the first *rem keys equal to Tge - 1 in position order.
+//
+// First pass: a histogram of 4096 bins linear in the score over [lo, hi], bin(key) =
+// floor(score * s - lo_score * s) with s = 4096 / (hi_score - lo_score), the product and
+// difference rounded once (an fma), clamped to [0, 4095].  A once-rounded function of a
+// real that is monotone in the score is monotone, so every key of a higher bin is larger
+// than every key of a lower one, and the bin d holding the k-th largest key leaves r =
+// (k minus the keys above d) to choose inside it.  Scores of one row cluster far below
+// the f32 exponent scale, so a bin this fine holds a few keys: they are listed and wave
+// 0 finds the r-th largest exactly.  A bin of more than 64 keys (ties, or a degenerate
+// spread) falls back to radix passes over the keys in [min, max] of that bin, in digits
+// of up to 12 bits below the common prefix.  Absent keys and keys outside the range in
+// play go to per-lane dummy words.  Every thread must call.
 // ---------------------------------------------------------------------------
-template <int SMAX>
-__device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, int k, uint32_t* hist, int* misc,
-                                         uint32_t* Tge_out, int* rem_out) {
-  static_assert(SMAX % 8 == 0, "slot groups of 8");
-  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u, cnt = 0;
-#pragma unroll
-  for (int g = 0; g < SMAX / 8; g++) {
-    if (g * 8 >= S) break;
-#pragma unroll
-    for (int jj = 0; jj < 8; jj++) {
-      const uint32_t key = kr[g * 8 + jj];
-      mn = min(mn, key - 1u);                         // absent keys wrap to 0xFFFFFFFF
-      mx = max(mx, key);
-      cnt += key != 0u ? 1u : 0u;
-    }
-  }
-  mn = wave_min_u32(mn);                              // still key - 1 (absent: 0xFFFFFFFF)
+// the f32 score a key encodes (the inverse of radix_key for keys of finite scores)
+__device__ __forceinline__ float key_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// min and max over the workgroup.  Every thread must call.
+__device__ __forceinline__ void block_min_max(uint32_t& mn, uint32_t& mx, int* misc) {
+  const int lane = lane_id(), wv = wave_id();
+  mn = wave_min_u32(mn);
   mx = wave_max_u32(mx);
-  cnt = wave_sum_u32(cnt);
   uint32_t* red = reinterpret_cast<uint32_t*>(misc) + 16;
   if (lane == 0) {
     red[wv] = mn;
     red[NWAVE + wv] = mx;
-    red[2 * NWAVE + wv] = cnt;
-  }
-  {
-    const v4i z = {0, 0, 0, 0};
-    v4i* h4 = reinterpret_cast<v4i*>(hist);
-    h4[tid] = z;                                        // bins of the first buffer
-    h4[tid + NT] = z;
   }
   __syncthreads();
-  cnt = 0;
 #pragma unroll
   for (int i = 0; i < NWAVE; i++) {
     mn = min(mn, red[i]);
     mx = max(mx, red[NWAVE + i]);
-    cnt += red[2 * NWAVE + i];
   }
-  if ((int)cnt < k) return false;
-  mn += 1u;                                           // the smallest present key
-  if (mn == mx) {  // every key equal: the first k of them (all of them when cnt == k)
-    *Tge_out = (int)cnt == k ? mn : mn + 1u;
-    *rem_out = (int)cnt == k ? 0 : k;
+  __syncthreads();
+}
+
+// zero the 4096 bins of both histogram buffers (no barrier)
+__device__ __forceinline__ void clear_hist(uint32_t* hist) {
+  const v4i z = {0, 0, 0, 0};
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int b = 0; b < 2; b++) {
+    v4i* h4 = reinterpret_cast<v4i*>(hist + b * HIST_WORDS);
+    h4[t] = z;
+    h4[t + NT] = z;
+  }
+}
+
+template <int SMAX>
+__device__ __forceinline__ bool kth_select(const uint32_t (&kr)[SMAX], int S, int cnt, uint32_t lo, uint32_t hi,
+                                           int k, uint32_t* hist, int* misc, uint32_t* Tge_out, int* rem_out) {
+  static_assert(SMAX % 4 == 0, "slot groups of 4");
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  if (cnt < k) return false;
+  if (lo == hi) {  // every key equal: the first k of them (all of them when cnt == k)
+    *Tge_out = cnt == k ? lo : lo + 1u;
+    *rem_out = cnt == k ? 0 : k;
     return true;
   }
-  const int top = 31 - __clz(mn ^ mx);               // highest bit that differs
+  const uint32_t dummy = 4096u + (uint32_t)lane;
+  uint32_t klo = lo, khi = hi;                        // keys in play: [klo, khi]
+  int rem = k, buf = 0;
+
+  // ---- linear pass
+  const float fmin = key_float(lo);
+  const float span = key_float(hi) - fmin;
+  const float scale = 4096.0f / span;
+  if (span <= 3.0e38f && scale <= 3.0e38f) {          // both finite (false for inf, NaN)
+    const float off = -fmin * scale;
+    uint32_t idx[SMAX];
+    if (tid == 0) misc[11] = 0;                       // list counter
+#pragma unroll
+    for (int g = 0; g < SMAX / 4; g++) {
+      if (g * 4 < S) {
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          const int j = g * 4 + jj;
+          const uint32_t key = kr[j];
+          const uint32_t b = min(__float2uint_rz(fmaf(key_float(max(key, lo)), scale, off)), 4095u);
+          idx[j] = key != 0u ? b : dummy;
+          atomicAdd(&hist[idx[j]], 1u);
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) idx[g * 4 + jj] = dummy;
+      }
+    }
+    __syncthreads();
+    find_digit(hist, 4096, rem, misc);
+    const uint32_t d = (uint32_t)misc[8];
+    const int r = misc[9];
+    const int c = misc[10];
+    if (c <= 64) {
+      // the c keys of bin d into a list (the dummy words of the second buffer), then the
+      // r-th largest of them on wave 0
+      uint32_t* lst = hist + HIST_WORDS + 4096;
+#pragma unroll
+      for (int g = 0; g < SMAX / 4; g++) {
+        if (g * 4 >= S) break;
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++)
+          if (idx[g * 4 + jj] == d) lst[atomicAdd(&misc[11], 1)] = kr[g * 4 + jj];
+      }
+      __syncthreads();
+      if (wv == 0) {
+        // the r-th largest listed key: the x with #{> x} < r <= #{>= x} (lanes past c
+        // hold 0, below every key)
+        const uint32_t v = lane < c ? lst[lane] : 0u;
+        uint32_t T = 0u;
+        int gt = 0, eq = 0;
+        for (int i2 = 0; i2 < c; i2++) {
+          const uint32_t x = (uint32_t)__builtin_amdgcn_readlane((int)v, i2);
+          const int g2 = (int)__popcll(__ballot(v > x));
+          const int e2 = (int)__popcll(__ballot(v == x));
+          if (g2 < r && r <= g2 + e2) {
+            T = x;
+            gt = g2;
+            eq = e2;
+            break;
+          }
+        }
+        if (lane == 0) {
+          // keys above T are all selected; r - gt of the eq keys equal to T
+          misc[12] = (int)(r - gt == eq ? T : T + 1u);
+          misc[13] = r - gt == eq ? 0 : r - gt;
+        }
+      }
+      __syncthreads();
+      *Tge_out = (uint32_t)misc[12];
+      *rem_out = misc[13];
+      return true;
+    }
+    // a crowded bin: its key range, then radix passes over it
+    uint32_t bmn = 0xFFFFFFFFu, bmx = 0u;
+#pragma unroll
+    for (int g = 0; g < SMAX / 4; g++) {
+      if (g * 4 >= S) break;
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const bool in = idx[g * 4 + jj] == d;
+        const uint32_t key = kr[g * 4 + jj];
+        bmn = min(bmn, in ? key : 0xFFFFFFFFu);
+        bmx = max(bmx, in ? key : 0u);
+      }
+    }
+    block_min_max(bmn, bmx, misc);
+    klo = bmn;
+    khi = bmx;
+    rem = r;
+    if (r == c) {                                     // all of bin d
+      *Tge_out = klo;
+      *rem_out = 0;
+      return true;
+    }
+    if (klo == khi) {                                 // r of the c equal keys of bin d
+      *Tge_out = klo + 1u;
+      *rem_out = r;
+      return true;
+    }
+    buf = 1;                                          // still clear
+  }
+
+  // ---- radix passes over the keys in [klo, khi]
+  const int top = 31 - __clz(klo ^ khi);             // highest bit that differs
   uint32_t mask = (top == 31) ? 0u : ~((2u << top) - 1u);
-  uint32_t prefix = mn & mask;
+  uint32_t prefix = klo & mask;
+  const uint32_t span_k = khi - klo;
   const int nb = top + 1;                             // bits left to resolve
   const int npass = (nb + 11) / 12;
   const int wdef = (nb + npass - 1) / npass;
-  int rem = k, shift = nb, buf = 0;
-  const uint32_t dummy = 4096u + (uint32_t)lane;
+  int shift = nb;
   while (true) {
     const int width = wdef < shift ? wdef : shift;
     shift -= width;
     uint32_t* h = hist + buf * HIST_WORDS;
 #pragma unroll
-    for (int g = 0; g < SMAX / 8; g++) {
-      if (g * 8 >= S) break;
+    for (int g = 0; g < SMAX / 4; g++) {
+      if (g * 4 >= S) break;
 #pragma unroll
-      for (int jj = 0; jj < 8; jj++) {
-        const uint32_t key = kr[g * 8 + jj];
+      for (int jj = 0; jj < 4; jj++) {
+        const uint32_t key = kr[g * 4 + jj];
         const uint32_t dg = __builtin_amdgcn_ubfe(key, (uint32_t)shift, (uint32_t)width);
-        atomicAdd(&h[((key & mask) == prefix) ? dg : dummy], 1u);
+        const bool in = key - klo <= span_k && (key & mask) == prefix;   // absent keys wrap out
+        atomicAdd(&h[in ? dg : dummy], 1u);
       }
     }
     {
@@ -411,9 +533,10 @@ __device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, int 
     const uint32_t dmask = (1u << width) - 1u;
     prefix |= d << shift;
     mask |= dmask << shift;
-    if (c == r && (shift == 0 || prefix != 0u)) {
+    if (c == r) {
       // every key of this digit is selected: the top k are exactly the keys >= prefix
-      *Tge_out = prefix;
+      // (and >= klo: keys below klo belong to lower bins)
+      *Tge_out = max(prefix, klo);
       *rem_out = 0;
       return true;
     }
@@ -431,64 +554,78 @@ __device__ __forceinline__ bool kth_regs(const uint32_t (&kr)[SMAX], int S, int 
 // Emission of the top k in segment order (thread t's slots j < S precede thread t + 1's;
 // the caller lays positions out ascending in that order; absent slots hold key 0): a
 // key is selected when key >= Tge, or, when rem > 0, key == Tge - 1 and it is among
-// the first rem such keys.  out[0 .. k) receives the selected positions pr[j] (stores
-// of unselected slots go outside the buffer resource and are dropped).  Returns the
-// number selected.  Every thread must call.
+// the first rem such keys.  The selected positions pr[j] are staged in LDS (stage:
+// k words, free for this use) and copied to out[0 .. k) with coalesced stores.  Returns
+// the number selected.  Every thread must call.
 template <int SMAX>
 __device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], const uint32_t (&pr)[SMAX], int S,
-                                             uint32_t Tge, int rem, int32_t* out, int k, int* misc) {
-  constexpr int OOB = 0x7FFFFFF0;
+                                             uint32_t Tge, int rem, int32_t* out, int k, int* misc,
+                                             uint32_t* stage) {
   const uint32_t T = Tge - 1u;
   int gt = 0, eq = 0;
 #pragma unroll
-  for (int g = 0; g < SMAX / 8; g++) {
-    if (g * 8 >= S) break;
+  for (int g = 0; g < SMAX / 4; g++) {
+    if (g * 4 >= S) break;
 #pragma unroll
-    for (int jj = 0; jj < 8; jj++) gt += kr[g * 8 + jj] >= Tge ? 1 : 0;
+    for (int jj = 0; jj < 4; jj++) gt += kr[g * 4 + jj] >= Tge ? 1 : 0;
   }
   if (rem > 0) {
 #pragma unroll
-    for (int g = 0; g < SMAX / 8; g++) {
-      if (g * 8 >= S) break;
+    for (int g = 0; g < SMAX / 4; g++) {
+      if (g * 4 >= S) break;
 #pragma unroll
-      for (int jj = 0; jj < 8; jj++) eq += kr[g * 8 + jj] == T ? 1 : 0;
+      for (int jj = 0; jj < 4; jj++) eq += kr[g * 4 + jj] == T ? 1 : 0;
     }
   }
   int tot;
   const int packed = block_excl_scan(gt | (eq << 16), misc, &tot);
   const int before_gt = packed & 0xFFFF, before_eq = packed >> 16;
-  __amdgpu_buffer_rsrc_t ro = make_rsrc(out, (int64_t)k * 4);
   if (rem == 0) {
-    int o4 = before_gt * 4;
+    int o = before_gt;
 #pragma unroll
-    for (int g = 0; g < SMAX / 8; g++) {
-      if (g * 8 >= S) break;
+    for (int g = 0; g < SMAX / 4; g++) {
+      if (g * 4 >= S) break;
 #pragma unroll
-      for (int jj = 0; jj < 8; jj++) {
-        const bool sel = kr[g * 8 + jj] >= Tge;
-        __builtin_amdgcn_raw_buffer_store_b32(pr[g * 8 + jj], ro, sel ? o4 : OOB, 0, 0);
-        o4 += sel ? 4 : 0;
+      for (int jj = 0; jj < 4; jj++) {
+        const bool sel = kr[g * 4 + jj] >= Tge;
+        if (sel && o < k) stage[o] = pr[g * 4 + jj];
+        o += sel ? 1 : 0;
       }
     }
   } else {
     int o = before_gt + (before_eq < rem ? before_eq : rem);
     int er = before_eq;
 #pragma unroll
-    for (int g = 0; g < SMAX / 8; g++) {
-      if (g * 8 >= S) break;
+    for (int g = 0; g < SMAX / 4; g++) {
+      if (g * 4 >= S) break;
 #pragma unroll
-      for (int jj = 0; jj < 8; jj++) {
-        const uint32_t key = kr[g * 8 + jj];
+      for (int jj = 0; jj < 4; jj++) {
+        const uint32_t key = kr[g * 4 + jj];
         const bool e = key == T;
         const bool sel = key >= Tge || (e && er < rem);
         er += e ? 1 : 0;
-        __builtin_amdgcn_raw_buffer_store_b32(pr[g * 8 + jj], ro, (sel && o < k) ? o * 4 : OOB, 0, 0);
+        if (sel && o < k) stage[o] = pr[g * 4 + jj];
         o += sel ? 1 : 0;
       }
     }
   }
+  __syncthreads();
   const int tg = tot & 0xFFFF, te = tot >> 16;
-  return tg + (te < rem ? te : rem);
+  const int got = tg + (te < rem ? te : rem);
+  const int ne = got < k ? got : k;
+  if ((reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+    for (int q = threadIdx.x; 4 * q < ne; q += NT) {
+      if (4 * q + 4 <= ne) {
+        *reinterpret_cast<v4u*>(out + 4 * q) = *reinterpret_cast<const v4u*>(stage + 4 * q);
+      } else {
+        for (int j = 0; j < 4; j++)
+          if (4 * q + j < ne) out[4 * q + j] = (int32_t)stage[4 * q + j];
+      }
+    }
+  } else {
+    for (int p = threadIdx.x; p < ne; p += NT) out[p] = (int32_t)stage[p];
+  }
+  return got;
 }
 
 // Position of the rem-th set bit of bm[0 .. words) (1-based rem).  Every thread must call.
@@ -543,26 +680,31 @@ __device__ int emit_bitmap(const uint32_t* bm, int words, int* misc, int32_t* ou
   return tot;
 }
 
-// Top k of the candidate set (K, P)[0 .. E) over positions [0, n), given the threshold
-// (T, rem) of kth_regs, through a position bitmap (the candidates need not be in
-// position order).  Returns the number emitted.  Every thread must call.
-__device__ int select_explicit(const uint32_t* K, const uint32_t* P, int E, int n, int k, uint32_t T, int rem,
-                               uint32_t* bm, int* misc, int32_t* out) {
+// Top k of the candidates cand[0 .. E) (key << 32 | position) over positions [0, n),
+// given a threshold from kth_select (keys > T, and the first rem keys equal to T in
+// position order), through a position bitmap (the candidates need not be in position
+// order).  Returns the number emitted.  Every thread must call.
+__device__ int select_explicit(const uint64_t* cand, int E, int n, int k, uint32_t T, int rem, uint32_t* bm,
+                               int* misc, int32_t* out) {
   const int tid = threadIdx.x;
   const int words = (n + 31) >> 5;
   for (int i = tid; i < words; i += NT) bm[i] = 0;
   __syncthreads();
   int pos_cut = -1;                                   // keys equal to T at positions <= pos_cut
   if (rem > 0) {
-    for (int e = tid; e < E; e += NT)
-      if (K[e] == T) atomicOr(&bm[P[e] >> 5], 1u << (P[e] & 31));
+    for (int e = tid; e < E; e += NT) {
+      const uint64_t c = cand[e];
+      const uint32_t p = (uint32_t)c;
+      if ((uint32_t)(c >> 32) == T) atomicOr(&bm[p >> 5], 1u << (p & 31));
+    }
     __syncthreads();
     pos_cut = (int)nth_set_bit(bm, words, rem, misc);
     for (int i = tid; i < words; i += NT) bm[i] = 0;
     __syncthreads();
   }
   for (int e = tid; e < E; e += NT) {
-    const uint32_t key = K[e], p = P[e];
+    const uint64_t c = cand[e];
+    const uint32_t key = (uint32_t)(c >> 32), p = (uint32_t)c;
     if (key > T || (key == T && (int)p <= pos_cut)) atomicOr(&bm[p >> 5], 1u << (p & 31));
   }
   __syncthreads();
@@ -647,7 +789,7 @@ __device__ inline void candidate_params(int n, int C, int k, int* m, int* cap) {
   mm = mm > 64 ? 64 : mm;
   int cc = 2 * mm + 16;
   cc = cc > C ? C : cc;
-  cc = cc > CAP_MAX ? CAP_MAX : cc;
+  cc = cc > CAP_MAX - 2 ? CAP_MAX - 2 : cc;          // slots 0 and 1 hold the header and the maximum
   *m = mm;
   *cap = cc;
 }
@@ -674,6 +816,8 @@ __device__ inline void wait_pages_through(int x, int issued) {
     case 6: wait_vmcnt<6>(); break;
     case 8: wait_vmcnt<8>(); break;
     case 10: wait_vmcnt<10>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 14: wait_vmcnt<14>(); break;
     default: wait_vmcnt<0>(); break;
   }
 }
@@ -839,154 +983,206 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, int* misc) {
   return (uint32_t)(a[0] + a[1] + a[2] + a[3] + b[0] + b[1] + b[2] + b[3]);
 }
 
-// t[0] and t[2] summed, t[1] maxed over the workgroup.  Every thread must call.
-__device__ __forceinline__ void block_sum_max_sum(uint32_t (&t)[3], int* misc) {
-  const uint32_t a = wave_sum_u32(t[0]), b = wave_max_u32(t[1]), c = wave_sum_u32(t[2]);
+// t[0] and t[3] summed, t[1] and t[2] maxed over the workgroup.  Every thread must call.
+__device__ __forceinline__ void block_sum_max_max_sum(uint32_t (&t)[4], int* misc) {
+  const uint32_t a = wave_sum_u32(t[0]), b = wave_max_u32(t[1]), c = wave_max_u32(t[2]), d = wave_sum_u32(t[3]);
   const int wv = wave_id();
   if (lane_id() == 0) {
     misc[wv] = (int)a;
     misc[NWAVE + wv] = (int)b;
     misc[2 * NWAVE + wv] = (int)c;
+    misc[3 * NWAVE + wv] = (int)d;
   }
   __syncthreads();
-  uint32_t sa = 0, mb = 0, sc = 0;
+  uint32_t sa = 0, mb = 0, mc = 0, sd = 0;
 #pragma unroll
   for (int i = 0; i < NWAVE; i++) {
     sa += (uint32_t)misc[i];
     mb = max(mb, (uint32_t)misc[NWAVE + i]);
-    sc += (uint32_t)misc[2 * NWAVE + i];
+    mc = max(mc, (uint32_t)misc[2 * NWAVE + i]);
+    sd += (uint32_t)misc[3 * NWAVE + i];
   }
   __syncthreads();
   t[0] = sa;
   t[1] = mb;
-  t[2] = sc;
+  t[2] = mc;
+  t[3] = sd;
 }
 
-// The row's published candidates into LDS in position order: FK[e] = key, FP[e] =
-// position for e < E.  Chunk w's candidates sit at erow[w * CAP_MAX + s] for s < its
-// count cnt8[w] <= 64 SLOTS.  Chunks come in groups of 8: group g starts at position-
-// ordered offset gbase[g], so candidate s of chunk w goes to slot gbase[w / 8] + (counts
-// of the chunks before w in its group) + s, known before anything is loaded.  In batch
-// b wave v takes the GPB groups b NWAVE GPB + v GPB + j (j < GPB), issuing one 64-slot
-// load per lane and chunk for all of them before the first use; slots past a count
-// point outside the buffer resource (no traffic, zero result) and write into the last
-// 64 LDS slots, which E <= FIN_ENT - 64 leaves free.  No barrier inside.
-template <int SLOTS>
-__device__ __forceinline__ void gather_candidates(const uint64_t* erow, int wact, const uint8_t* cnt8,
-                                                  const uint32_t* gbase, uint32_t* FK, uint32_t* FP) {
+// Candidate blocks: chunk w of a row owns CAP_MAX 8-byte slots, of which the first
+// 64 G are written by every call (G = block_groups(cap)).  Slot 0 is the header t_w |
+// (overflow << 16 | count) << 32, slot 1 the chunk's largest key, slots 2 .. count + 1
+// the candidates as key << 32 | position, ascending in position, and the rest of the 64 G
+// slots zero.  The upper word of a header, a maximum or a zero slot is below any key,
+// so "upper word >= t*" alone picks the candidates that count.
+__host__ __device__ inline int block_groups(int cap) { return (2 + cap + 63) >> 6; }
+
+// One batch of the gather: wave v reads, with 16-byte loads, the 64 G slots of the
+// chunks w0 .. w0 + 32 / G (w0 = b0 + v 32 / G): load q of lane l covers slots
+// 2 (l & 31), + 1 of chunk w0 + 2 q + (l >> 5) (G = 1), or slots 64 (l >> 5) + 2 (l & 31),
+// + 1 of chunk w0 + q (G = 2).  All loads are issued before any is used; chunks at or
+// past wact point outside the buffer resource (no traffic, zero result).
+template <int G>
+__device__ __forceinline__ void gather_issue(__amdgpu_buffer_rsrc_t rent, int wact, int b0, uint64_t (&e)[32]) {
   constexpr int OOB = 0x7FFFFFF0;
-  constexpr int GPB = 4 / SLOTS;                        // groups a wave and batch
-  constexpr int L = GPB * 8 * SLOTS;                    // loads a lane and batch (32)
-  const int lane = lane_id(), wv = wave_id();
-  __amdgpu_buffer_rsrc_t rent = make_rsrc(erow, (int64_t)wact * CAP_MAX * 8);
-  const int groups = (wact + 7) / 8;
-  const int dummy = FIN_ENT - 64 + lane;
-#pragma unroll 1
-  for (int gb = wv * GPB; gb < groups; gb += NWAVE * GPB) {
-    int off[L], at[L];
+  const int lane = lane_id();
+  const int w0 = b0 + wave_id() * (32 / G);
+  const int h = lane >> 5, l2 = 2 * (lane & 31);
 #pragma unroll
-    for (int j = 0; j < GPB; j++) {
-      const int g = gb + j;
-      const int w0 = g * 8;
-      // group g's 8 chunk counts (one byte a chunk; bytes past wact are 0) and its base,
-      // as wave-uniform values
-      const bool live = g < groups;
-      const v2i_t cq = live ? *reinterpret_cast<const v2i_t*>(cnt8 + w0) : v2i_t{0, 0};
-      const uint32_t c0 = (uint32_t)__builtin_amdgcn_readfirstlane(cq[0]);
-      const uint32_t c1 = (uint32_t)__builtin_amdgcn_readfirstlane(cq[1]);
-      int base = live ? __builtin_amdgcn_readfirstlane((int)gbase[g]) : 0;
-#pragma unroll
-      for (int q = 0; q < 8; q++) {
-        const int cu = (int)(((q < 4 ? c0 : c1) >> ((q & 3) * 8)) & 0xFFu);
-#pragma unroll
-        for (int s2 = 0; s2 < SLOTS; s2++) {
-          const int sl = s2 * 64 + lane;
-          const bool v = sl < cu;
-          off[(j * 8 + q) * SLOTS + s2] = v ? ((w0 + q) * CAP_MAX + sl) * 8 : OOB;
-          at[(j * 8 + q) * SLOTS + s2] = v ? base + sl : dummy;
-        }
-        base += cu;
-      }
-    }
-    uint64_t e[L];
-#pragma unroll
-    for (int i = 0; i < L; i++)
-      e[i] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rent, off[i], 0, 0));
-#pragma unroll
-    for (int i = 0; i < L; i++) {
-      FK[at[i]] = (uint32_t)(e[i] >> 32);
-      FP[at[i]] = (uint32_t)e[i];
-    }
+  for (int q = 0; q < 16; q++) {
+    const int w = G == 1 ? w0 + 2 * q + h : w0 + q;
+    const int slot = G == 1 ? l2 : 64 * h + l2;
+    const int off = w < wact ? (w * CAP_MAX + slot) * 8 : OOB;
+    const v4u x = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rent, off, 0, 0));
+    e[2 * q] = ((uint64_t)x[1] << 32) | x[0];
+    e[2 * q + 1] = ((uint64_t)x[3] << 32) | x[2];
   }
 }
 
-// Top k of the E candidates FK[0 .. E) (with positions FP[e], or e itself when
-// IMPLICIT), laid out in position order; candidates below lo do not count.  Thread t
-// holds candidates [t S, t S + S), S odd so that the strided LDS reads are free of
-// bank conflicts.  Returns false (writing nothing) when fewer than k candidates count.
-// Every thread must call.
-template <int SMAX, bool IMPLICIT>
-__device__ __forceinline__ bool select_emit(const uint32_t* FK, const uint32_t* FP, int E, uint32_t lo, int k,
-                                            uint32_t* hist, int* misc, int32_t* out, int* got) {
-  const int S = ((E + NT - 1) / NT) | 1;
-  const int e0 = threadIdx.x * S;
+// The candidates of a loaded batch with key >= lo into cand[E0 ...], in position order
+// (within a load the lanes run in slot and chunk order, two slots a lane): a ballot per
+// load and slot parity ranks the kept slots within the wave, the wave totals place the
+// waves.  Dropped slots write to the 64 dummy entries past FIN_ENT.  Returns the
+// batch's kept count.  Every thread must call.
+__device__ __forceinline__ int gather_place(const uint64_t (&e)[32], uint32_t lo, int E0, uint64_t* cand, int* misc) {
+  const int lane = lane_id(), wv = wave_id();
+  int o = 0;
+  int r0[16], r1[16];
+#pragma unroll
+  for (int q = 0; q < 16; q++) {
+    const bool k0 = (uint32_t)(e[2 * q] >> 32) >= lo;
+    const bool k1 = (uint32_t)(e[2 * q + 1] >> 32) >= lo;
+    const uint64_t m0 = __ballot(k0), m1 = __ballot(k1);
+    const int before = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m0, 0u)) +
+                       (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m1, 0u));
+    r0[q] = k0 ? o + before : -1;
+    r1[q] = k1 ? o + before + (k0 ? 1 : 0) : -1;
+    o += (int)__popcll(m0) + (int)__popcll(m1);
+  }
+  if (lane == 0) misc[wv] = o;
+  __syncthreads();
+  const v4i ta = reinterpret_cast<const v4i*>(misc)[0];
+  const v4i tb = reinterpret_cast<const v4i*>(misc)[1];
+  const int t[8] = {ta[0], ta[1], ta[2], ta[3], tb[0], tb[1], tb[2], tb[3]};
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; i++) {
+    before += (i < wv) ? t[i] : 0;
+    tot += t[i];
+  }
+  __syncthreads();
+  const int base = E0 + before;
+  const int dummy = FIN_ENT + lane;
+#pragma unroll
+  for (int q = 0; q < 16; q++) {
+    cand[r0[q] >= 0 ? base + r0[q] : dummy] = e[2 * q];
+    cand[r1[q] >= 0 ? base + r1[q] : dummy] = e[2 * q + 1];
+  }
+  return tot;
+}
+
+// slots a thread holds for E entries: a multiple of 4
+__device__ __forceinline__ int slots_for(int E) { return ((E + NT - 1) / NT + 3) & ~3; }
+
+// zero cand[E .. NT S) (S = slots_for(E)); no barrier
+__device__ __forceinline__ void pad_cand(uint64_t* cand, int E) {
+  const int end = NT * slots_for(E);
+  for (int e = E + (int)threadIdx.x; e < end; e += NT) cand[e] = 0ull;
+}
+
+// Top k of the E candidates cand[0 .. E) (in position order, keys within [lo, hi], zero
+// up to NT slots_for(E)).  Thread t holds candidates [t S, t S + S); the candidate area
+// stages the output once they are in registers.  Both histogram buffers must be clear.
+// Returns false (writing nothing) when fewer than k are present.  Every thread must call.
+template <int SMAX>
+__device__ __forceinline__ bool select_cand(uint64_t* cand, int E, uint32_t lo, uint32_t hi, int k, uint32_t* hist,
+                                            int* misc, int32_t* out, int* got) {
+  const int S = slots_for(E);
+  const v4u* src = reinterpret_cast<const v4u*>(cand + threadIdx.x * S);
   uint32_t kr[SMAX], pr[SMAX];
 #pragma unroll
-  for (int j = 0; j < SMAX; j++) {
-    kr[j] = 0u;
-    pr[j] = 0u;
-  }
+  for (int g = 0; g < SMAX / 4; g++) {
+    if (g * 4 < S) {
+      const v4u x = src[2 * g], y = src[2 * g + 1];
+      pr[g * 4 + 0] = x[0]; kr[g * 4 + 0] = x[1];
+      pr[g * 4 + 1] = x[2]; kr[g * 4 + 1] = x[3];
+      pr[g * 4 + 2] = y[0]; kr[g * 4 + 2] = y[1];
+      pr[g * 4 + 3] = y[2]; kr[g * 4 + 3] = y[3];
+    } else {
 #pragma unroll
-  for (int g = 0; g < SMAX / 8; g++) {
-    if (g * 8 >= S) break;
-#pragma unroll
-    for (int jj = 0; jj < 8; jj++) {
-      const int j = g * 8 + jj, e = e0 + j;
-      const bool v = j < S && e < E;
-      const uint32_t key = v ? FK[e] : 0u;
-      kr[j] = key >= lo ? key : 0u;
-      pr[j] = IMPLICIT ? (uint32_t)e : (v ? FP[e] : 0u);
+      for (int jj = 0; jj < 4; jj++) { kr[g * 4 + jj] = 0u; pr[g * 4 + jj] = 0u; }
     }
   }
   uint32_t Tge;
   int rem;
-  if (!kth_regs<SMAX>(kr, S, k, hist, misc, &Tge, &rem)) return false;
-  *got = emit_segments<SMAX>(kr, pr, S, Tge, rem, out, k, misc);
+  if (!kth_select<SMAX>(kr, S, E, lo, hi, k, hist, misc, &Tge, &rem)) return false;
+  *got = emit_segments<SMAX>(kr, pr, S, Tge, rem, out, k, misc, reinterpret_cast<uint32_t*>(cand));
   return true;
 }
 
-// Candidate path when the certificate fails.  T0 = the k-th candidate (if there are
-// k); every chunk whose local threshold t_w (tw[w], 0xFFFFFFFF when it published
-// nothing) is above T0 is re-read from the row's scores for its unpublished keys >= T0,
-// after which every key >= T0 of the row is a candidate, and the top k is taken from
-// that set through a position bitmap.  Returns true when it selected, false to fall
-// back to the multi-pass select over memory.  Every thread must call.
-__device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact, int E, int C,
-                                            __amdgpu_buffer_rsrc_t rs, uint32_t* FK, uint32_t* FP, uint32_t* bm,
+// Top k of all n keys of a row held at their positions (fk[p], zero up to NT
+// slots_for(n)), keys within [lo, hi].  As select_cand otherwise.
+template <int SMAX>
+__device__ __forceinline__ bool select_all(uint32_t* fk, int n, uint32_t lo, uint32_t hi, int k, uint32_t* hist,
+                                           int* misc, int32_t* out, int* got) {
+  const int S = slots_for(n);
+  const int e0 = threadIdx.x * S;
+  const v4u* src = reinterpret_cast<const v4u*>(fk + e0);
+  uint32_t kr[SMAX], pr[SMAX];
+#pragma unroll
+  for (int g = 0; g < SMAX / 4; g++) {
+    const v4u x = g * 4 < S ? src[g] : v4u{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+      kr[g * 4 + jj] = x[jj];
+      pr[g * 4 + jj] = (uint32_t)(e0 + g * 4 + jj);
+    }
+  }
+  uint32_t Tge;
+  int rem;
+  if (!kth_select<SMAX>(kr, S, n, lo, hi, k, hist, misc, &Tge, &rem)) return false;
+  *got = emit_segments<SMAX>(kr, pr, S, Tge, rem, out, k, misc, fk);
+  return true;
+}
+
+// Candidate path when the certificate fails.  cand[0 .. E) holds every key >= lo of the
+// chunks that did not overflow (bm[w] = 0xFFFFFFFF marks an overflowed chunk, which
+// holds none); every key of the row is <= hi.  T0 = the k-th candidate (if there are
+// k); every chunk whose held range does not reach down to T0 (an overflowed chunk, or lo
+// > T0) is re-read from the row's scores for its keys >= T0 that are not held, after
+// which every key >= T0 of the row is a candidate, and the top k is taken from that set
+// through a position bitmap.  Returns true when it selected, false to fall back to the
+// multi-pass select over memory.  Every thread must call.
+__device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact, int E, int C, uint32_t lo,
+                                            uint32_t hi, __amdgpu_buffer_rsrc_t rs, uint64_t* cand, uint32_t* bm,
                                             uint32_t* hist, int* misc, int32_t* out) {
   const int tid = threadIdx.x;
-  constexpr int SR = 32;
+  constexpr int SR = FIN_ENT / NT;
   uint32_t kr[SR];
   auto load_keys = [&](int n_ent) {
-    int S = (n_ent + NT - 1) / NT;
-    S |= 1;
-    const int e0 = tid * S;
+    const int S = slots_for(n_ent);
+    const uint64_t* src = cand + tid * S;
 #pragma unroll
-    for (int j = 0; j < SR; j++) kr[j] = (j < S && e0 + j < n_ent) ? FK[e0 + j] : 0u;
+    for (int j = 0; j < SR; j++) kr[j] = j < S ? (uint32_t)(src[j] >> 32) : 0u;
     return S;
   };
   uint32_t T = 0;
   int rem = 0;
+  pad_cand(cand, E);
+  clear_hist(hist);
+  __syncthreads();
   const int S0 = load_keys(E);
-  const bool full = E >= k && kth_regs<SR>(kr, S0, k, hist, misc, &T, &rem);
+  const bool full = E >= k && kth_select<SR>(kr, S0, E, lo, hi, k, hist, misc, &T, &rem);
   // the k-th largest candidate is Tge - 1 when ties are cut, else at least Tge
   const uint32_t lowT = full ? (rem > 0 ? T - 1u : T) : 0u;
-  // failing chunks listed in bm[4 NT ...] (tw[] occupies bm[0 .. 4 NT))
+  // failing chunks listed in bm[4 NT ...] (the flags occupy bm[0 .. 4 NT)); a chunk
+  // holds its keys >= held(w) = (overflowed ? none : lo)
+  auto held = [&](uint32_t w) { return bm[w] == 0xFFFFFFFFu ? 0xFFFFFFFFu : lo; };
   uint32_t* fl = bm + 4 * NT;
   int nfail = 0;
   for (int w0 = 0; w0 < wact; w0 += NT) {
     const int w = w0 + tid;
-    const bool f = w < wact && (!full || bm[w] > lowT);
+    const bool f = w < wact && (!full || held((uint32_t)w) > lowT);
     int tot;
     const int o = block_excl_scan(f ? 1 : 0, misc, &tot);
     if (f) fl[nfail + o] = (uint32_t)w;
@@ -997,7 +1193,7 @@ __device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact
 #pragma unroll 1
   for (int f = 0; f < nfail; f++) {
     const uint32_t w = fl[f];
-    const uint32_t twf = bm[w];
+    const uint32_t twf = held(w);
     const int p0 = (int)w * C;
 #pragma unroll 1
     for (int base = 0; base < C; base += NT) {
@@ -1011,49 +1207,21 @@ __device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact
       int tot;
       const int oo = block_excl_scan(take ? 1 : 0, misc, &tot);
       if (Ecur + tot > FIN_ENT) return false;
-      if (take) { FK[Ecur + oo] = key; FP[Ecur + oo] = (uint32_t)p; }
+      if (take) cand[Ecur + oo] = ((uint64_t)key << 32) | (uint32_t)p;
       Ecur += tot;
     }
   }
-  __syncthreads();
   if (Ecur < k) return false;
+  pad_cand(cand, Ecur);
+  clear_hist(hist);
+  __syncthreads();
   const int S1 = load_keys(Ecur);
-  if (!kth_regs<SR>(kr, S1, k, hist, misc, &T, &rem)) return false;
-  // select_explicit takes keys > T - 1 (>= Tge) and the first rem keys equal to Tge - 1
-  const int got = select_explicit(FK, FP, Ecur, nr, k, T - 1u, rem, bm, misc, out);
+  const uint32_t lo2 = min(lo, max(lowT, 0x00800000u));   // every candidate is >= lo2
+  if (!kth_select<SR>(kr, S1, Ecur, lo2, hi, k, hist, misc, &T, &rem)) return false;
+  // select_explicit takes keys > Tge - 1 and the first rem keys equal to Tge - 1
+  const int got = select_explicit(cand, Ecur, nr, k, T - 1u, rem, bm, misc, out);
   if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
   return true;
-}
-
-// x[u] for a runtime u < 4 without indexing registers
-__device__ inline int pick4(const int (&x)[4], int u) {
-  return u == 0 ? x[0] : u == 1 ? x[1] : u == 2 ? x[2] : x[3];
-}
-
-// Exclusive scan of v and maximum of m over the workgroup.  Every thread must call.
-__device__ inline int block_scan_max(int v, uint32_t m, int* misc, int* total, uint32_t* mall) {
-  const int lane = lane_id(), wv = wave_id();
-  const int x = wave_incl_scan(v);
-  m = wave_max_u32(m);
-  if (lane == 63) misc[wv] = x;
-  if (lane == 0) misc[NWAVE + wv] = (int)m;
-  __syncthreads();
-  int before = 0, tot = 0;
-  uint32_t mx = 0;
-  const v4i* m4 = reinterpret_cast<const v4i*>(misc);
-  const v4i s0 = m4[0], s1 = m4[1], x0 = m4[2], x1 = m4[3];
-  const int sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-  const int xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-#pragma unroll
-  for (int i = 0; i < NWAVE; i++) {
-    before += (i < wv) ? sv[i] : 0;
-    tot += sv[i];
-    mx = mx > (uint32_t)xv[i] ? mx : (uint32_t)xv[i];
-  }
-  __syncthreads();
-  *total = tot;
-  *mall = mx;
-  return x - v + before;
 }
 
 // How a row of n keys selects (the same decision in both launches): nothing to select
@@ -1084,15 +1252,12 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
   const int C = a.chunk;
   const int chunk_base = c * C;
   uint8_t* const ws = a.ws;
-
   const int gbound = a.gmax[g];
+  scalars_ready(ge, gbound, a.mode, a.chunk, a.chunk_shift, a.ws, a.nk, a.pt, a.q, a.w, a.kc, a.ks, a.scores, a.ld,
+                a.max_pages, a.num_pages, a.k, a.ent_stride, a.off_ent);
   if (c > 0 && chunk_base >= gbound) return;      // beyond every row of this group
   const bool do_score = (a.mode & MODE_SCORE) != 0;
   const bool do_pub = (a.mode & MODE_PUBLISH) != 0;
-  if (*reinterpret_cast<const uint32_t*>(ws + WS_MAGIC_OFF) != WS_MAGIC) {
-    if (tid == 0 && c == 0 && g == 0) raise_error(ws, IDX_DERR_WS);
-    return;
-  }
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   if (do_score) {
     // Queries and head weights of the group's rows into LDS first (2R + 1 DMA per
@@ -1108,16 +1273,23 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
     }
     if (lane < 8) dma16(a.w + (int64_t)(row0 + (wv % R)) * H * 2 + lane * 16, lds0 + L_W + (wv % R) * (H * 2));
   }
-  // n_keys of the group's rows and the chunk's page ids of every row, in one load
-  // (lanes [0, R): n_keys; lanes [8, 8 + R*P): page_table[row][c*P + j])
-  int ld_lane = 0;
-  if (lane < R) {
-    ld_lane = a.nk[row0 + lane];
-  } else if (do_score && lane >= 8 && lane < 8 + R * P) {
+  // n_keys of the group's rows, the chunk's page ids of every row and the workspace's
+  // magic word, in one load (lanes [0, R): n_keys; lanes [8, 8 + R*P):
+  // page_table[row][c*P + j]; lane 63: the magic word)
+  // (three loads into distinct registers, so that none waits for another)
+  int ld_nk = 0, ld_pt = 0, ld_mg = 0;
+  if (lane < R) ld_nk = a.nk[row0 + lane];
+  if (do_score && lane >= 8 && lane < 8 + R * P) {
     const int i = (lane - 8) / P, j = (lane - 8) % P;
-    if (c * P + j < a.max_pages) ld_lane = a.pt[(int64_t)(row0 + i) * a.max_pages + c * P + j];
+    if (c * P + j < a.max_pages) ld_pt = a.pt[(int64_t)(row0 + i) * a.max_pages + c * P + j];
   }
+  if (lane == 63) ld_mg = *reinterpret_cast<const int*>(ws + WS_MAGIC_OFF);
   wait_vmcnt<0>();
+  const int ld_lane = ld_nk | ld_pt | ld_mg;   // disjoint lanes
+  if ((uint32_t)__builtin_amdgcn_readlane(ld_lane, 63) != WS_MAGIC) {
+    if (tid == 0 && c == 0 && g == 0) raise_error(ws, IDX_DERR_WS);
+    return;
+  }
 
   int n[GR];
   int nmax = 0, rmax = 0;
@@ -1148,7 +1320,6 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
   }
 
   float* const sc_lds = LDS_PTR(float, L_SC);
-  uint64_t* const meta = reinterpret_cast<uint64_t*>(ws + a.off_meta);
   uint64_t* const ent = reinterpret_cast<uint64_t*>(ws + a.off_ent);
 
   if (do_score) {
@@ -1179,60 +1350,80 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
     __syncthreads();
   }
 
+  // ---------------- scores out (first: their latency overlaps the publication) ------
+  // thread t stores 4 consecutive scores: row 4 t / C, positions 4 t % C .. + 4
+  if (do_score && 4 * tid < R * C) {
+    const int i = (4 * tid) >> a.chunk_shift, p = (4 * tid) & (C - 1);
+    const int nv = n[i] - chunk_base;
+    float* dst = a.scores + (int64_t)(row0 + i) * a.ld + chunk_base + p;
+    const v4f v = *reinterpret_cast<const v4f*>(sc_lds + i * CMAX + p);
+    if (p + 4 <= nv && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      *reinterpret_cast<v4f*>(dst) = v;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        if (p + j < nv) dst[j] = v[j];
+    }
+  }
+
   // ---------------- publish (wave i handles row i) -----------------------------------
   if (do_pub && wv < R) {
     const int i = wv;
     const int nr = n[i];
     const int nv = nr - chunk_base;
     if (nv > 0 && row_path(nr, k, shift) == PATH_CAND) {
-      // candidates: every key of the chunk >= t_w (the m-th largest of the 64 lane
-      // maxima), as (key << 32 | position), in ascending position order; a chunk with
-      // more than cap of them publishes none and is flagged
+      // the chunk's candidate block (the first 64 G slots, staged in LDS, then one
+      // coalesced store a slot group): slot 0 = t_w | (overflow << 16 | count) << 32, slot 1
+      // = the chunk's largest key, slots 2 .. count + 1 = every key of the chunk >= t_w
+      // (the m-th largest of the 64 lane maxima) as key << 32 | position, ascending in
+      // position, then zeros.  A chunk with more than cap such keys publishes none of
+      // them and sets the overflow flag.
       const int grow = row0 + i;
       int m, cap;
       candidate_params(nr, C, k, &m, &cap);
+      const v4f* src = reinterpret_cast<const v4f*>(sc_lds + i * CMAX + lane * 8);
+      const v4f f0 = src[0], f1 = src[1];
+      const float fv[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
       uint32_t key[8];
       uint32_t lmax = 0;
 #pragma unroll
       for (int j = 0; j < 8; j++) {
         const int p = lane * 8 + j;
-        key[j] = (p < nv && p < C) ? radix_key(sc_lds[i * CMAX + p]) : 0u;
+        key[j] = (p < nv && p < C) ? radix_key(fv[j]) : 0u;
         lmax = lmax > key[j] ? lmax : key[j];
       }
       const uint32_t thr = wave_kth_largest(lmax, m);
+      const uint32_t cmax = wave_max_u32(lmax);
       int cnt = 0;
 #pragma unroll
       for (int j = 0; j < 8; j++) cnt += (key[j] != 0u && key[j] >= thr) ? 1 : 0;
       const int incl = wave_incl_scan(cnt);
       const int total = __shfl(incl, 63);
-      uint32_t cw;
-      if (total > cap) {
-        cw = 1u << 16;
-      } else {
-        int o = incl - cnt;
-        uint64_t* dst = ent + ((int64_t)grow * a.ent_stride + c) * CAP_MAX;
+      const int G = block_groups(cap);
+      uint64_t* stg = LDS_PTR(uint64_t, L_KEYS) + i * CAP_MAX;   // the pages are consumed
+      stg[lane] = 0ull;
+      if (G == 2) stg[64 + lane] = 0ull;
+      const bool fits = total <= cap;
+      if (fits) {
+        int o = 2 + incl - cnt;
 #pragma unroll
         for (int j = 0; j < 8; j++)
           if (key[j] != 0u && key[j] >= thr) {
-            dst[o] = ((uint64_t)key[j] << 32) | (uint32_t)(chunk_base + lane * 8 + j);
+            stg[o] = ((uint64_t)key[j] << 32) | (uint32_t)(chunk_base + lane * 8 + j);
             o++;
           }
-        cw = (uint32_t)total;
       }
-      if (lane == 0) meta[(int64_t)grow * a.meta_stride + c] = ((uint64_t)thr << 32) | cw;
-    }
-  }
-
-  // ---------------- scores out -------------------------------------------------------
-  if (do_score) {
-#pragma unroll
-    for (int i = 0; i < GR; i++) {
-      if (i >= R) break;
-      const int nv = n[i] - chunk_base;
-      float* dst = a.scores + (int64_t)(row0 + i) * a.ld + chunk_base;
-      __amdgpu_buffer_rsrc_t rs = make_rsrc(dst, (int64_t)(nv > 0 ? (nv < C ? nv : C) : 0) * 4);
-      for (int p = tid; p < C; p += NT)
-        if (p < nv) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc_lds[i * CMAX + p]), rs, p * 4, 0, 0);
+      if (lane == 0) {
+        stg[0] = ((uint64_t)(fits ? (uint32_t)total : (1u << 16)) << 32) | thr;
+        stg[1] = cmax;
+      }
+      // this wave's LDS writes before its reads (LDS executes a wave's operations in order)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      uint64_t* blk = ent + ((int64_t)grow * a.ent_stride + c) * CAP_MAX;
+      blk[lane] = stg[lane];
+      if (G == 2) blk[64 + lane] = stg[64 + lane];
     }
   }
 }
@@ -1247,17 +1438,22 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
   const int lane = tid & 63;
   const int wv = wave_id();
   const uint32_t ge = a.grp[blockIdx.y];
+  scalars_ready(ge, a.gmax[blockIdx.y], a.ws, a.nk, a.k, a.chunk, a.chunk_shift, a.topk, a.scores, a.ld,
+                a.ent_stride, a.off_ent);
   const int R = (int)(ge >> 24);
   const int i = blockIdx.x;
-  if (i >= R) return;
-  const int grow = (int)(ge & 0xFFFFFFu) + i;
+  const int grow = (int)(ge & 0xFFFFFFu) + (i < R ? i : R - 1);   // a row of the group either way
   uint8_t* const ws = a.ws;
-  if (*reinterpret_cast<const uint32_t*>(ws + WS_MAGIC_OFF) != WS_MAGIC) {
+  // the magic word and the row's key count in flight together, before any branch
+  const uint32_t magic = *reinterpret_cast<const uint32_t*>(ws + WS_MAGIC_OFF);
+  int nr = __builtin_amdgcn_readfirstlane(a.nk[grow]);
+  asm volatile("" ::"s"(magic), "s"(nr));          // both loads issued before the branches below
+  if (i >= R) return;
+  if (magic != WS_MAGIC) {
     if (tid == 0 && i == 0 && blockIdx.y == 0) raise_error(ws, IDX_DERR_WS);
     return;
   }
   const int gbound = a.gmax[blockIdx.y];
-  int nr = __builtin_amdgcn_readfirstlane(a.nk[grow]);
   if (nr < 0 || nr > gbound) {
     if (tid == 0) raise_error(ws, IDX_DERR_NKEYS);
     nr = nr < 0 ? 0 : gbound;
@@ -1271,92 +1467,106 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
   }
   int* misc = LDS_PTR(int, L_MISC);
   uint32_t* hist = LDS_PTR(uint32_t, L_HIST);
-  uint32_t* FK = LDS_PTR(uint32_t, L_FK);
-  uint32_t* FP = LDS_PTR(uint32_t, L_FP);
+  uint64_t* cand = LDS_PTR(uint64_t, L_CAND);
   uint32_t* bm = LDS_PTR(uint32_t, L_BM);
   const float* srow = a.scores + (int64_t)grow * a.ld;
   __amdgpu_buffer_rsrc_t rs = make_rsrc(srow, (int64_t)nr * 4);
+  clear_hist(hist);                                  // ordered before use by the barriers below
   bool done = false;
   if (path == PATH_ALL) {
-    // every key of the row into LDS (FK[p] for position p), coalesced: thread t reads
-    // positions t + NT j
-    constexpr int JA = ALL_MAX / NT;
-    const int J = (nr + NT - 1) / NT;
-    uint32_t kv[JA];
+    // every key of the row into LDS at its position, 16-byte loads: thread t reads
+    // positions 4 t + 4 NT j .. + 4; positions past the row read 0 from outside the
+    // buffer resource and are stored as absent keys up to NT slots_for(nr)
+    uint32_t* fk = reinterpret_cast<uint32_t*>(cand);
+    constexpr int JA = ALL_MAX / (4 * NT);
+    const int J = (nr + 4 * NT - 1) / (4 * NT);
+    v4u kv[JA];
 #pragma unroll
     for (int j = 0; j < JA; j++)
-      kv[j] = j < J ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, tid * 4, j * NT * 4, 0) : 0u;
+      kv[j] = j < J ? __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, j * NT * 16, 0))
+                    : v4u{0u, 0u, 0u, 0u};
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;              // key - 1 domain for the minimum
 #pragma unroll
     for (int j = 0; j < JA; j++)
-      if (j < J) FK[j * NT + tid] = radix_key(__uint_as_float(kv[j]));
-    __syncthreads();
+      if (j < J) {
+        uint32_t x0 = kv[j][0], x1 = kv[j][1], x2 = kv[j][2], x3 = kv[j][3];
+        asm volatile("" : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3));   // keeps the conversion (and its wait) out of the load's branch
+        const int p = 4 * tid + 4 * NT * j;
+        const uint32_t y[4] = {p + 0 < nr ? radix_key(__uint_as_float(x0)) : 0u,
+                               p + 1 < nr ? radix_key(__uint_as_float(x1)) : 0u,
+                               p + 2 < nr ? radix_key(__uint_as_float(x2)) : 0u,
+                               p + 3 < nr ? radix_key(__uint_as_float(x3)) : 0u};
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          mn = min(mn, y[c] - 1u);
+          mx = max(mx, y[c]);
+        }
+        *reinterpret_cast<v4u*>(fk + p) = v4u{y[0], y[1], y[2], y[3]};
+      }
+    block_min_max(mn, mx, misc);                     // its barriers also publish fk
     int got = -1;
-    done = select_emit<56, true>(FK, FP, nr, 0u, k, hist, misc, out, &got);
+    done = select_all<ALL_MAX / NT>(fk, nr, mn + 1u, mx, k, hist, misc, out, &got);
     if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
   } else if (path == PATH_CAND) {
-    // ---- chunk words: thread t reads the words of chunks t + NT u (u < upt)
     const int wact = (nr + C - 1) >> a.chunk_shift;
     const int upt = (wact + NT - 1) / NT;
-    const uint64_t* mrow = reinterpret_cast<const uint64_t*>(ws + a.off_meta) + (int64_t)grow * a.meta_stride;
     const uint64_t* erow = reinterpret_cast<const uint64_t*>(ws + a.off_ent) + (int64_t)grow * a.ent_stride * CAP_MAX;
-    __amdgpu_buffer_rsrc_t rmeta = make_rsrc(mrow, (int64_t)wact * 8);
-    uint64_t mv[4];
-#pragma unroll
-    for (int u = 0; u < 4; u++)
-      mv[u] = (u < upt) ? __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rmeta, (tid + NT * u) * 8, 0, 0))
-                        : 0ull;
+    __amdgpu_buffer_rsrc_t rent = make_rsrc(erow, (int64_t)wact * CAP_MAX * 8);
     int m_unused, cap;
     candidate_params(nr, C, k, &m_unused, &cap);
-    uint8_t* cnt8 = LDS_PTR(uint8_t, L_CO);
-    uint32_t* gcnt = LDS_PTR(uint32_t, L_GRP);
-    uint32_t* gbase = gcnt + 256;
-    if (tid < 256) gcnt[tid] = 0;
-    __syncthreads();
-    // per chunk: its count (cnt8), per group of 8 chunks: the count (gcnt); bm[w] =
-    // t_w (0xFFFFFFFF: overflowed, published nothing) for the rare path; E = the
-    // candidates published, t* = the largest t_w, whether any chunk overflowed
-    uint32_t pub = 0, tmax = 0, ovs = 0;
+    const int G = block_groups(cap);
+    // the first gather batch and the chunk headers with their maxima (thread t: chunks
+    // t + NT u; past wact outside the buffer resource) in flight together
+    uint64_t e[32];
+    if (G == 1) gather_issue<1>(rent, wact, 0, e);
+    else gather_issue<2>(rent, wact, 0, e);
+    v4u hv[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+      hv[u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rent, (tid + NT * u) * CAP_MAX * 8, 0, 0));
+    // the candidates published, t* = the largest t_w of the chunks that did not
+    // overflow, the largest key of the row, the overflows; bm[w] flags an overflowed
+    // chunk for the rare path
+    uint32_t t4[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < 4; u++) {
-      const int w = tid + NT * u;
       if (u >= upt) break;
-      const uint32_t lw = (uint32_t)mv[u];
-      const bool live = w < wact;
-      const bool ov = live && ((lw >> 16) & 1u);
-      const uint32_t cu = (live && !ov) ? (lw & 0xFFFFu) : 0u;
-      const uint32_t twu = (uint32_t)(mv[u] >> 32);
-      cnt8[w] = (uint8_t)cu;                       // w < 4 NT: bytes past wact read as 0
-      if (cu) atomicAdd(&gcnt[w >> 3], cu);
-      pub += cu;
-      ovs += ov ? 1u : 0u;
-      if (live && !ov) tmax = max(tmax, twu);
-      if (live) bm[w] = ov ? 0xFFFFFFFFu : twu;
-    }
-    uint32_t t3[3] = {pub, tmax, ovs};
-    block_sum_max_sum(t3, misc);
-    const int E = (int)t3[0];
-    // keys >= t* are all published (t* is at least every chunk's t_w): if k of them are
-    // here, the k-th is among them and no chunk hides a key of the top k
-    const uint32_t lo = t3[1];
-    ovs = t3[2];
-    if (E <= FIN_ENT - 64) {
-      // group bases: an exclusive scan of the 256 group counts (wave 0, 4 a lane)
-      if (wv == 0) {
-        const v4i c4 = reinterpret_cast<const v4i*>(gcnt)[lane];
-        const int t = c4[0] + c4[1] + c4[2] + c4[3];
-        const int b = wave_incl_scan(t) - t;
-        reinterpret_cast<v4i*>(gbase)[lane] = v4i{b, b + c4[0], b + c4[0] + c4[1], b + c4[0] + c4[1] + c4[2]};
+      const int w = tid + NT * u;
+      if (w < wact) {
+        const uint32_t tw = hv[u][0], flags = hv[u][1], cmax = hv[u][2];
+        const bool ov = (flags >> 16) & 1u;
+        t4[0] += flags & 0xFFFFu;
+        if (!ov) t4[1] = max(t4[1], tw);
+        t4[2] = max(t4[2], cmax);
+        t4[3] += ov ? 1u : 0u;
+        bm[w] = ov ? 0xFFFFFFFFu : 0u;
       }
+    }
+    block_sum_max_max_sum(t4, misc);
+    // keys >= t* are all published (t* is at least every chunk's t_w): if k of them are
+    // here, the k-th is among them and no chunk hides a key of the top k.  Only they are
+    // gathered.  (0x00800000 is the smallest key of a finite score.)
+    const uint32_t lo = t4[1] > 0x00800000u ? t4[1] : 0x00800000u;
+    const uint32_t hi = t4[2] > lo ? t4[2] : lo;
+    if ((int)t4[0] <= FIN_ENT) {
+      int E = 0;
+      const int per_batch = (32 / G) * NWAVE;
+      for (int b0 = 0; b0 < wact; b0 += per_batch) {
+        if (b0 > 0) {
+          if (G == 1) gather_issue<1>(rent, wact, b0, e);
+          else gather_issue<2>(rent, wact, b0, e);
+        }
+        E += gather_place(e, lo, E, cand, misc);
+      }
+      pad_cand(cand, E);
       __syncthreads();
-      if (cap > 64) gather_candidates<2>(erow, wact, cnt8, gbase, FK, FP);
-      else gather_candidates<1>(erow, wact, cnt8, gbase, FK, FP);
-      __syncthreads();
-      if (ovs == 0) {
+      if (t4[3] == 0u) {
         int got = -1;
-        done = select_emit<32, false>(FK, FP, E, lo, k, hist, misc, out, &got);
+        done = select_cand<FIN_ENT / NT>(cand, E, lo, hi, k, hist, misc, out, &got);
         if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
       }
-      if (!done && nr <= BITMAP_KEYS) done = rare_select(ws, nr, k, wact, E, C, rs, FK, FP, bm, hist, misc, out);
+      if (!done && nr <= BITMAP_KEYS)
+        done = rare_select(ws, nr, k, wact, E, C, lo, hi, rs, cand, bm, hist, misc, out);
     }
   }
   if (!done) {
@@ -1411,8 +1621,8 @@ Plan plan_topk(int max_keys) {
 }
 
 struct WsLayout {
-  uint64_t off_meta, off_ent, total;
-  int meta_stride, ent_stride;
+  uint64_t off_ent, total;
+  int ent_stride;
 };
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -1421,10 +1631,8 @@ WsLayout layout_for(int rows, int max_keys) {
   const Plan a = plan_score(max_keys), b = plan_topk(max_keys);
   const int stride = (a.wg > b.wg ? a.wg : b.wg);
   WsLayout L;
-  L.meta_stride = stride;
-  L.ent_stride = stride < 4 * NT ? stride : 4 * NT;
-  L.off_meta = WS_HDR;
-  L.off_ent = align256(L.off_meta + (uint64_t)rows * stride * 8);
+  L.ent_stride = stride < 4 * NT ? stride : 4 * NT;     // rows with more chunks never publish
+  L.off_ent = WS_HDR;
   L.total = align256(L.off_ent + (uint64_t)rows * L.ent_stride * CAP_MAX * 8);
   return L;
 }
@@ -1498,9 +1706,7 @@ int launch(const KArgs& args, int P, dim3 grid, bool score_launch, bool select_l
 
 void fill_common(KArgs& args, const WsLayout& L, void* ws) {
   args.ws = static_cast<uint8_t*>(ws);
-  args.meta_stride = L.meta_stride;
   args.ent_stride = L.ent_stride;
-  args.off_meta = L.off_meta;
   args.off_ent = L.off_ent;
 }
 
