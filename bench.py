@@ -1,19 +1,20 @@
-"""Benchmark of the fused score + exact top-2048 call on one MI355X.
+"""Benchmark of the score + exact top-2048 call on one MI355X.
 
 A step is one idx_score_topk call (every stage of the hot path: page walk and key
 streaming, the bf16 MFMA contraction, the ReLU / head-weighted epilogue, the radix
-keys, the candidate exchange, the threshold and the ascending emission) over the
-4-row x 131,072-key verify workload: one request, rows seeing 131,069..131,072 keys,
-64 heads of dimension 128, pages of 64 FP8-E4M3 keys with per-key f32 scales on a
-seeded random page permutation, k = 2048.  Inputs are synthetic and resident in HBM
-before the timed region; the steps rotate over several copies of the key cache
-(32 by default, over 512 MiB) so that keys come from HBM rather than the 256 MiB
-last-level cache.
+keys, the per-chunk candidate publication, the threshold and the ascending emission),
+two launches on the stream (score_kernel<8>, then select_kernel), over the 4-row x
+131,072-key verify workload: one request, rows seeing 131,069..131,072 keys, 64 heads
+of dimension 128, pages of 64 FP8-E4M3 keys with per-key f32 scales on a seeded random
+page permutation, k = 2048.  Inputs are synthetic and resident in HBM before the timed
+region; the steps rotate over several copies of the key cache (32 by default, over 512
+MiB) so that keys come from HBM rather than the 256 MiB last-level cache.
 
-Prints one JSON line.  The roofline object is for the dominant (and only) kernel,
-idx_kernel<8>; its duration is the HIP-event time of the timed steps on the launch
-stream divided by the step count.  The CPU baseline is the oracle as it stands,
-timed on the host over the same workload.
+Prints one JSON line.  "roofline" is for the call (both launches: the scoring launch
+dominates); its duration is the HIP-event time of the timed steps on the launch stream
+divided by the step count.  "roofline_score_kernel" times idx_score (the scoring launch
+alone) the same way.  The CPU baseline is the oracle as it stands, timed on the host
+over the same workload.
 """
 import argparse
 import hashlib
@@ -46,10 +47,10 @@ def kernel_source_hash():
 
 
 def measured_traffic(kernel_hash, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary (FETCH_SIZE and
-    WRITE_SIZE, scaled by a copy kernel's readings), if it was taken on the current kernel
-    source and workload; else None."""
-    path = os.path.join(ROOT, "profiles", "idx_kernel8_c2_traffic.txt")
+    """HBM bytes per call (both launches) from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by a copy kernel's readings), if it was taken on the
+    current kernel source and workload; else None."""
+    path = os.path.join(ROOT, "profiles", "score_select_c2_traffic.txt")
     try:
         lines = open(path).read().splitlines()
     except OSError:
@@ -83,8 +84,8 @@ def main():
                          "many MiB five times: the calibration dispatch for the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU; the multi-GPU sharding is a design, "
-                                   "not a build (see DESIGN.md)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; sharding over several GPUs is "
+                                   "designed but not built", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np
@@ -128,21 +129,28 @@ def main():
         if rc:
             raise idx.IdxError(rc, "idx_score_topk")
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = e0.elapsed_time(e1)
-    ms_per_step = ms_total / args.steps
+    def score_only(i):
+        s, _ = structs[i % copies]
+        rc = L.idx_score(ctypes.byref(s), sptr, scores.shape[1], wsp, ws.nbytes, ctypes.c_void_p(sp))
+        if rc:
+            raise idx.IdxError(rc, "idx_score")
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, time.perf_counter() - t0
+
+    ms_score, _ = timed(score_only)
+    ms_per_step, wall = timed(step)
     code, detail = idx.device_status(ws)
     if code != 0:
         raise RuntimeError(f"device error {detail:#x}")
@@ -163,6 +171,7 @@ def main():
     dur_s = ms_per_step * 1e-3
     flops_rate = aflops / dur_s / 1e12
     bytes_rate = abytes / dur_s / 1e9
+    score_rate = aflops / (ms_score * 1e-3) / 1e12
     workload = (f"{args.config}: {prob.num_req} request(s), {prob.rows} rows, n_keys "
                 f"{int(prob.n_keys.min())}..{int(prob.n_keys.max())}, H=64, D=128, page 64, k={prob.k}, "
                 f"FP8-E4M3 keys + f32 scales, bf16 q and w")
@@ -184,11 +193,16 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; the workload recipe in workloads/synth.py)",
         "config": {"workload": workload, "key_rows": key_rows, "rotate_copies": copies,
-                   "entry_point": "idx_score_topk (one kernel launch)", "parallelism": "single GPU"},
+                   "entry_point": "idx_score_topk (score_kernel<8> then select_kernel on one stream)",
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "dtype": "bf16", "achieved": flops_rate, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops_rate / BF16_PEAK_TFLOPS,
-                     "traffic": traffic, "kernel": "idx_kernel<8>",
+                     "traffic": traffic, "kernel": "score_kernel<8> + select_kernel (one call)",
                      "algorithmic_flops_per_launch": aflops},
+        "roofline_score_kernel": {"bound": "mfma", "dtype": "bf16", "achieved": score_rate,
+                                  "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": score_rate / BF16_PEAK_TFLOPS, "kernel": "score_kernel<8> (idx_score)",
+                                  "us_per_launch": ms_score * 1e3},
         "roofline_hbm": {"bound": "hbm", "achieved": bytes_rate, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": bytes_rate / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": abytes},
         "roofline_fp8_context": {"achieved": flops_rate, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
