@@ -81,7 +81,7 @@ static_assert(BITMAP_KEYS / 8 >= 4 * NT * 8, "the failing-chunk list (2 words a 
 static_assert(ALL_MAX % (4 * NT) == 0 && FIN_ENT % (4 * NT) == 0, "register segments of whole slot groups");
 static_assert(ALL_MAX * 4 <= FIN_ENT * 8, "all-keys rows fit the candidate area");
 static_assert(L_CAND % 16 == 0, "16-byte candidate reads");
-static_assert(CAP_MAX == 128, "a chunk's header and candidates are gathered in at most two 64-slot groups");
+static_assert(CAP_MAX == 128, "a chunk's candidate block has at most four 32-slot groups");
 static_assert(L_SCORE_END <= 160 * 1024 && L_FIN_END <= 160 * 1024, "LDS budget");
 
 // workspace header (bytes)
@@ -176,13 +176,19 @@ __device__ __forceinline__ void scalars_ready(const T&... v) {
 // is a negative int32, every positive float a positive one
 __device__ inline float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-// m-th largest of one value per lane (m >= 1): the largest t with #{v >= t} >= m.
-__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int m) {
-  uint32_t t = 0;
-  for (int b = 31; b >= 0; --b) {
-    uint32_t cand = t | (1u << b);
-    uint64_t bal = __ballot(v >= cand);
-    if (__popcll(bal) >= m) t = cand;
+// A lower bound t of the m-th largest of one value per lane (1 <= m <= 64), for values
+// known to lie in [lo, hi] with at least m lanes >= lo: bisection over the bits below the
+// common prefix of lo and hi, at most `bits` of them from the top, keeping #{v >= t} >= m.
+// With every bit searched, t is the m-th largest itself.
+__device__ __forceinline__ uint32_t wave_kth_bound(uint32_t v, int m, uint32_t lo, uint32_t hi, int bits) {
+  const uint32_t diff = lo ^ hi;
+  if (diff == 0u) return lo;
+  const int top = 31 - __clz(diff);
+  uint32_t t = top == 31 ? 0u : lo & ~((2u << top) - 1u);
+  const int last = top - bits + 1 > 0 ? top - bits + 1 : 0;
+  for (int b = top; b >= last; --b) {
+    const uint32_t c = t | (1u << b);
+    if ((int)__popcll(__ballot(v >= c)) >= m) t = c;
   }
   return t;
 }
@@ -780,18 +786,21 @@ __device__ void global_select_row(const float* row, int n, int k, int32_t* out, 
   }
 }
 
-// m (lane-maximum rank used as the local threshold) and the candidate cap, from the
-// row length n, chunk size C and k.  About k*C/n keys of a chunk reach the top k.
-__device__ inline void candidate_params(int n, int C, int k, int* m, int* cap) {
+// m (the rank of a chunk's local threshold: its m-th largest key), the number G of
+// 32-slot groups of its candidate block and the candidate cap 32 G - 2 (slots 0 and 1
+// hold the header and the maximum), from the row length n, chunk size C and k.  About
+// k*C/n keys of a chunk reach the top k; m adds a margin so that the largest threshold
+// over the chunks stays below the row's k-th key, and the cap leaves room for ties.
+__device__ inline void candidate_params(int n, int C, int k, int* m, int* cap, int* groups) {
   // k * C <= 2^20 and n >= 1: 32-bit arithmetic is exact
   const uint32_t lam = ((uint32_t)(k * C) + (uint32_t)n - 1u) / (uint32_t)n;
   int mm = (int)(lam + lam / 4u + 12u);
   mm = mm > 64 ? 64 : mm;
-  int cc = 2 * mm + 16;
-  cc = cc > C ? C : cc;
-  cc = cc > CAP_MAX - 2 ? CAP_MAX - 2 : cc;          // slots 0 and 1 hold the header and the maximum
+  const int need = mm + (mm / 4 > 4 ? mm / 4 : 4);
+  const int G = need <= 30 ? 1 : (need <= 62 ? 2 : 4);
   *m = mm;
-  *cap = cc;
+  *cap = 32 * G - 2;
+  *groups = G;
 }
 
 // Whether any / every thread of the workgroup holds p (misc[48 .. 56) as scratch).
@@ -1009,30 +1018,37 @@ __device__ __forceinline__ void block_sum_max_max_sum(uint32_t (&t)[4], int* mis
   t[3] = sd;
 }
 
-// Candidate blocks: chunk w of a row owns CAP_MAX 8-byte slots, of which the first
-// 64 G are written by every call (G = block_groups(cap)).  Slot 0 is the header t_w |
+// Candidate blocks: chunk w of a row owns the 32 G 8-byte slots [32 G w, 32 G w + 32 G)
+// of the row's block area (G from candidate_params; the area has room for CAP_MAX slots
+// a chunk), all written by every call that uses them.  Slot 0 is the header t_w |
 // (overflow << 16 | count) << 32, slot 1 the chunk's largest key, slots 2 .. count + 1
-// the candidates as key << 32 | position, ascending in position, and the rest of the 64 G
-// slots zero.  The upper word of a header, a maximum or a zero slot is below any key,
-// so "upper word >= t*" alone picks the candidates that count.
-__host__ __device__ inline int block_groups(int cap) { return (2 + cap + 63) >> 6; }
+// the candidates as key << 32 | position, ascending in position, and the rest zero.  The
+// upper word of a header, a maximum or a zero slot is below any key, so "upper word >=
+// t*" alone picks the candidates that count.
 
-// One batch of the gather: wave v reads, with 16-byte loads, the 64 G slots of the
-// chunks w0 .. w0 + 32 / G (w0 = b0 + v 32 / G): load q of lane l covers slots
-// 2 (l & 31), + 1 of chunk w0 + 2 q + (l >> 5) (G = 1), or slots 64 (l >> 5) + 2 (l & 31),
-// + 1 of chunk w0 + q (G = 2).  All loads are issued before any is used; chunks at or
-// past wact point outside the buffer resource (no traffic, zero result).
+// loads a lane issues per gather batch (two slots each)
+constexpr int GQ = 8;
+
+// chunks a batch covers (all waves)
+__host__ __device__ inline int batch_chunks(int G) { return NWAVE * GQ * 4 / G; }
+
+// One batch of the gather: wave v reads, with 16-byte loads, the 32 G slots of each of
+// the chunks w0 .. w0 + 4 GQ / G (w0 = b0 + v 4 GQ / G).  Load q of lane l covers slots
+// 2 (l % 16 G), + 1 of chunk w0 + q 4 / G + l / 16 G, so within a wave the loads run in
+// chunk order and the lanes of a load in chunk and slot order.  All loads are issued
+// before any is used; chunks at or past wact point outside the buffer resource (no
+// traffic, zero result).
 template <int G>
-__device__ __forceinline__ void gather_issue(__amdgpu_buffer_rsrc_t rent, int wact, int b0, uint64_t (&e)[32]) {
+__device__ __forceinline__ void gather_issue(__amdgpu_buffer_rsrc_t rent, int wact, int b0, uint64_t (&e)[2 * GQ]) {
   constexpr int OOB = 0x7FFFFFF0;
+  constexpr int LPC = 16 * G;                         // lanes per chunk
   const int lane = lane_id();
-  const int w0 = b0 + wave_id() * (32 / G);
-  const int h = lane >> 5, l2 = 2 * (lane & 31);
+  const int w0 = b0 + wave_id() * (GQ * 4 / G) + lane / LPC;
+  const int slot = 2 * (lane % LPC);
 #pragma unroll
-  for (int q = 0; q < 16; q++) {
-    const int w = G == 1 ? w0 + 2 * q + h : w0 + q;
-    const int slot = G == 1 ? l2 : 64 * h + l2;
-    const int off = w < wact ? (w * CAP_MAX + slot) * 8 : OOB;
+  for (int q = 0; q < GQ; q++) {
+    const int w = w0 + q * (4 / G);
+    const int off = w < wact ? (w * 32 * G + slot) * 8 : OOB;
     const v4u x = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rent, off, 0, 0));
     e[2 * q] = ((uint64_t)x[1] << 32) | x[0];
     e[2 * q + 1] = ((uint64_t)x[3] << 32) | x[2];
@@ -1044,12 +1060,12 @@ __device__ __forceinline__ void gather_issue(__amdgpu_buffer_rsrc_t rent, int wa
 // load and slot parity ranks the kept slots within the wave, the wave totals place the
 // waves.  Dropped slots write to the 64 dummy entries past FIN_ENT.  Returns the
 // batch's kept count.  Every thread must call.
-__device__ __forceinline__ int gather_place(const uint64_t (&e)[32], uint32_t lo, int E0, uint64_t* cand, int* misc) {
+__device__ __forceinline__ int gather_place(const uint64_t (&e)[2 * GQ], uint32_t lo, int E0, uint64_t* cand, int* misc) {
   const int lane = lane_id(), wv = wave_id();
   int o = 0;
-  int r0[16], r1[16];
+  int r0[GQ], r1[GQ];
 #pragma unroll
-  for (int q = 0; q < 16; q++) {
+  for (int q = 0; q < GQ; q++) {
     const bool k0 = (uint32_t)(e[2 * q] >> 32) >= lo;
     const bool k1 = (uint32_t)(e[2 * q + 1] >> 32) >= lo;
     const uint64_t m0 = __ballot(k0), m1 = __ballot(k1);
@@ -1074,7 +1090,7 @@ __device__ __forceinline__ int gather_place(const uint64_t (&e)[32], uint32_t lo
   const int base = E0 + before;
   const int dummy = FIN_ENT + lane;
 #pragma unroll
-  for (int q = 0; q < 16; q++) {
+  for (int q = 0; q < GQ; q++) {
     cand[r0[q] >= 0 ? base + r0[q] : dummy] = e[2 * q];
     cand[r1[q] >= 0 ? base + r1[q] : dummy] = e[2 * q + 1];
   }
@@ -1372,15 +1388,18 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
     const int nr = n[i];
     const int nv = nr - chunk_base;
     if (nv > 0 && row_path(nr, k, shift) == PATH_CAND) {
-      // the chunk's candidate block (the first 64 G slots, staged in LDS, then one
-      // coalesced store a slot group): slot 0 = t_w | (overflow << 16 | count) << 32, slot 1
-      // = the chunk's largest key, slots 2 .. count + 1 = every key of the chunk >= t_w
-      // (the m-th largest of the 64 lane maxima) as key << 32 | position, ascending in
-      // position, then zeros.  A chunk with more than cap such keys publishes none of
-      // them and sets the overflow flag.
+      // the chunk's candidate block (32 G slots, staged in LDS, then stored coalesced):
+      // slot 0 = t_w | (overflow << 16 | count) << 32, slot 1 = the chunk's largest key,
+      // slots 2 .. count + 1 = every key of the chunk >= t_w as key << 32 | position,
+      // ascending in position, then zeros.  t_w is a lower bound of the chunk's m-th
+      // largest key, so at least m keys are published.  thr0, a bound of the m-th largest
+      // of the 64 lane maxima (8 keys a lane, 12 bisection steps), is one; the keys >= thr0
+      // (at most 64 of them, else thr0 is t_w) are narrowed to t_w by 8 more steps over
+      // [thr0, chunk max].  A chunk with more than cap keys >= t_w publishes none of them
+      // and sets the overflow flag.
       const int grow = row0 + i;
-      int m, cap;
-      candidate_params(nr, C, k, &m, &cap);
+      int m, cap, G;
+      candidate_params(nr, C, k, &m, &cap, &G);
       const v4f* src = reinterpret_cast<const v4f*>(sc_lds + i * CMAX + lane * 8);
       const v4f f0 = src[0], f1 = src[1];
       const float fv[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
@@ -1392,17 +1411,37 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
         key[j] = (p < nv && p < C) ? radix_key(fv[j]) : 0u;
         lmax = lmax > key[j] ? lmax : key[j];
       }
-      const uint32_t thr = wave_kth_largest(lmax, m);
       const uint32_t cmax = wave_max_u32(lmax);
+      const uint32_t thr0 = wave_kth_bound(lmax, m, wave_min_u32(lmax), cmax, 12);
+      int cnt0 = 0;
+#pragma unroll
+      for (int j = 0; j < 8; j++) cnt0 += (key[j] != 0u && key[j] >= thr0) ? 1 : 0;
+      const int incl0 = wave_incl_scan(cnt0);
+      const int total0 = __builtin_amdgcn_readlane(incl0, 63);
+      uint32_t thr = thr0;
+      if (total0 <= 64) {
+        uint32_t* kst = LDS_PTR(uint32_t, L_Q) + i * 64;   // the queries are in registers
+        int o = incl0 - cnt0;
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+          if (key[j] != 0u && key[j] >= thr0) {
+            kst[o] = key[j];
+            o++;
+          }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint32_t v = lane < total0 ? kst[lane] : 0u;
+        thr = wave_kth_bound(v, m, thr0, cmax, 8);
+      }
       int cnt = 0;
 #pragma unroll
       for (int j = 0; j < 8; j++) cnt += (key[j] != 0u && key[j] >= thr) ? 1 : 0;
       const int incl = wave_incl_scan(cnt);
       const int total = __shfl(incl, 63);
-      const int G = block_groups(cap);
+      const int SL = 32 * G;
       uint64_t* stg = LDS_PTR(uint64_t, L_KEYS) + i * CAP_MAX;   // the pages are consumed
-      stg[lane] = 0ull;
-      if (G == 2) stg[64 + lane] = 0ull;
+      for (int q = lane; q < SL; q += 64) stg[q] = 0ull;
       const bool fits = total <= cap;
       if (fits) {
         int o = 2 + incl - cnt;
@@ -1421,9 +1460,8 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      uint64_t* blk = ent + ((int64_t)grow * a.ent_stride + c) * CAP_MAX;
-      blk[lane] = stg[lane];
-      if (G == 2) blk[64 + lane] = stg[64 + lane];
+      uint64_t* blk = ent + (int64_t)grow * a.ent_stride * CAP_MAX + (int64_t)c * SL;
+      for (int q = lane; q < SL; q += 64) blk[q] = stg[q];
     }
   }
 }
@@ -1511,19 +1549,23 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
     const int wact = (nr + C - 1) >> a.chunk_shift;
     const int upt = (wact + NT - 1) / NT;
     const uint64_t* erow = reinterpret_cast<const uint64_t*>(ws + a.off_ent) + (int64_t)grow * a.ent_stride * CAP_MAX;
-    __amdgpu_buffer_rsrc_t rent = make_rsrc(erow, (int64_t)wact * CAP_MAX * 8);
-    int m_unused, cap;
-    candidate_params(nr, C, k, &m_unused, &cap);
-    const int G = block_groups(cap);
+    int m_unused, cap, G;
+    candidate_params(nr, C, k, &m_unused, &cap, &G);
+    const int SL = 32 * G;                           // slots a chunk
+    __amdgpu_buffer_rsrc_t rent = make_rsrc(erow, (int64_t)wact * SL * 8);
     // the first gather batch and the chunk headers with their maxima (thread t: chunks
     // t + NT u; past wact outside the buffer resource) in flight together
-    uint64_t e[32];
-    if (G == 1) gather_issue<1>(rent, wact, 0, e);
-    else gather_issue<2>(rent, wact, 0, e);
+    uint64_t e[2 * GQ];
+    auto issue = [&](int b0) {
+      if (G == 1) gather_issue<1>(rent, wact, b0, e);
+      else if (G == 2) gather_issue<2>(rent, wact, b0, e);
+      else gather_issue<4>(rent, wact, b0, e);
+    };
+    issue(0);
     v4u hv[4];
 #pragma unroll
     for (int u = 0; u < 4; u++)
-      hv[u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rent, (tid + NT * u) * CAP_MAX * 8, 0, 0));
+      hv[u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rent, (tid + NT * u) * SL * 8, 0, 0));
     // the candidates published, t* = the largest t_w of the chunks that did not
     // overflow, the largest key of the row, the overflows; bm[w] flags an overflowed
     // chunk for the rare path
@@ -1550,12 +1592,9 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
     const uint32_t hi = t4[2] > lo ? t4[2] : lo;
     if ((int)t4[0] <= FIN_ENT) {
       int E = 0;
-      const int per_batch = (32 / G) * NWAVE;
+      const int per_batch = batch_chunks(G);
       for (int b0 = 0; b0 < wact; b0 += per_batch) {
-        if (b0 > 0) {
-          if (G == 1) gather_issue<1>(rent, wact, b0, e);
-          else gather_issue<2>(rent, wact, b0, e);
-        }
+        if (b0 > 0) issue(b0);
         E += gather_place(e, lo, E, cand, misc);
       }
       pad_cand(cand, E);
