@@ -273,18 +273,22 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   return x - v + before;
 }
 
-// Histogram increment of one key per lane (when `m`), aggregated over the wave for
-// the bin of the first participating lane: radix digits of nearby scores pile into
+// Histogram increment of one key per lane (when `m`), aggregated over the wave: up to
+// four rounds each add the count of the bin of the first lane still pending with one
+// atomic, then the rest add one each.  Radix digits of nearby or tied scores pile into
 // a few bins, and serialised LDS atomics on one address are the cost to avoid.
 __device__ inline void hist_add(uint32_t* hist, bool m, uint32_t bin) {
-  const uint64_t mb = __ballot(m);
-  if (mb == 0) return;
-  const int first = __ffsll((unsigned long long)mb) - 1;
-  const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, first);
-  const bool same = m && bin == lb;
-  const uint64_t sb = __ballot(same);
-  if (lane_id() == first) atomicAdd(&hist[lb], (uint32_t)__popcll(sb));
-  if (m && !same) atomicAdd(&hist[bin], 1u);
+  uint64_t act = __ballot(m);
+#pragma unroll
+  for (int round = 0; round < 4; round++) {
+    if (act == 0) return;
+    const int first = __ffsll((unsigned long long)act) - 1;
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, first);
+    const uint64_t sb = __ballot(bin == lb) & act;
+    if (lane_id() == first) atomicAdd(&hist[lb], (uint32_t)__popcll(sb));
+    act &= ~sb;
+  }
+  if ((act >> lane_id()) & 1ull) atomicAdd(&hist[bin], 1u);
 }
 
 // Radix digit search: the digit d of hist[0 .. nbins) (nbins a power of two, <= 4096)
@@ -718,71 +722,108 @@ __device__ int select_explicit(const uint64_t* cand, int E, int n, int k, uint32
 }
 
 // Exact top-k of row scores in global memory (n > k), one workgroup, LDS for the
-// histogram only: radix select over all scores, then an ordered emission.
-__device__ void global_select_row(const float* row, int n, int k, int32_t* out, uint32_t* hist, int* misc) {
+// histogram only.  Radix passes of 11, 11 and 10 bits over all scores (16-byte loads, 32
+// keys a thread in flight) find the k-th key; they stop early once every key of the
+// digit found is selected, or when all keys are equal (min = max, from the first pass).
+// The result is (Tge, rem): every key >= Tge is selected, and the first rem keys equal to
+// Tge - 1.  An ordered emission (16 consecutive positions a thread, one block scan a
+// round) writes the list and stops once k positions are out.  Every thread must call.
+__device__ __forceinline__ void global_select_row(const float* row, int n, int k, int32_t* out, uint32_t* hist, int* misc) {
   const int tid = threadIdx.x;
   __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (int64_t)n * 4);
-  uint32_t prefix = 0, mask = 0;
-  int rem = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
+  constexpr int U = 8;                                // 16-byte loads a thread per round
+  constexpr int ROUND = NT * 4 * U;
+  uint32_t prefix = 0, mask = 0, Tge = 0;
+  int rem = k, trem = 0;
+  bool resolved = false;
+  for (int pass = 0; pass < 3 && !resolved; pass++) {
+    const int width = pass < 2 ? 11 : 10;
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = 1 << width;
+    for (int b = tid; b < nb; b += NT) hist[b] = 0;
     __syncthreads();
-    for (int base = 0; base < n; base += NT * 8) {
-      uint32_t v[8];
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int base = 0; base < n; base += ROUND) {
+      v4u v[U];
 #pragma unroll
-      for (int j = 0; j < 8; j++)
-        v[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (base + j * NT + tid) * 4, 0, 0);
+      for (int u = 0; u < U; u++)
+        v[u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, (base + (u * NT + tid) * 4) * 4, 0, 0));
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const int p = base + j * NT + tid;
-        const uint32_t key = radix_key(__uint_as_float(v[j]));
-        hist_add(hist, p < n && (key & mask) == prefix, (key >> shift) & 255u);
+      for (int u = 0; u < U; u++)
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          const int p = base + (u * NT + tid) * 4 + c;
+          const bool valid = p < n;
+          const uint32_t key = radix_key(__uint_as_float(v[u][c]));
+          if (pass == 0) {
+            mn = min(mn, valid ? key : 0xFFFFFFFFu);
+            mx = max(mx, valid ? key : 0u);
+          }
+          hist_add(hist, valid && (key & mask) == prefix, (key >> shift) & (uint32_t)(nb - 1));
+        }
+    }
+    if (pass == 0) {
+      block_min_max(mn, mx, misc);
+      if (mn == mx) {                                 // all keys equal: the first k of them
+        Tge = mn + 1u;
+        trem = k;
+        break;
       }
     }
     __syncthreads();
-    find_digit(hist, 256, rem, misc);
-    prefix |= (uint32_t)misc[8] << shift;
-    mask |= 0xFFu << shift;
-    rem = misc[9];
+    find_digit(hist, nb, rem, misc);
+    const uint32_t d = (uint32_t)misc[8];
+    const int r = misc[9];
+    const int cnt = misc[10];
+    prefix |= d << shift;
+    mask |= (uint32_t)(nb - 1) << shift;
+    if (cnt == r) {                                   // every key of digit d: the keys >= prefix
+      Tge = prefix;
+      trem = 0;
+      resolved = true;
+    } else if (pass == 2) {                           // r of the keys equal to prefix
+      Tge = prefix + 1u;
+      trem = r;
+      resolved = true;
+    }
+    rem = r;
     __syncthreads();
   }
-  const uint32_t T = prefix;
-  int eq_carry = 0, sel_carry = 0;
-  for (int base = 0; base < n; base += NT * 8) {
-    const int p0 = base + tid * 8;
-    uint32_t key[8];
+  const uint32_t Teq = Tge - 1u;
+  int gt_carry = 0, eq_carry = 0;
+  for (int base = 0; base < n; base += NT * 16) {
+    const int p0 = base + tid * 16;
+    uint32_t key[16];
 #pragma unroll
-    for (int j = 0; j < 8; j++)
-      key[j] = radix_key(__uint_as_float(
-          (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, (p0 + j) * 4, 0, 0)));
-    int ceq = 0;
+    for (int u = 0; u < 4; u++) {
+      const v4u x = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, p0 * 4 + 16 * u, 0, 0));
 #pragma unroll
-    for (int j = 0; j < 8; j++) ceq += (p0 + j < n && key[j] == T) ? 1 : 0;
-    int eq_tot;
-    int eq_before = block_excl_scan(ceq, misc, &eq_tot) + eq_carry;
-    bool sel[8];
-    int cs = 0;
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const bool valid = p0 + j < n;
-      bool s = valid && key[j] > T;
-      if (valid && key[j] == T) {
-        s = eq_before < rem;
-        eq_before++;
-      }
-      sel[j] = s;
-      cs += s ? 1 : 0;
+      for (int c = 0; c < 4; c++) key[4 * u + c] = p0 + 4 * u + c < n ? radix_key(__uint_as_float(x[c])) : 0u;
     }
-    int sel_tot;
-    int o = block_excl_scan(cs, misc, &sel_tot) + sel_carry;
+    int gt = 0, eq = 0;
 #pragma unroll
-    for (int j = 0; j < 8; j++)
-      if (sel[j]) {
+    for (int j = 0; j < 16; j++) {
+      gt += key[j] != 0u && key[j] >= Tge ? 1 : 0;
+      eq += key[j] != 0u && key[j] == Teq ? 1 : 0;
+    }
+    int tot;
+    const int packed = block_excl_scan(gt | (eq << 16), misc, &tot);
+    int gtc = gt_carry + (packed & 0xFFFF), eqc = eq_carry + (packed >> 16);
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      if (key[j] == 0u) continue;
+      if (key[j] >= Tge) {
+        const int o = gtc + (eqc < trem ? eqc : trem);
         if (o < k) out[o] = p0 + j;
-        o++;
+        gtc++;
+      } else if (key[j] == Teq) {
+        if (eqc < trem && gtc + eqc < k) out[gtc + eqc] = p0 + j;
+        eqc++;
       }
-    eq_carry += eq_tot;
-    sel_carry += sel_tot;
+    }
+    gt_carry += tot & 0xFFFF;
+    eq_carry += tot >> 16;
+    if (gt_carry + (eq_carry < trem ? eq_carry : trem) >= k) break;
   }
 }
 
@@ -1161,14 +1202,15 @@ __device__ __forceinline__ bool select_all(uint32_t* fk, int n, uint32_t lo, uin
   return true;
 }
 
-// Candidate path when the certificate fails.  cand[0 .. E) holds every key >= lo of the
-// chunks that did not overflow (bm[w] = 0xFFFFFFFF marks an overflowed chunk, which
-// holds none); every key of the row is <= hi.  T0 = the k-th candidate (if there are
-// k); every chunk whose held range does not reach down to T0 (an overflowed chunk, or lo
-// > T0) is re-read from the row's scores for its keys >= T0 that are not held, after
-// which every key >= T0 of the row is a candidate, and the top k is taken from that set
-// through a position bitmap.  Returns true when it selected, false to fall back to the
-// multi-pass select over memory.  Every thread must call.
+// Candidate path when the certificate fails.  cand[0 .. E) holds every published key >=
+// lo (chunk w published its keys >= bm[w]; bm[w] = 0xFFFFFFFF marks an overflowed chunk,
+// which published none), so chunk w holds its keys >= held(w) = max(bm[w], lo); every key
+// of the row is <= hi.  T0 = the k-th candidate (if there are k), at most the row's k-th
+// key; every chunk whose held range does not reach down to T0 is re-read from the row's
+// scores for its keys in [T0, held(w)), after which every key >= T0 of the row is a
+// candidate, and the top k is taken from that set through a position bitmap.  Returns
+// true when it selected, false to fall back to the multi-pass select over memory.  Every
+// thread must call.
 __device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact, int E, int C, uint32_t lo,
                                             uint32_t hi, __amdgpu_buffer_rsrc_t rs, uint64_t* cand, uint32_t* bm,
                                             uint32_t* hist, int* misc, int32_t* out) {
@@ -1191,9 +1233,11 @@ __device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact
   const bool full = E >= k && kth_select<SR>(kr, S0, E, lo, hi, k, hist, misc, &T, &rem);
   // the k-th largest candidate is Tge - 1 when ties are cut, else at least Tge
   const uint32_t lowT = full ? (rem > 0 ? T - 1u : T) : 0u;
-  // failing chunks listed in bm[4 NT ...] (the flags occupy bm[0 .. 4 NT)); a chunk
-  // holds its keys >= held(w) = (overflowed ? none : lo)
-  auto held = [&](uint32_t w) { return bm[w] == 0xFFFFFFFFu ? 0xFFFFFFFFu : lo; };
+  // failing chunks listed in bm[4 NT ...] (the thresholds occupy bm[0 .. 4 NT))
+  auto held = [&](uint32_t w) {
+    const uint32_t b = bm[w];
+    return b == 0xFFFFFFFFu ? b : (b > lo ? b : lo);
+  };
   uint32_t* fl = bm + 4 * NT;
   int nfail = 0;
   for (int w0 = 0; w0 < wact; w0 += NT) {
@@ -1205,27 +1249,41 @@ __device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact
     nfail += tot;
   }
   __syncthreads();
+  // the failing chunks' keys in [lowT, held(w)), in one pass over all of them (8 keys a
+  // thread a round; the candidate order is free, the emission goes through a bitmap).
+  // Give up once they overflow the candidate area, or at once without a T0 (every key
+  // of every chunk would be taken) when the chunks hold too many keys.
+  if (!full && E + nfail * C > FIN_ENT) return false;
+  const int cshift = 31 - __clz(C);
+  const int tot_keys = nfail * C;
   int Ecur = E;
 #pragma unroll 1
-  for (int f = 0; f < nfail; f++) {
-    const uint32_t w = fl[f];
-    const uint32_t twf = held(w);
-    const int p0 = (int)w * C;
-#pragma unroll 1
-    for (int base = 0; base < C; base += NT) {
-      const int p = p0 + base + tid;
-      bool take = false;
-      uint32_t key = 0;
-      if (base + tid < C && p < nr) {
-        key = radix_key(__uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, p * 4, 0, 0)));
-        take = key >= lowT && key < twf;
-      }
-      int tot;
-      const int oo = block_excl_scan(take ? 1 : 0, misc, &tot);
-      if (Ecur + tot > FIN_ENT) return false;
-      if (take) cand[Ecur + oo] = ((uint64_t)key << 32) | (uint32_t)p;
-      Ecur += tot;
+  for (int base = 0; base < tot_keys; base += NT * 8) {
+    uint32_t raw[8];
+    int pos[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int f = base + j * NT + tid;
+      const int w = f < tot_keys ? (int)fl[f >> cshift] : 0;
+      pos[j] = f < tot_keys ? (w << cshift) + (f & (C - 1)) : nr;
+      raw[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, pos[j] < nr ? pos[j] * 4 : 0x7FFFFFF0, 0, 0);
     }
+    uint32_t key[8];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      key[j] = radix_key(__uint_as_float(raw[j]));
+      const bool take = pos[j] < nr && key[j] >= lowT && key[j] < held((uint32_t)(pos[j] >> cshift));
+      if (!take) pos[j] = -1;
+      cnt += take ? 1 : 0;
+    }
+    int tot;
+    int o = Ecur + block_excl_scan(cnt, misc, &tot);
+    if (Ecur + tot > FIN_ENT) return false;
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      if (pos[j] >= 0) cand[o++] = ((uint64_t)key[j] << 32) | (uint32_t)pos[j];
+    Ecur += tot;
   }
   if (Ecur < k) return false;
   pad_cand(cand, Ecur);
@@ -1567,8 +1625,8 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
     for (int u = 0; u < 4; u++)
       hv[u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rent, (tid + NT * u) * SL * 8, 0, 0));
     // the candidates published, t* = the largest t_w of the chunks that did not
-    // overflow, the largest key of the row, the overflows; bm[w] flags an overflowed
-    // chunk for the rare path
+    // overflow, the largest key of the row, the overflows; bm[w] keeps chunk w's t_w
+    // (every key >= it is published) or ~0 for an overflowed chunk, for the rare path
     uint32_t t4[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < 4; u++) {
@@ -1581,7 +1639,7 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
         if (!ov) t4[1] = max(t4[1], tw);
         t4[2] = max(t4[2], cmax);
         t4[3] += ov ? 1u : 0u;
-        bm[w] = ov ? 0xFFFFFFFFu : 0u;
+        bm[w] = ov ? 0xFFFFFFFFu : tw;
       }
     }
     block_sum_max_max_sum(t4, misc);
@@ -1604,8 +1662,19 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
         done = select_cand<FIN_ENT / NT>(cand, E, lo, hi, k, hist, misc, out, &got);
         if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
       }
-      if (!done && nr <= BITMAP_KEYS)
-        done = rare_select(ws, nr, k, wact, E, C, lo, hi, rs, cand, bm, hist, misc, out);
+      if (!done && nr <= BITMAP_KEYS) {
+        uint32_t glo = lo;
+        if (E < k) {
+          // fewer than k keys >= t*: every published key instead, chunk w held from its own t_w
+          glo = 0x00800000u;
+          E = 0;
+          for (int b0 = 0; b0 < wact; b0 += per_batch) {
+            issue(b0);
+            E += gather_place(e, glo, E, cand, misc);
+          }
+        }
+        done = rare_select(ws, nr, k, wact, E, C, glo, hi, rs, cand, bm, hist, misc, out);
+      }
     }
   }
   if (!done) {

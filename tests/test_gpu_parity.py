@@ -43,6 +43,16 @@ def test_candidate_path(n, k):
     check_against_oracle(prob, run_all(prob))
 
 
+@pytest.mark.parametrize("n,rows,keys", [(262144, 4, "normal"), (524287, 1, "normal"), (262144, 2, "recent"),
+                                         (300001, 3, "ties")])
+def test_rows_past_128k(n, rows, keys):
+    """Rows of 2-4x the 128K keys (512 to 1,024 chunks): the candidate gather runs in several
+    batches; recent keys and ties at this length take the multi-pass select over memory."""
+    prob = make_problem([n], [rows], seed=6000 + n + rows, keys=keys, recent=4096, name=f"long{n}x{rows}{keys}")
+    print(f"case n={n} rows={rows} keys={keys}", flush=True)
+    check_against_oracle(prob, run_all(prob))
+
+
 def test_mixed_requests_with_bounds():
     prob = make_problem([700, 5000, 30000, 50000, 3], [4, 1, 3, 2, 1], seed=77, name="mixed5")
     bounds = [int(prob.n_keys[a:b].max()) for a, b in zip(prob.req_indptr[:-1], prob.req_indptr[1:])]
