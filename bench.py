@@ -10,9 +10,11 @@ page permutation, k = 2048.  Inputs are synthetic and resident in HBM before the
 region; the steps rotate over several copies of the key cache (32 by default, over 512
 MiB) so that keys come from HBM rather than the 256 MiB last-level cache.
 
-Prints one JSON line.  "roofline" is for the call (both launches: the scoring launch
-dominates); its duration is the HIP-event time of the timed steps on the launch stream
-divided by the step count.  "roofline_score_kernel" times idx_score (the scoring launch
+Prints one JSON line.  The steps are timed twice with HIP events: back to back on the
+stream, and as replays of a hipGraph of captured calls (exactly the same number of
+calls, no host launch cost between them).  The graph figure is the reported one; the
+stream figure is kept under "timing".  "roofline" is for the call (both launches: the
+scoring launch dominates); "roofline_score_kernel" times idx_score (the scoring launch
 alone) the same way.  The CPU baseline is the oracle as it stands, timed on the host
 over the same workload.
 """
@@ -122,20 +124,21 @@ def main():
     sptr, lptr = ctypes.c_void_p(scores.data_ptr()), ctypes.c_void_p(lists.data_ptr())
     wsp = ctypes.c_void_p(ws.ptr)
 
-    def step(i):
+    def step(i, st=sp):
         s, _ = structs[i % copies]
         rc = L.idx_score_topk(ctypes.byref(s), prob.k, sptr, scores.shape[1], lptr, wsp, ws.nbytes,
-                              ctypes.c_void_p(sp))
+                              ctypes.c_void_p(st))
         if rc:
             raise idx.IdxError(rc, "idx_score_topk")
 
-    def score_only(i):
+    def score_only(i, st=sp):
         s, _ = structs[i % copies]
-        rc = L.idx_score(ctypes.byref(s), sptr, scores.shape[1], wsp, ws.nbytes, ctypes.c_void_p(sp))
+        rc = L.idx_score(ctypes.byref(s), sptr, scores.shape[1], wsp, ws.nbytes, ctypes.c_void_p(st))
         if rc:
             raise idx.IdxError(rc, "idx_score")
 
     def timed(fn):
+        """Back-to-back calls on the stream: HIP events around exactly `steps` calls."""
         for i in range(args.warmup):
             fn(i)
         torch.cuda.synchronize()
@@ -149,8 +152,43 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps, time.perf_counter() - t0
 
-    ms_score, _ = timed(score_only)
-    ms_per_step, wall = timed(step)
+    # a hipGraph of `calls` calls (a divisor of the step count, at most 64; call i uses key
+    # copy i mod copies), replayed steps / calls times: exactly `steps` calls, no host
+    # launch cost between them
+    calls = max(d for d in range(1, min(64, args.steps) + 1) if args.steps % d == 0)
+
+    def graph_timed(fn):
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cs):
+            for i in range(calls):
+                fn(i, cs.cuda_stream)
+        torch.cuda.synchronize()
+        g.replay()                                   # warm replay
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for _ in range(args.steps // calls):
+            g.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        del g
+        return ms
+
+    ms_score_stream, _ = timed(score_only)
+    ms_stream, wall = timed(step)
+    graph_error = None
+    try:
+        ms_score = graph_timed(score_only)
+        ms_per_step = graph_timed(step)
+        mode = "hipGraph replay"
+    except Exception as exc:                          # report the stream timing instead
+        graph_error = f"{type(exc).__name__}: {exc}"
+        ms_score, ms_per_step, mode = ms_score_stream, ms_stream, "stream"
     code, detail = idx.device_status(ws)
     if code != 0:
         raise RuntimeError(f"device error {detail:#x}")
@@ -207,7 +245,10 @@ def main():
                          "frac": bytes_rate / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": abytes},
         "roofline_fp8_context": {"achieved": flops_rate, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                                  "frac": flops_rate / FP8_PEAK_TFLOPS},
-        "host_wall_s": wall,
+        "timing": {"mode": mode, "graph_calls_per_replay": calls if mode != "stream" else None,
+                   "replays": args.steps // calls if mode != "stream" else None,
+                   "stream_us_per_call": ms_stream * 1e3, "stream_us_per_score_launch": ms_score_stream * 1e3,
+                   "stream_host_wall_s": wall, "graph_error": graph_error},
         "kernel_source_sha256_16": khash,
     }
 

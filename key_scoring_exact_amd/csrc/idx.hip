@@ -1735,9 +1735,14 @@ struct WsLayout {
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
+// The block area holds, per row, one block per chunk of any call of up to max_keys
+// keys: plan_score gives at most min(256, pages) chunks while it uses fewer than 8 pages a
+// chunk and ceil(pages / 8) beyond, plan_topk ceil(pages / 8); both bounds grow with
+// max_keys, so a workspace sized for max_keys serves every smaller call.
 WsLayout layout_for(int rows, int max_keys) {
-  const Plan a = plan_score(max_keys), b = plan_topk(max_keys);
-  const int stride = (a.wg > b.wg ? a.wg : b.wg);
+  const int pages = pages_for(max_keys) > 0 ? pages_for(max_keys) : 1;
+  const int lo = pages < 256 ? pages : 256, hi = (pages + PMAX - 1) / PMAX;
+  const int stride = lo > hi ? lo : hi;
   WsLayout L;
   L.ent_stride = stride < 4 * NT ? stride : 4 * NT;     // rows with more chunks never publish
   L.off_ent = WS_HDR;

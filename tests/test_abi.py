@@ -73,6 +73,26 @@ def test_workspace_bytes(L):
     assert L.idx_workspace_bytes(1, 10, 8, None) == _lib.IDX_EINVAL
 
 
+def test_workspace_bytes_monotone(L):
+    """A workspace sized for (rows, max_keys) serves every call with fewer rows or keys:
+    a call checks its workspace against idx_workspace_bytes of its own shape, and the
+    size never decreases in either argument (the chunk plan of a smaller key count can
+    use more, smaller chunks)."""
+    out = ctypes.c_size_t(0)
+    for rows in (1, 4, 16):
+        prev = 0
+        for m in list(range(0, 140000, 257)) + [262143, 300000, 524287, 1 << 20]:
+            assert L.idx_workspace_bytes(rows, m, 2048, ctypes.byref(out)) == 0
+            assert out.value >= prev, (rows, m)
+            prev = out.value
+    for m in (0, 30000, 40000, 131072):
+        sizes = []
+        for rows in (1, 2, 4, 8, 64):
+            assert L.idx_workspace_bytes(rows, m, 2048, ctypes.byref(out)) == 0
+            sizes.append(out.value)
+        assert sizes == sorted(sizes), m
+
+
 FAKE = 0x10000000  # an aligned address that validation never dereferences
 
 
