@@ -434,6 +434,20 @@ __device__ __forceinline__ bool kth_select(const uint32_t (&kr)[SMAX], int S, in
     const uint32_t d = (uint32_t)misc[8];
     const int r = misc[9];
     const int c = misc[10];
+    if (c == 1) {
+      // bin d holds one key, the k-th: every key above it and it are in (r == 1)
+#pragma unroll
+      for (int g = 0; g < SMAX / 4; g++) {
+        if (g * 4 >= S) break;
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++)
+          if (idx[g * 4 + jj] == d) misc[12] = (int)kr[g * 4 + jj];
+      }
+      __syncthreads();
+      *Tge_out = (uint32_t)misc[12];
+      *rem_out = 0;
+      return true;
+    }
     if (c <= 64) {
       // the c keys of bin d into a list (the dummy words of the second buffer), then the
       // r-th largest of them on wave 0
@@ -564,13 +578,12 @@ __device__ __forceinline__ bool kth_select(const uint32_t (&kr)[SMAX], int S, in
 // Emission of the top k in segment order (thread t's slots j < S precede thread t + 1's;
 // the caller lays positions out ascending in that order; absent slots hold key 0): a
 // key is selected when key >= Tge, or, when rem > 0, key == Tge - 1 and it is among
-// the first rem such keys.  The selected positions pr[j] are staged in LDS (stage:
-// k words, free for this use) and copied to out[0 .. k) with coalesced stores.  Returns
-// the number selected.  Every thread must call.
+// the first rem such keys.  Each thread stores its selected positions pr[j] straight
+// to their ranks in out[0 .. k) (a contiguous run a thread, the runs in thread order).
+// Returns the number selected.  Every thread must call.
 template <int SMAX>
 __device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], const uint32_t (&pr)[SMAX], int S,
-                                             uint32_t Tge, int rem, int32_t* out, int k, int* misc,
-                                             uint32_t* stage) {
+                                             uint32_t Tge, int rem, int32_t* out, int k, int* misc) {
   const uint32_t T = Tge - 1u;
   int gt = 0, eq = 0;
 #pragma unroll
@@ -598,7 +611,7 @@ __device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], const u
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
         const bool sel = kr[g * 4 + jj] >= Tge;
-        if (sel && o < k) stage[o] = pr[g * 4 + jj];
+        if (sel && o < k) out[o] = (int32_t)pr[g * 4 + jj];
         o += sel ? 1 : 0;
       }
     }
@@ -614,27 +627,13 @@ __device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], const u
         const bool e = key == T;
         const bool sel = key >= Tge || (e && er < rem);
         er += e ? 1 : 0;
-        if (sel && o < k) stage[o] = pr[g * 4 + jj];
+        if (sel && o < k) out[o] = (int32_t)pr[g * 4 + jj];
         o += sel ? 1 : 0;
       }
     }
   }
-  __syncthreads();
   const int tg = tot & 0xFFFF, te = tot >> 16;
   const int got = tg + (te < rem ? te : rem);
-  const int ne = got < k ? got : k;
-  if ((reinterpret_cast<uintptr_t>(out) & 15) == 0) {
-    for (int q = threadIdx.x; 4 * q < ne; q += NT) {
-      if (4 * q + 4 <= ne) {
-        *reinterpret_cast<v4u*>(out + 4 * q) = *reinterpret_cast<const v4u*>(stage + 4 * q);
-      } else {
-        for (int j = 0; j < 4; j++)
-          if (4 * q + j < ne) out[4 * q + j] = (int32_t)stage[4 * q + j];
-      }
-    }
-  } else {
-    for (int p = threadIdx.x; p < ne; p += NT) out[p] = (int32_t)stage[p];
-  }
   return got;
 }
 
@@ -842,6 +841,55 @@ __device__ inline void candidate_params(int n, int C, int k, int* m, int* cap, i
   *m = mm;
   *cap = 32 * G - 2;
   *groups = G;
+}
+
+// A chunk's local threshold from one histogram, with no bisection: the 512 scores of a
+// full chunk (8 a lane, fv / their radix keys kr, every key present) are counted into
+// 128 bins linear in the score over [smallest lane maximum, largest score], which holds
+// at least the 64 lane maxima, so at least m keys (m <= 64).  Bin b* is the first, from
+// the top, whose running count reaches m.  The bin index is a monotone function of the
+// score, so the keys of bins <= b* are exactly the keys >= the smallest of them, which
+// becomes t.  Returns false (the caller bisects instead) when the chunk is partial, all
+// lane maxima are equal, the span is not finite, or more than cap keys would publish.
+// hst: 128 words of LDS owned by this wave.  All 64 lanes must call.
+__device__ __forceinline__ bool chunk_bound_linear(const float (&fv)[8], const uint32_t (&kr)[8], uint32_t lmax,
+                                                   uint32_t cmax, int m, int cap, uint32_t* hst, uint32_t* t) {
+  const int lane = lane_id();
+  if (__ballot(lmax == 0u) != 0ull) return false;
+  const uint32_t lmin = wave_min_u32(lmax);
+  if (lmin == cmax) return false;
+  const float hf = key_float(cmax), lf = key_float(lmin);
+  const float span = hf - lf;
+  const float scale = 128.0f / span;
+  if (!(span <= 3.0e38f) || !(scale <= 3.0e38f)) return false;
+  reinterpret_cast<uint64_t*>(hst)[lane] = 0ull;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint32_t bn[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    bn[j] = (kr[j] != 0u && fv[j] >= lf) ? min(__float2uint_rz((hf - fv[j]) * scale), 127u) : 128u;
+    if (bn[j] < 128u) atomicAdd(&hst[bn[j]], 1u);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t h2 = reinterpret_cast<const uint64_t*>(hst)[lane];   // bins 2 lane, 2 lane + 1
+  const int c0 = (int)(uint32_t)h2, c1 = (int)(uint32_t)(h2 >> 32);
+  const int incl = wave_incl_scan(c0 + c1);                            // keys in bins <= 2 lane + 1
+  const uint64_t r1 = __ballot(incl >= m);
+  if (r1 == 0ull) return false;
+  const int f = __ffsll((unsigned long long)r1) - 1;
+  const bool first = ((__ballot(incl - c1 >= m) >> f) & 1ull) != 0ull;
+  const uint32_t bstar = 2u * (uint32_t)f + (first ? 0u : 1u);
+  const int count = __builtin_amdgcn_readlane(first ? incl - c1 : incl, f);
+  if (count > cap) return false;
+  uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < 8; j++) mn = bn[j] <= bstar ? min(mn, kr[j]) : mn;
+  *t = wave_min_u32(mn);
+  return true;
 }
 
 // Whether any / every thread of the workgroup holds p (misc[48 .. 56) as scratch).
@@ -1173,7 +1221,7 @@ __device__ __forceinline__ bool select_cand(uint64_t* cand, int E, uint32_t lo, 
   uint32_t Tge;
   int rem;
   if (!kth_select<SMAX>(kr, S, E, lo, hi, k, hist, misc, &Tge, &rem)) return false;
-  *got = emit_segments<SMAX>(kr, pr, S, Tge, rem, out, k, misc, reinterpret_cast<uint32_t*>(cand));
+  *got = emit_segments<SMAX>(kr, pr, S, Tge, rem, out, k, misc);
   return true;
 }
 
@@ -1198,7 +1246,7 @@ __device__ __forceinline__ bool select_all(uint32_t* fk, int n, uint32_t lo, uin
   uint32_t Tge;
   int rem;
   if (!kth_select<SMAX>(kr, S, n, lo, hi, k, hist, misc, &Tge, &rem)) return false;
-  *got = emit_segments<SMAX>(kr, pr, S, Tge, rem, out, k, misc, fk);
+  *got = emit_segments<SMAX>(kr, pr, S, Tge, rem, out, k, misc);
   return true;
 }
 
@@ -1470,27 +1518,31 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
         lmax = lmax > key[j] ? lmax : key[j];
       }
       const uint32_t cmax = wave_max_u32(lmax);
-      const uint32_t thr0 = wave_kth_bound(lmax, m, wave_min_u32(lmax), cmax, 12);
-      int cnt0 = 0;
+      uint32_t thr;
+      // the queries are in registers: their LDS area holds each wave's scratch
+      if (!chunk_bound_linear(fv, key, lmax, cmax, m, cap, LDS_PTR(uint32_t, L_Q) + 1024 + i * 128, &thr)) {
+        const uint32_t thr0 = wave_kth_bound(lmax, m, wave_min_u32(lmax), cmax, 12);
+        int cnt0 = 0;
 #pragma unroll
-      for (int j = 0; j < 8; j++) cnt0 += (key[j] != 0u && key[j] >= thr0) ? 1 : 0;
-      const int incl0 = wave_incl_scan(cnt0);
-      const int total0 = __builtin_amdgcn_readlane(incl0, 63);
-      uint32_t thr = thr0;
-      if (total0 <= 64) {
-        uint32_t* kst = LDS_PTR(uint32_t, L_Q) + i * 64;   // the queries are in registers
-        int o = incl0 - cnt0;
+        for (int j = 0; j < 8; j++) cnt0 += (key[j] != 0u && key[j] >= thr0) ? 1 : 0;
+        const int incl0 = wave_incl_scan(cnt0);
+        const int total0 = __builtin_amdgcn_readlane(incl0, 63);
+        thr = thr0;
+        if (total0 <= 64) {
+          uint32_t* kst = LDS_PTR(uint32_t, L_Q) + i * 64;
+          int o = incl0 - cnt0;
 #pragma unroll
-        for (int j = 0; j < 8; j++)
-          if (key[j] != 0u && key[j] >= thr0) {
-            kst[o] = key[j];
-            o++;
-          }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const uint32_t v = lane < total0 ? kst[lane] : 0u;
-        thr = wave_kth_bound(v, m, thr0, cmax, 8);
+          for (int j = 0; j < 8; j++)
+            if (key[j] != 0u && key[j] >= thr0) {
+              kst[o] = key[j];
+              o++;
+            }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const uint32_t v = lane < total0 ? kst[lane] : 0u;
+          thr = wave_kth_bound(v, m, thr0, cmax, 8);
+        }
       }
       int cnt = 0;
 #pragma unroll
@@ -1611,19 +1663,19 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
     candidate_params(nr, C, k, &m_unused, &cap, &G);
     const int SL = 32 * G;                           // slots a chunk
     __amdgpu_buffer_rsrc_t rent = make_rsrc(erow, (int64_t)wact * SL * 8);
-    // the first gather batch and the chunk headers with their maxima (thread t: chunks
-    // t + NT u; past wact outside the buffer resource) in flight together
+    // the chunk headers with their maxima (thread t: chunks t + NT u; past wact outside
+    // the buffer resource), then the first gather batch, in flight together
     uint64_t e[2 * GQ];
     auto issue = [&](int b0) {
       if (G == 1) gather_issue<1>(rent, wact, b0, e);
       else if (G == 2) gather_issue<2>(rent, wact, b0, e);
       else gather_issue<4>(rent, wact, b0, e);
     };
-    issue(0);
     v4u hv[4];
 #pragma unroll
     for (int u = 0; u < 4; u++)
       hv[u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rent, (tid + NT * u) * SL * 8, 0, 0));
+    issue(0);                                        // after the headers: their reduction overlaps it
     // the candidates published, t* = the largest t_w of the chunks that did not
     // overflow, the largest key of the row, the overflows; bm[w] keeps chunk w's t_w
     // (every key >= it is published) or ~0 for an overflowed chunk, for the rare path
