@@ -58,7 +58,7 @@ extern "C" {
 /* Return codes. */
 #define IDX_OK 0
 #define IDX_EINVAL 1       /* null pointer, bad size/stride/alignment, k out of [1, IDX_KMAX], bad req_indptr */
-#define IDX_EUNSUPPORTED 2 /* heads/dim/page size not the compiled ones, > IDX_GROUP_ROWS rows in a request, > IDX_MAX_REQ requests */
+#define IDX_EUNSUPPORTED 2 /* heads/dim/page size not the compiled ones, > IDX_MAX_REQ row groups */
 #define IDX_EWORKSPACE 3   /* workspace null or smaller than idx_workspace_bytes() */
 #define IDX_EHIP 4         /* a HIP runtime call or launch failed; see idx_last_hip_error() */
 #define IDX_EDEVICE 5      /* a sticky device-side error was found by idx_device_status() */
@@ -71,10 +71,12 @@ extern "C" {
 
 typedef struct idx_problem {
   int32_t rows;              /* R >= 1 step rows */
-  int32_t num_req;           /* 1 <= num_req <= IDX_MAX_REQ */
+  int32_t num_req;           /* 1 <= num_req; their row groups (below) at most IDX_MAX_REQ */
   const int32_t* req_indptr; /* HOST [num_req + 1]: request j owns rows [req_indptr[j], req_indptr[j+1]);
-                                req_indptr[0] = 0, strictly increasing, req_indptr[num_req] = rows,
-                                at most IDX_GROUP_ROWS rows per request */
+                                req_indptr[0] = 0, strictly increasing, req_indptr[num_req] = rows.
+                                A request's rows are scored in groups of at most IDX_GROUP_ROWS
+                                consecutive rows, each group reading the request's keys once;
+                                at most IDX_MAX_REQ groups in all (sum of ceil(rows_j / 4)) */
   int32_t heads;             /* must be IDX_HEADS */
   int32_t dim;               /* must be IDX_DIM */
   int32_t page_size;         /* must be IDX_PAGE_SIZE */

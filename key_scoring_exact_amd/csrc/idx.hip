@@ -1813,10 +1813,12 @@ int validate_problem(const idx_problem* p) {
   if (p->num_req > IDX_MAX_REQ) return IDX_EUNSUPPORTED;
   if (p->rows > (1 << 24) - 1) return IDX_EUNSUPPORTED;
   if (p->req_indptr[0] != 0 || p->req_indptr[p->num_req] != p->rows) return IDX_EINVAL;
+  int groups = 0;
   for (int j = 0; j < p->num_req; j++) {
     const int32_t r = p->req_indptr[j + 1] - p->req_indptr[j];
     if (r < 1) return IDX_EINVAL;
-    if (r > IDX_GROUP_ROWS) return IDX_EUNSUPPORTED;
+    groups += (r + IDX_GROUP_ROWS - 1) / IDX_GROUP_ROWS;
+    if (groups > IDX_MAX_REQ) return IDX_EUNSUPPORTED;
   }
   if (p->num_pages < 1 || p->max_pages < 1 || p->max_keys < 0) return IDX_EINVAL;
   if (p->req_max_keys)
@@ -1910,12 +1912,19 @@ int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int3
   args.chunk_shift = 31 - __builtin_clz((unsigned)pl.chunk);
   args.mode = select ? (MODE_SCORE | MODE_PUBLISH) : MODE_SCORE;
   fill_common(args, L, ws);
+  // a request of more than IDX_GROUP_ROWS rows is scored as consecutive groups of at
+  // most IDX_GROUP_ROWS of its rows; each group walks the request's pages once
+  int groups = 0;
   for (int j = 0; j < p->num_req; j++) {
-    args.grp[j] = (uint32_t)p->req_indptr[j] | ((uint32_t)(p->req_indptr[j + 1] - p->req_indptr[j]) << 24);
     const int bound = p->req_max_keys ? p->req_max_keys[j] : p->max_keys;
-    args.gmax[j] = bound;
+    for (int r0 = p->req_indptr[j]; r0 < p->req_indptr[j + 1]; r0 += IDX_GROUP_ROWS) {
+      const int rn = p->req_indptr[j + 1] - r0 < IDX_GROUP_ROWS ? p->req_indptr[j + 1] - r0 : IDX_GROUP_ROWS;
+      args.grp[groups] = (uint32_t)r0 | ((uint32_t)rn << 24);
+      args.gmax[groups] = bound;
+      groups++;
+    }
   }
-  return launch(args, pl.pages_per_wg, dim3(pl.wg, p->num_req), true, select, static_cast<hipStream_t>(stream));
+  return launch(args, pl.pages_per_wg, dim3(pl.wg, groups), true, select, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace

@@ -148,11 +148,18 @@ def test_problem_validation(L, field, value, code):
 def test_req_indptr_validation(L):
     for vals, code in [((0, 4, 5), _lib.IDX_EINVAL),      # last != rows
                        ((1, 4, 6), _lib.IDX_EINVAL),      # first != 0
-                       ((0, 0, 6), _lib.IDX_EINVAL),      # empty request
-                       ((0, 1, 6), _lib.IDX_EUNSUPPORTED)]:  # 5 rows in a request
+                       ((0, 0, 6), _lib.IDX_EINVAL)]:     # empty request
         ip = (ctypes.c_int32 * 3)(*vals)
         p, keep = make_problem(req_indptr=ctypes.cast(ip, ctypes.POINTER(ctypes.c_int32)))
         assert call_all(L, p) == (code, code), vals
+    # a request of more than IDX_GROUP_ROWS rows is split into row groups; more than
+    # IDX_MAX_REQ groups in all is refused (1,025 rows in one request: 257 groups; 2 x 512
+    # rows: exactly 256)
+    for rows, ptr, code in [(1025, (0, 1025), _lib.IDX_EUNSUPPORTED), (1025, (0, 1, 1025), _lib.IDX_EUNSUPPORTED)]:
+        ip = (ctypes.c_int32 * len(ptr))(*ptr)
+        p, keep = make_problem(rows=rows, num_req=len(ptr) - 1,
+                               req_indptr=ctypes.cast(ip, ctypes.POINTER(ctypes.c_int32)))
+        assert call_all(L, p) == (code, code), ptr
     p, keep = make_problem(req_indptr=None)
     assert call_all(L, p) == (_lib.IDX_EINVAL, _lib.IDX_EINVAL)
     rm = (ctypes.c_int32 * 2)(3200, 3201)                  # a request bound above max_keys

@@ -125,3 +125,18 @@ def test_stale_workspace_contents_are_ignored():
         body.copy_(torch.randint(0, 256, body.shape, dtype=torch.uint8, device="cuda", generator=gen))
         res = run_all(prob, ws=ws)
         check_against_oracle(prob, res)
+
+
+@pytest.mark.parametrize("rows,n", [(5, 3000), (8, 9000), (8, 40000), (6, 131072)])
+def test_long_verify_chains(rows, n):
+    """More than four verify rows in a request: the rows are scored in groups of at most
+    four over the request's pages (each group walks the pages once)."""
+    prob = make_problem([n], [rows], seed=8000 + n + rows, name=f"chain{rows}x{n}")
+    print(f"case rows={rows} n={n}", flush=True)
+    check_against_oracle(prob, run_all(prob))
+
+
+def test_mixed_requests_with_long_chains():
+    prob = make_problem([9000, 1500, 30000], [8, 1, 5], seed=88, name="mixed_long")
+    bounds = [int(prob.n_keys[a:b].max()) for a, b in zip(prob.req_indptr[:-1], prob.req_indptr[1:])]
+    check_against_oracle(prob, run_all(prob, req_max_keys=bounds))
