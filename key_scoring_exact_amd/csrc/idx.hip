@@ -1148,7 +1148,8 @@ __device__ __forceinline__ void gather_issue(__amdgpu_buffer_rsrc_t rent, int wa
 // (within a load the lanes run in slot and chunk order, two slots a lane): a ballot per
 // load and slot parity ranks the kept slots within the wave, the wave totals place the
 // waves.  Dropped slots write to the 64 dummy entries past FIN_ENT.  Returns the
-// batch's kept count.  Every thread must call.
+// batch's kept count, or -1 (writing nothing) when E0 plus that count would pass
+// FIN_ENT.  Every thread must call.
 __device__ __forceinline__ int gather_place(const uint64_t (&e)[2 * GQ], uint32_t lo, int E0, uint64_t* cand, int* misc) {
   const int lane = lane_id(), wv = wave_id();
   int o = 0;
@@ -1176,6 +1177,7 @@ __device__ __forceinline__ int gather_place(const uint64_t (&e)[2 * GQ], uint32_
     tot += t[i];
   }
   __syncthreads();
+  if (E0 + tot > FIN_ENT) return -1;                 // would not fit: nothing written
   const int base = E0 + before;
   const int dummy = FIN_ENT + lane;
 #pragma unroll
@@ -1700,13 +1702,21 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
     // gathered.  (0x00800000 is the smallest key of a finite score.)
     const uint32_t lo = t4[1] > 0x00800000u ? t4[1] : 0x00800000u;
     const uint32_t hi = t4[2] > lo ? t4[2] : lo;
-    if ((int)t4[0] <= FIN_ENT) {
-      int E = 0;
-      const int per_batch = batch_chunks(G);
-      for (int b0 = 0; b0 < wact; b0 += per_batch) {
-        if (b0 > 0) issue(b0);
-        E += gather_place(e, lo, E, cand, misc);
+    // the keys >= t* (not every published key: from about 1,024 chunks a row, the
+    // published keys can pass the LDS capacity while those >= t* fit)
+    int E = 0;
+    bool fits = true;
+    const int per_batch = batch_chunks(G);
+    for (int b0 = 0; b0 < wact; b0 += per_batch) {
+      if (b0 > 0) issue(b0);
+      const int got = gather_place(e, lo, E, cand, misc);
+      if (got < 0) {
+        fits = false;
+        break;
       }
+      E += got;
+    }
+    if (fits) {
       pad_cand(cand, E);
       __syncthreads();
       if (t4[3] == 0u) {
@@ -1714,7 +1724,7 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
         done = select_cand<FIN_ENT / NT>(cand, E, lo, hi, k, hist, misc, out, &got);
         if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
       }
-      if (!done && nr <= BITMAP_KEYS) {
+      if (!done && nr <= BITMAP_KEYS && (E >= k || (int)t4[0] <= FIN_ENT)) {
         uint32_t glo = lo;
         if (E < k) {
           // fewer than k keys >= t*: every published key instead, chunk w held from its own t_w

@@ -43,8 +43,8 @@ def test_candidate_path(n, k):
     check_against_oracle(prob, run_all(prob))
 
 
-@pytest.mark.parametrize("n,rows,keys", [(262144, 4, "normal"), (524287, 1, "normal"), (262144, 2, "recent"),
-                                         (300001, 3, "ties")])
+@pytest.mark.parametrize("n,rows,keys", [(262144, 4, "normal"), (524287, 1, "normal"), (524288, 4, "normal"),
+                                         (262144, 2, "recent"), (300001, 3, "ties")])
 def test_rows_past_128k(n, rows, keys):
     """Rows of 2-4x the 128K keys (512 to 1,024 chunks): the candidate gather runs in several
     batches; recent keys and ties at this length take the multi-pass select over memory."""
