@@ -3,4 +3,4 @@
 Only tests, the smoke check and the benchmark's CPU baseline may use this
 package; the GPU library neither imports nor links it.
 """
-from . import indexer, check  # noqa: F401
+from . import indexer, check, prep  # noqa: F401
