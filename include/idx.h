@@ -130,6 +130,24 @@ int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys,
 int idx_score_topk(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores,
                    int32_t* topk, void* ws, size_t ws_bytes, void* stream);
 
+/* Index-query preparation (the GLM-5.3 indexer page, Modifications item 2, "the query
+ * once a row": each row's index query is roped and Hadamard-transformed once and
+ * published in bf16; Modifications item 0: that transform runs in f32, then rounds to
+ * bf16).  For every row r and head h, with x = q_pre[r][h][:] (bf16 [rows][64][128]):
+ *   1. RoPE on dimensions [0, rope_dim): pair i < rope_dim / 2 is (i, i + rope_dim / 2)
+ *      (interleaved = 0) or (2 i, 2 i + 1) (interleaved = 1); its values (a, b) become
+ *      (a c - b s, a s + b c) with c = cos_tab[r][i], s = sin_tab[r][i] (f32
+ *      [rows][rope_dim / 2], the caller's rotation table for the row's position).
+ *      Dimensions >= rope_dim pass through.
+ *   2. The Hadamard transform: y = H x / sqrt(128), H the Sylvester Hadamard matrix,
+ *      H[i][j] = (-1)^popcount(i & j).
+ * q_out[r][h][:] = y rounded to bf16 (nearest, ties to even), computed in f32.  All
+ * pointers are device pointers, 4-byte aligned; q_out must not overlap q_pre.
+ * rope_dim is even in [0, 128] (cos_tab / sin_tab may be NULL when it is 0).  One
+ * launch on `stream`.  Returns IDX_OK, IDX_EINVAL or IDX_EHIP. */
+int idx_prep_query(const void* q_pre, const float* cos_tab, const float* sin_tab, int32_t rows,
+                   int32_t rope_dim, int32_t interleaved, void* q_out, void* stream);
+
 /* Synchronise `stream`, read and clear the workspace's sticky device error.
  * Returns IDX_OK, IDX_EDEVICE (with *detail = IDX_DERR_* bits when detail is
  * not NULL), or IDX_EHIP. */

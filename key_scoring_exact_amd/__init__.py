@@ -177,6 +177,25 @@ def topk(scores: torch.Tensor, n_keys: torch.Tensor, k: int, max_keys: int, ws: 
     return out
 
 
+def prep_query(q_pre: torch.Tensor, cos: Optional[torch.Tensor], sin: Optional[torch.Tensor], rope_dim: int,
+               interleaved: bool = False, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The prepared index query, bf16 [rows, 64, 128]: RoPE on the first rope_dim dims of
+    every head from the per-row table cos / sin f32 [rows, rope_dim / 2] (half-split or
+    interleaved pairs), then the orthonormal Hadamard transform; f32 arithmetic, bf16 out."""
+    rows = int(q_pre.shape[0])
+    if out is None:
+        out = torch.empty_like(q_pre)
+    cp = ctypes.c_void_p(_ptr(cos, torch.float32)) if rope_dim > 0 else None
+    sp = ctypes.c_void_p(_ptr(sin, torch.float32)) if rope_dim > 0 else None
+    if tuple(q_pre.shape[1:]) != (IDX_HEADS, IDX_DIM) or out.shape != q_pre.shape:
+        raise ValueError("expected q_pre and out of shape [rows, 64, 128]")
+    bf = (torch.bfloat16, torch.int16)
+    _check(lib().idx_prep_query(ctypes.c_void_p(_ptr(q_pre, bf)), cp, sp, rows, int(rope_dim),
+                                1 if interleaved else 0, ctypes.c_void_p(_ptr(out, bf)),
+                                ctypes.c_void_p(_stream(stream))), "idx_prep_query")
+    return out
+
+
 def device_status(ws: Workspace, stream=None):
     """(code, detail bits): synchronises the stream, reads and clears the sticky error."""
     detail = ctypes.c_uint32(0)

@@ -1746,6 +1746,71 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Index-query preparation: one wave per (row, head), lane l holding dimensions 2 l and
+// 2 l + 1 in f32.  RoPE reads each pair's partner through LDS, then the Hadamard
+// transform runs as 7 butterfly stages (stride 1 within a lane, strides 2 .. 64 across
+// lanes l and l ^ (stride / 2)), then a scale by 1/sqrt(128) and a round to bf16.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);   // finite inputs
+}
+
+constexpr int PREP_WAVES = 4;   // waves (row, head pairs) a workgroup
+
+__global__ __launch_bounds__(64 * PREP_WAVES) void prep_query_kernel(const uint32_t* qp, const float* cs, const float* sn,
+                                                                     uint32_t* qo, int rows, int rope_dim,
+                                                                     int interleaved) {
+  __shared__ float buf[PREP_WAVES][D];
+  const int lane = threadIdx.x & 63;
+  const int wl = threadIdx.x >> 6;
+  const int64_t task = (int64_t)blockIdx.x * PREP_WAVES + wl;        // row * H + head
+  if (task >= (int64_t)rows * H) return;
+  const int r = (int)(task / H);
+  const uint32_t two = qp[task * (D / 2) + lane];                      // bf16 dims 2 l, 2 l + 1
+  float v[2] = {__uint_as_float(two << 16), __uint_as_float(two & 0xFFFF0000u)};
+  float* b = buf[wl];
+  b[2 * lane] = v[0];
+  b[2 * lane + 1] = v[1];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int half = rope_dim >> 1;
+#pragma unroll
+  for (int e = 0; e < 2; e++) {
+    const int d = 2 * lane + e;
+    if (d < rope_dim) {
+      int i, partner;
+      bool first;
+      if (interleaved) {
+        i = d >> 1;
+        partner = d ^ 1;
+        first = (d & 1) == 0;
+      } else {
+        first = d < half;
+        i = first ? d : d - half;
+        partner = first ? d + half : d - half;
+      }
+      const float c = cs[(int64_t)r * half + i], s = sn[(int64_t)r * half + i];
+      const float x = b[d], y = b[partner];
+      // the pair (a, b) becomes (a c - b s, a s + b c)
+      v[e] = first ? fmaf(x, c, -(y * s)) : fmaf(y, s, x * c);
+    }
+  }
+  float a0 = v[0] + v[1], a1 = v[0] - v[1];                            // stride 1
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {                                   // stride 2 m
+    const float p0 = __shfl_xor(a0, m), p1 = __shfl_xor(a1, m);
+    const bool hi = (lane & m) != 0;
+    a0 = hi ? p0 - a0 : a0 + p0;
+    a1 = hi ? p1 - a1 : a1 + p1;
+  }
+  constexpr float inv_sqrt_d = 0.08838834764831845f;                   // 1 / sqrt(128)
+  qo[task * (D / 2) + lane] =
+      (uint32_t)f32_to_bf16_rne(a0 * inv_sqrt_d) | ((uint32_t)f32_to_bf16_rne(a1 * inv_sqrt_d) << 16);
+}
+
 __global__ void fill_kernel(uint32_t* p, int64_t words, uint32_t magic) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < words) p[i] = (i == 0) ? magic : 0u;
@@ -2010,6 +2075,23 @@ int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys, int3
     if (rc) return rc;
   }
   return IDX_OK;
+}
+
+int idx_prep_query(const void* q_pre, const float* cos_tab, const float* sin_tab, int32_t rows, int32_t rope_dim,
+                   int32_t interleaved, void* q_out, void* stream) {
+  if (!q_pre || !q_out || rows < 1 || rows > (1 << 24) - 1) return IDX_EINVAL;
+  if (rope_dim < 0 || rope_dim > IDX_DIM || (rope_dim & 1) || (interleaved != 0 && interleaved != 1)) return IDX_EINVAL;
+  if (rope_dim > 0 && (!cos_tab || !sin_tab)) return IDX_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(q_pre) & 3) || (reinterpret_cast<uintptr_t>(q_out) & 3) ||
+      (reinterpret_cast<uintptr_t>(cos_tab) & 3) || (reinterpret_cast<uintptr_t>(sin_tab) & 3))
+    return IDX_EINVAL;
+  const int64_t tasks = (int64_t)rows * IDX_HEADS;
+  const int blocks = (int)((tasks + PREP_WAVES - 1) / PREP_WAVES);
+  hipLaunchKernelGGL(prep_query_kernel, dim3(blocks), dim3(64 * PREP_WAVES), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint32_t*>(q_pre), cos_tab, sin_tab, static_cast<uint32_t*>(q_out), rows,
+                     rope_dim, interleaved);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? IDX_OK : hip_fail(e);
 }
 
 int idx_device_status(void* ws, size_t ws_bytes, void* stream, uint32_t* detail) {

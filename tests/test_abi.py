@@ -210,3 +210,14 @@ def test_workspace_init_and_status_validation(L):
     assert L.idx_workspace_init(FAKE, 1000, None) == _lib.IDX_EINVAL
     assert L.idx_device_status(None, 1024, None, None) == _lib.IDX_EINVAL
 
+
+
+def test_prep_query_validation(L):
+    """idx_prep_query refuses bad arguments before any launch."""
+    ok = dict(q=FAKE, c=FAKE, s=FAKE, rows=4, rope=64, il=0, out=FAKE + 0x100000)
+    cases = [dict(q=None), dict(out=None), dict(rows=0), dict(rope=-2), dict(rope=3), dict(rope=130),
+             dict(il=2), dict(c=None), dict(s=None), dict(q=FAKE + 2), dict(out=FAKE + 2), dict(c=FAKE + 1)]
+    for over in cases:
+        a = dict(ok, **over)
+        rc = L.idx_prep_query(a["q"], a["c"], a["s"], a["rows"], a["rope"], a["il"], a["out"], None)
+        assert rc == _lib.IDX_EINVAL, over

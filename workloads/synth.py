@@ -191,3 +191,13 @@ def make_config(name: str, *, scale_down: Optional[int] = None) -> Problem:
         if spec.get("keys") == "recent":
             spec["recent"] = max(1, 4096 // scale_down)
     return make_problem(name=name if not scale_down else f"{name}/{scale_down}", **spec)
+
+
+def rope_table(positions, rope_dim: int, theta: float = 10000.0):
+    """A RoPE rotation table for rows at the given positions: (cos, sin), f32
+    [rows, rope_dim / 2], angle position * theta ** (-2 i / rope_dim) for pair i,
+    evaluated in f64 and rounded to f32 (a caller-side input of query preparation)."""
+    pos = np.asarray(positions, dtype=np.float64)[:, None]
+    i = np.arange(rope_dim // 2, dtype=np.float64)[None, :]
+    ang = pos * theta ** (-2.0 * i / max(rope_dim, 1))
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
