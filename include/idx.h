@@ -130,6 +130,16 @@ int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys,
 int idx_score_topk(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores,
                    int32_t* topk, void* ws, size_t ws_bytes, void* stream);
 
+/* As idx_score_topk(), and also each list as physical cache slots, the form the sparse
+ * attention reads (the indexer page's selection stages cache slots, Modifications
+ * item 3): slots[r * k + i] = page_table[r][p / 64] * 64 + p % 64 for
+ * the list entry p = topk[r * k + i] >= 0, and -1 where the list holds -1 (or where the
+ * page id lies outside the pool, which also raises IDX_DERR_PAGE).  slots: device
+ * int32 [rows][k], distinct from topk.  Same launches; the selection launch maps the
+ * list after writing it. */
+int idx_score_topk_slots(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores,
+                         int32_t* topk, int32_t* slots, void* ws, size_t ws_bytes, void* stream);
+
 /* Index-query preparation (the GLM-5.3 indexer page, Modifications item 2, "the query
  * once a row": each row's index query is roped and Hadamard-transformed once and
  * published in bf16; Modifications item 0: that transform runs in f32, then rounds to

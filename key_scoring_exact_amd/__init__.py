@@ -164,6 +164,23 @@ def score_topk(p: DeviceProblem, k: int, ws: Workspace, scores: Optional[torch.T
     return scores, out
 
 
+def score_topk_slots(p: DeviceProblem, k: int, ws: Workspace, scores: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None, slots: Optional[torch.Tensor] = None, stream=None):
+    """(scores, lists, slots): as score_topk, plus each list as physical cache slots [rows, k]."""
+    if scores is None:
+        scores = torch.empty((p.rows, max(1, p.max_keys)), dtype=torch.float32, device=p.q.device)
+    if out is None:
+        out = torch.empty((p.rows, k), dtype=torch.int32, device=p.q.device)
+    if slots is None:
+        slots = torch.empty((p.rows, k), dtype=torch.int32, device=p.q.device)
+    s, keep = p.struct()
+    _check(lib().idx_score_topk_slots(ctypes.byref(s), int(k), ctypes.c_void_p(_ptr(scores, torch.float32)),
+                                      scores.shape[1], ctypes.c_void_p(_ptr(out, torch.int32)),
+                                      ctypes.c_void_p(_ptr(slots, torch.int32)), ctypes.c_void_p(ws.ptr), ws.nbytes,
+                                      ctypes.c_void_p(_stream(stream))), "idx_score_topk_slots")
+    return scores, out, slots
+
+
 def topk(scores: torch.Tensor, n_keys: torch.Tensor, k: int, max_keys: int, ws: Workspace,
          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Exact top-k lists [rows, k] int32 of given f32 scores [rows, ld]."""

@@ -58,6 +58,7 @@ SIGNATURES = {
     "idx_score": (ctypes.c_int, [ctypes.POINTER(IdxProblem), _vp, _i64, _vp, _sz, _vp]),
     "idx_topk": (ctypes.c_int, [_vp, _i64, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "idx_score_topk": (ctypes.c_int, [ctypes.POINTER(IdxProblem), _i32, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "idx_score_topk_slots": (ctypes.c_int, [ctypes.POINTER(IdxProblem), _i32, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "idx_prep_query": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "idx_device_status": (ctypes.c_int, [_vp, _sz, _vp, ctypes.POINTER(ctypes.c_uint32)]),
     "idx_strerror": (ctypes.c_char_p, [ctypes.c_int]),

@@ -98,6 +98,7 @@ struct KArgs {
   const int32_t* nk;        // int32 [rows]
   float* scores;            // [rows][ld]: written (MODE_SCORE) or read
   int32_t* topk;            // [rows][k]
+  int32_t* slots;           // [rows][k] or null: the lists as physical cache slots
   uint8_t* ws;
   int64_t ld;
   int32_t rows, max_pages, max_keys, num_pages, k;
@@ -1582,8 +1583,7 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
 // Launch 2: workgroup (i, g) selects row i of request g.  Launch 1 has ended, so its
 // scores and candidates are in memory.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+__device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = wave_id();
@@ -1598,10 +1598,10 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
   const uint32_t magic = *reinterpret_cast<const uint32_t*>(ws + WS_MAGIC_OFF);
   int nr = __builtin_amdgcn_readfirstlane(a.nk[grow]);
   asm volatile("" ::"s"(magic), "s"(nr));          // both loads issued before the branches below
-  if (i >= R) return;
+  if (i >= R) return false;
   if (magic != WS_MAGIC) {
     if (tid == 0 && i == 0 && blockIdx.y == 0) raise_error(ws, IDX_DERR_WS);
-    return;
+    return false;
   }
   const int gbound = a.gmax[blockIdx.y];
   if (nr < 0 || nr > gbound) {
@@ -1613,7 +1613,7 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
   const int path = row_path(nr, k, a.chunk_shift);
   if (path == PATH_NONE) {
     for (int p = tid; p < k; p += NT) out[p] = p < nr ? p : -1;
-    return;
+    return true;
   }
   int* misc = LDS_PTR(int, L_MISC);
   uint32_t* hist = LDS_PTR(uint32_t, L_HIST);
@@ -1743,6 +1743,31 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
     // ---- exact multi-pass select over the row's scores in memory
     __syncthreads();
     global_select_row(srow, nr, k, out, hist, misc);
+  }
+  return true;
+}
+
+// Launch 2.  With a slot array, each written list is then mapped to physical cache
+// slots through the row's own page-table row: slot = page_table[row][p / 64] * 64 +
+// p % 64, and -1 for -1 padding (or for a page id outside the pool, which the scoring
+// launch has already reported).
+__global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  if (!select_row(a, smem) || a.slots == nullptr) return;
+  __syncthreads();                                   // the list's stores, visible to the workgroup
+  const uint32_t ge = a.grp[blockIdx.y];
+  const int grow = (int)(ge & 0xFFFFFFu) + (int)blockIdx.x;
+  const int32_t* lst = a.topk + (int64_t)grow * a.k;
+  int32_t* sl = a.slots + (int64_t)grow * a.k;
+  const int32_t* ptr = a.pt + (int64_t)grow * a.max_pages;
+  for (int i = threadIdx.x; i < a.k; i += NT) {
+    const int p = lst[i];
+    int v = -1;
+    if (p >= 0) {
+      const int ph = ptr[p / PS];
+      v = (ph >= 0 && ph < a.num_pages) ? ph * PS + (p % PS) : -1;
+    }
+    sl[i] = v;
   }
 }
 
@@ -1952,8 +1977,8 @@ void fill_common(KArgs& args, const WsLayout& L, void* ws) {
   args.off_ent = L.off_ent;
 }
 
-int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int32_t* topk, void* ws,
-                size_t ws_bytes, void* stream, bool select) {
+int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int32_t* topk, int32_t* slots,
+                void* ws, size_t ws_bytes, void* stream, bool select) {
   int rc = validate_problem(p);
   if (rc) return rc;
   if (!scores || ld < 1 || ld < (int64_t)p->max_keys) return IDX_EINVAL;
@@ -1977,6 +2002,7 @@ int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int3
   args.nk = p->n_keys;
   args.scores = scores;
   args.topk = topk;
+  args.slots = slots;
   args.ld = ld;
   args.rows = p->rows;
   args.max_pages = p->max_pages;
@@ -2026,12 +2052,18 @@ int idx_workspace_init(void* ws, size_t ws_bytes, void* stream) {
 }
 
 int idx_score(const idx_problem* p, float* scores, int64_t ld_scores, void* ws, size_t ws_bytes, void* stream) {
-  return run_problem(p, 1, scores, ld_scores, nullptr, ws, ws_bytes, stream, false);
+  return run_problem(p, 1, scores, ld_scores, nullptr, nullptr, ws, ws_bytes, stream, false);
 }
 
 int idx_score_topk(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores, int32_t* topk, void* ws,
                    size_t ws_bytes, void* stream) {
-  return run_problem(p, k, scores, ld_scores, topk, ws, ws_bytes, stream, true);
+  return run_problem(p, k, scores, ld_scores, topk, nullptr, ws, ws_bytes, stream, true);
+}
+
+int idx_score_topk_slots(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores, int32_t* topk,
+                         int32_t* slots, void* ws, size_t ws_bytes, void* stream) {
+  if (!slots || (topk && slots == topk)) return IDX_EINVAL;
+  return run_problem(p, k, scores, ld_scores, topk, slots, ws, ws_bytes, stream, true);
 }
 
 int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys, int32_t rows, int32_t max_keys,

@@ -150,3 +150,17 @@ def topk(problem, row_scores_list=None) -> np.ndarray:
     for r in range(problem.rows):
         out[r] = select(vs[r], int(problem.n_keys[r]), problem.k)
     return out
+
+
+def list_slots(problem, lists: np.ndarray) -> np.ndarray:
+    """Each list entry as its physical cache slot, through the row's own page-table row
+    (the same gather as the scoring: position p lives in page page_table[r][p // page]
+    at slot p % page); -1 padding stays -1."""
+    lists = np.asarray(lists, dtype=np.int64)
+    out = np.full(lists.shape, -1, dtype=np.int64)
+    for r in range(lists.shape[0]):
+        p = lists[r]
+        m = p >= 0
+        out[r, m] = problem.page_table[r][p[m] // problem.page_size].astype(np.int64) * problem.page_size + \
+            p[m] % problem.page_size
+    return out

@@ -140,3 +140,27 @@ def test_mixed_requests_with_long_chains():
     prob = make_problem([9000, 1500, 30000], [8, 1, 5], seed=88, name="mixed_long")
     bounds = [int(prob.n_keys[a:b].max()) for a, b in zip(prob.req_indptr[:-1], prob.req_indptr[1:])]
     check_against_oracle(prob, run_all(prob, req_max_keys=bounds))
+
+
+@pytest.mark.parametrize("contexts,rows", [([3000], [4]), ([131072], [4]), ([1500, 40000, 9000], [2, 3, 8])])
+def test_slot_output(contexts, rows):
+    """idx_score_topk_slots: the same scores and lists as idx_score_topk, and each list
+    entry as its physical cache slot through the row's own page-table row."""
+    import key_scoring_exact_amd as idx
+    from .gpu_helpers import device_problem
+    prob = make_problem(contexts, rows, seed=9100 + sum(contexts), name=f"slots{contexts}")
+    print(f"case slots {contexts} {rows}", flush=True)
+    dp = device_problem(prob)
+    ws = idx.Workspace(prob.rows, dp.max_keys, prob.k)
+    sc, ls, sl = idx.score_topk_slots(dp, prob.k, ws)
+    sc2, ls2 = idx.score_topk(dp, prob.k, ws)
+    assert idx.device_status(ws)[0] == 0
+    ls, sl = ls.cpu().numpy(), sl.cpu().numpy()
+    assert np.array_equal(ls, ls2.cpu().numpy())
+    a, b = sc.cpu().numpy().view(np.uint32), sc2.cpu().numpy().view(np.uint32)
+    for r in range(prob.rows):                     # positions past n_keys are not written
+        n = int(prob.n_keys[r])
+        assert np.array_equal(a[r, :n], b[r, :n]), r
+    assert np.array_equal(sl, O.list_slots(prob, ls))
+    res = dict(scores=sc.cpu().numpy(), lists=ls, scores_only=sc.cpu().numpy(), lists_topk=ls, code=0, detail=0)
+    check_against_oracle(prob, res)

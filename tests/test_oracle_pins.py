@@ -218,3 +218,20 @@ def test_select_special_cases():
     assert O.select(np.array([1.0, 2.0, 9.0, 0.0, 8.0]), 5, 3).tolist() == [1, 2, 4]
     with pytest.raises(ValueError):
         O.select(np.array([np.nan, 1.0]), 2, 1)
+
+
+def test_list_slots_identity_and_permutation():
+    """Slots of a list: with an identity page table they are the positions; with a
+    permuted table position p maps into page perm[p // 64] at slot p % 64; -1 stays."""
+    from workloads import make_problem
+    prob = make_problem([300], [2], seed=11, k=8, name="slots")
+    lists = np.array([[0, 1, 63, 64, 65, 299, -1, -1], [5, 70, 128, 200, 250, 296, 297, 298]])
+    ident = prob.page_table.copy()
+    ident[:] = np.arange(ident.shape[1])
+    prob.page_table = ident
+    assert np.array_equal(O.list_slots(prob, lists), lists)
+    perm = np.array([3, 0, 4, 1, 2], dtype=np.int32)
+    prob.page_table = np.tile(perm, (2, 1))
+    got = O.list_slots(prob, lists)
+    assert got[0, 0] == 3 * 64 and got[0, 2] == 3 * 64 + 63 and got[0, 3] == 0 and got[0, 5] == 2 * 64 + 43
+    assert got[0, 6] == -1 and got[1, 2] == 4 * 64
