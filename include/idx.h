@@ -130,6 +130,28 @@ int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys,
 int idx_score_topk(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores,
                    int32_t* topk, void* ws, size_t ws_bytes, void* stream);
 
+/* Keys written in the same launch (the indexer page, Modifications item 2, "keys this
+ * launch writes": each verify row publishes its own new index key as FP8 values and a
+ * scale, and a scoring pass holding that position patches it in from those pairs, for
+ * every row of the request, since the cache store need not be visible yet).  Row r's
+ * key, codes[r][0..128) (E4M3FN) and scales[r] (f32, finite, >= 0), takes logical
+ * position pos[r] of its request: physical slot page_table[r][pos / 64] * 64 + pos % 64.
+ * pos[r] = -1: the row writes no key.  0 <= pos[r] < n_keys[r] otherwise (a row sees
+ * its own key); other values raise IDX_DERR_NKEYS and are ignored.  Device pointers;
+ * codes 16-byte aligned. */
+typedef struct idx_new_keys {
+  const uint8_t* codes;    /* E4M3FN [rows][128] */
+  const float* scales;     /* f32 [rows] */
+  const int32_t* pos;      /* int32 [rows] */
+} idx_new_keys;
+
+/* As idx_score_topk(), with every row's new key (idx_new_keys) in place: the scores are
+ * those of the cache after the keys are written, and the launch also writes them into
+ * p->k_cache and p->k_scale (which this call therefore modifies).  At most 16 rows a
+ * request (else IDX_EUNSUPPORTED). */
+int idx_score_topk_append(const idx_problem* p, const idx_new_keys* nk, int32_t k, float* scores,
+                          int64_t ld_scores, int32_t* topk, void* ws, size_t ws_bytes, void* stream);
+
 /* As idx_score_topk(), and also each list as physical cache slots, the form the sparse
  * attention reads (the indexer page's selection stages cache slots, Modifications
  * item 3): slots[r * k + i] = page_table[r][p / 64] * 64 + p % 64 for

@@ -164,6 +164,25 @@ def score_topk(p: DeviceProblem, k: int, ws: Workspace, scores: Optional[torch.T
     return scores, out
 
 
+def score_topk_append(p: DeviceProblem, k: int, ws: Workspace, new_codes: torch.Tensor, new_scales: torch.Tensor,
+                      new_pos: torch.Tensor, scores: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                      stream=None):
+    """(scores, lists) with every row's new key written in the same launch: new_codes uint8
+    [rows, 128], new_scales f32 [rows], new_pos int32 [rows] (-1: none).  Writes the keys
+    into p.k_cache / p.k_scale."""
+    if scores is None:
+        scores = torch.empty((p.rows, max(1, p.max_keys)), dtype=torch.float32, device=p.q.device)
+    if out is None:
+        out = torch.empty((p.rows, k), dtype=torch.int32, device=p.q.device)
+    s, keep = p.struct()
+    nk = _lib.IdxNewKeys(_ptr(new_codes, torch.uint8), _ptr(new_scales, torch.float32), _ptr(new_pos, torch.int32))
+    _check(lib().idx_score_topk_append(ctypes.byref(s), ctypes.byref(nk), int(k),
+                                       ctypes.c_void_p(_ptr(scores, torch.float32)), scores.shape[1],
+                                       ctypes.c_void_p(_ptr(out, torch.int32)), ctypes.c_void_p(ws.ptr), ws.nbytes,
+                                       ctypes.c_void_p(_stream(stream))), "idx_score_topk_append")
+    return scores, out
+
+
 def score_topk_slots(p: DeviceProblem, k: int, ws: Workspace, scores: Optional[torch.Tensor] = None,
                      out: Optional[torch.Tensor] = None, slots: Optional[torch.Tensor] = None, stream=None):
     """(scores, lists, slots): as score_topk, plus each list as physical cache slots [rows, k]."""

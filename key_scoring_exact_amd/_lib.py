@@ -51,6 +51,10 @@ class IdxProblem(ctypes.Structure):
     ]
 
 
+class IdxNewKeys(ctypes.Structure):
+    _fields_ = [("codes", _vp), ("scales", _vp), ("pos", _vp)]
+
+
 SIGNATURES = {
     "idx_abi_version": (ctypes.c_int, []),
     "idx_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
@@ -58,6 +62,8 @@ SIGNATURES = {
     "idx_score": (ctypes.c_int, [ctypes.POINTER(IdxProblem), _vp, _i64, _vp, _sz, _vp]),
     "idx_topk": (ctypes.c_int, [_vp, _i64, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "idx_score_topk": (ctypes.c_int, [ctypes.POINTER(IdxProblem), _i32, _vp, _i64, _vp, _vp, _sz, _vp]),
+    "idx_score_topk_append": (ctypes.c_int, [ctypes.POINTER(IdxProblem), ctypes.POINTER(IdxNewKeys), _i32, _vp, _i64,
+                                             _vp, _vp, _sz, _vp]),
     "idx_score_topk_slots": (ctypes.c_int, [ctypes.POINTER(IdxProblem), _i32, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "idx_prep_query": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "idx_device_status": (ctypes.c_int, [_vp, _sz, _vp, ctypes.POINTER(ctypes.c_uint32)]),

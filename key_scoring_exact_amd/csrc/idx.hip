@@ -69,7 +69,9 @@ constexpr int L_KSC = PMAX * PS * D;                        // [PMAX][64] f32 ke
 constexpr int L_SC = L_KSC + PMAX * PS * 4;                 // [GR][CMAX] f32 scores of the chunk
 constexpr int L_Q = L_SC + GR * CMAX * 4;                   // [GR][64 heads][256 B] bf16 queries, swizzled
 constexpr int L_W = L_Q + GR * H * D * 2;                   // [GR][64] bf16 head weights
-constexpr int L_SCORE_END = L_W + GR * H * 2;
+constexpr int NEW_MAX = 16;                                 // rows a request, when keys are written in the launch
+constexpr int L_PATCH = L_W + GR * H * 2;                   // [NEW_MAX][128 B] the request's new key codes
+constexpr int L_SCORE_END = L_PATCH + NEW_MAX * D;
 // LDS layout, finishing phase
 constexpr int HIST_WORDS = 4096 + 64;                       // one histogram: 4096 bins + 64 per-lane dummies
 constexpr int L_HIST = 0;                                   // 2 histograms (low addresses: offsets fold into ds_add)
@@ -107,8 +109,16 @@ struct KArgs {
   int32_t mode;
   int32_t ent_stride;       // candidate blocks per row (>= chunks of a row that selects from candidates)
   uint64_t off_ent;
+  // keys written in this launch (null nw_pos: none): row r's key (codes nw_codes[r],
+  // scale nw_scales[r]) takes logical position nw_pos[r] (-1: none) of its request
+  const uint8_t* nw_codes;  // E4M3 [rows][128]
+  const float* nw_scales;   // f32 [rows]
+  const int32_t* nw_pos;    // int32 [rows]
+  uint8_t* kc_w;            // the cache, written
+  float* ks_w;
   uint32_t grp[IDX_MAX_REQ];// row0 | nrows << 24
   int32_t gmax[IDX_MAX_REQ];// host bound on the keys of each group's rows
+  uint32_t req[IDX_MAX_REQ];// the group's request: its first row | its rows << 24 (with nw_pos)
 };
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -925,8 +935,19 @@ __device__ inline void wait_pages_through(int x, int issued) {
 // scoring of one chunk: scores of the group's rows land in sc_lds[row][0..C)
 // TS = tile stride = waves per row (8 / R, 2 for R = 3); each wave scores one row.
 // ---------------------------------------------------------------------------
+// Keys written in this launch that fall in the chunk: bit b of `hit` is the request's
+// row b, whose key takes position readlane(npos, b) with scale readlane(nscl, b); its
+// codes are at L_PATCH + 128 b.  `mine` marks the rows of this workgroup's group, whose
+// keys it also stores to the cache.
+struct Patches {
+  uint64_t hit, mine;
+  int npos;
+  float nscl;
+};
+
 template <int P, int TS>
-__device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R, int c, const int* phys) {
+__device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R, int c, const int* phys,
+                                            const Patches& pt) {
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   float* const sc_lds = LDS_PTR(float, L_SC);
@@ -1020,6 +1041,39 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
   auto page_of_iter = [&](int i) { return ((i * TS + TS - 1) >> 1) < P - 1 ? ((i * TS + TS - 1) >> 1) : P - 1; };
 
   int issued = L0;
+  int patched = -1;                             // pages [0, patched] hold this launch's new keys
+  const int cbase = c * (P * PS);
+  // the new keys of pages (patched, x] into the landed pages (wave 0: 8 lanes of codes,
+  // one of scale), and into the cache for this group's rows; then a barrier
+  auto patch_pages = [&](int x) {
+    uint64_t todo = 0;
+    for (uint64_t m = pt.hit; m != 0; m &= m - 1) {
+      const int b = __builtin_ctzll(m);
+      const int j = (__builtin_amdgcn_readlane(pt.npos, b) - cbase) >> 6;
+      if (j > patched && j <= x) todo |= 1ull << b;
+    }
+    patched = x;
+    if (todo == 0) return;
+    if (wv == 0) {
+      for (uint64_t m = todo; m != 0; m &= m - 1) {
+        const int b = __builtin_ctzll(m);
+        const int pos = __builtin_amdgcn_readlane(pt.npos, b);
+        const int j = (pos - cbase) >> 6, kn = pos & (PS - 1);
+        const bool store = (pt.mine >> b) & 1ull;
+        const int64_t slot = (int64_t)phys[j] * PS + kn;
+        if (lane < 8) {
+          const v4i v = *reinterpret_cast<const v4i*>(smem + L_PATCH + b * D + lane * 16);
+          *reinterpret_cast<v4i*>(smem + L_KEYS + j * (PS * D) + kn * D + ((lane ^ ((kn >> 1) & 7)) << 4)) = v;
+          if (store) *reinterpret_cast<v4i*>(a.kc_w + slot * D + lane * 16) = v;
+        } else if (lane == 8) {
+          const float sv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pt.nscl), b));
+          LDS_PTR(float, L_KSC)[j * PS + kn] = sv;
+          if (store) a.ks_w[slot] = sv;
+        }
+      }
+    }
+    __syncthreads();
+  };
   auto ensure_page = [&](int x) {
     // pages [0, x] issued and landed (all waves' parts), then LOOKAHEAD more in flight
 #pragma unroll
@@ -1028,6 +1082,7 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
     if (issued < x + 1) issued = x + 1;
     wait_pages_through(x, issued);
     __syncthreads();
+    if (pt.hit != 0ull) patch_pages(x);
 #pragma unroll
     for (int j = 0; j < P; j++)
       if (j >= issued && j <= x + LOOKAHEAD) issue_page(j);
@@ -1398,6 +1453,24 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
     }
     if (lane < 8) dma16(a.w + (int64_t)(row0 + (wv % R)) * H * 2 + lane * 16, lds0 + L_W + (wv % R) * (H * 2));
   }
+  // keys written in this launch: the request's rows' codes into L_PATCH (wave 0, two
+  // DMAs: lane l of DMA i copies chunk l % 8 of row 8 i + l / 8), their positions and
+  // scales with the key counts below (lanes [0, request rows))
+  const uint32_t rq = a.nw_pos != nullptr ? a.req[g] : 0u;
+  const int rq0 = (int)(rq & 0xFFFFFFu), rqn = (int)(rq >> 24);
+  if (do_score && rqn > 0 && wv == 0) {
+#pragma unroll
+    for (int i2 = 0; i2 < 2; i2++) {
+      const int b = i2 * 8 + (lane >> 3);
+      if (b < rqn) dma16(a.nw_codes + (int64_t)(rq0 + b) * D + (lane & 7) * 16, lds0 + L_PATCH + i2 * 1024);
+    }
+  }
+  int ld_np = -1;
+  float ld_ns = 0.f;
+  if (do_score && lane < rqn) {
+    ld_np = a.nw_pos[rq0 + lane];
+    ld_ns = a.nw_scales[rq0 + lane];
+  }
   // n_keys of the group's rows, the chunk's page ids of every row and the workspace's
   // magic word, in one load (lanes [0, R): n_keys; lanes [8, 8 + R*P):
   // page_table[row][c*P + j]; lane 63: the magic word)
@@ -1461,9 +1534,23 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
       phys[j] = ph;
     }
     if (perr && tid == 0) raise_error(ws, perr);
-    if (R == 1) score_chunk<P, 8>(a, smem, R, c, phys);
-    else if (R == 2) score_chunk<P, 4>(a, smem, R, c, phys);
-    else score_chunk<P, 2>(a, smem, R, c, phys);
+    // the request's new keys in this chunk; a position outside [-1, the row's key
+    // count) is reported and ignored (each row's key is within what the row sees)
+    Patches pt = {0ull, 0ull, ld_np, ld_ns};
+    if (rqn > 0) {
+      const int own = lane - (row0 - rq0);           // this lane's row within the group
+      int nown = 0;
+#pragma unroll
+      for (int i2 = 0; i2 < GR; i2++) nown = (own == i2) ? n[i2] : nown;
+      const bool inr = lane < rqn;
+      const bool bad = inr && (ld_np < -1 || (own >= 0 && own < R && ld_np >= nown));
+      if (__ballot(bad) != 0ull && tid == 0) raise_error(ws, IDX_DERR_NKEYS);
+      pt.hit = __ballot(inr && !bad && ld_np >= chunk_base && ld_np < chunk_base + C && ld_np < nmax);
+      pt.mine = __ballot(inr && own >= 0 && own < R);
+    }
+    if (R == 1) score_chunk<P, 8>(a, smem, R, c, phys, pt);
+    else if (R == 2) score_chunk<P, 4>(a, smem, R, c, phys, pt);
+    else score_chunk<P, 2>(a, smem, R, c, phys, pt);
   } else {
 #pragma unroll
     for (int i = 0; i < GR; i++) {
@@ -1978,7 +2065,7 @@ void fill_common(KArgs& args, const WsLayout& L, void* ws) {
 }
 
 int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int32_t* topk, int32_t* slots,
-                void* ws, size_t ws_bytes, void* stream, bool select) {
+                void* ws, size_t ws_bytes, void* stream, bool select, const idx_new_keys* nk = nullptr) {
   int rc = validate_problem(p);
   if (rc) return rc;
   if (!scores || ld < 1 || ld < (int64_t)p->max_keys) return IDX_EINVAL;
@@ -2013,15 +2100,24 @@ int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int3
   args.chunk_shift = 31 - __builtin_clz((unsigned)pl.chunk);
   args.mode = select ? (MODE_SCORE | MODE_PUBLISH) : MODE_SCORE;
   fill_common(args, L, ws);
+  if (nk) {
+    args.nw_codes = nk->codes;
+    args.nw_scales = nk->scales;
+    args.nw_pos = nk->pos;
+    args.kc_w = const_cast<uint8_t*>(p->k_cache);
+    args.ks_w = const_cast<float*>(p->k_scale);
+  }
   // a request of more than IDX_GROUP_ROWS rows is scored as consecutive groups of at
   // most IDX_GROUP_ROWS of its rows; each group walks the request's pages once
   int groups = 0;
   for (int j = 0; j < p->num_req; j++) {
     const int bound = p->req_max_keys ? p->req_max_keys[j] : p->max_keys;
+    const int rows_j = p->req_indptr[j + 1] - p->req_indptr[j];
     for (int r0 = p->req_indptr[j]; r0 < p->req_indptr[j + 1]; r0 += IDX_GROUP_ROWS) {
       const int rn = p->req_indptr[j + 1] - r0 < IDX_GROUP_ROWS ? p->req_indptr[j + 1] - r0 : IDX_GROUP_ROWS;
       args.grp[groups] = (uint32_t)r0 | ((uint32_t)rn << 24);
       args.gmax[groups] = bound;
+      args.req[groups] = (uint32_t)p->req_indptr[j] | ((uint32_t)rows_j << 24);
       groups++;
     }
   }
@@ -2058,6 +2154,19 @@ int idx_score(const idx_problem* p, float* scores, int64_t ld_scores, void* ws, 
 int idx_score_topk(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores, int32_t* topk, void* ws,
                    size_t ws_bytes, void* stream) {
   return run_problem(p, k, scores, ld_scores, topk, nullptr, ws, ws_bytes, stream, true);
+}
+
+int idx_score_topk_append(const idx_problem* p, const idx_new_keys* nk, int32_t k, float* scores,
+                          int64_t ld_scores, int32_t* topk, void* ws, size_t ws_bytes, void* stream) {
+  if (!nk || !nk->codes || !nk->scales || !nk->pos) return IDX_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(nk->codes) & 15) || (reinterpret_cast<uintptr_t>(nk->scales) & 3) ||
+      (reinterpret_cast<uintptr_t>(nk->pos) & 3))
+    return IDX_EINVAL;
+  const int rc = validate_problem(p);
+  if (rc) return rc;
+  for (int j = 0; j < p->num_req; j++)
+    if (p->req_indptr[j + 1] - p->req_indptr[j] > NEW_MAX) return IDX_EUNSUPPORTED;
+  return run_problem(p, k, scores, ld_scores, topk, nullptr, ws, ws_bytes, stream, true, nk);
 }
 
 int idx_score_topk_slots(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores, int32_t* topk,

@@ -164,3 +164,23 @@ def list_slots(problem, lists: np.ndarray) -> np.ndarray:
         out[r, m] = problem.page_table[r][p[m] // problem.page_size].astype(np.int64) * problem.page_size + \
             p[m] % problem.page_size
     return out
+
+
+def with_new_keys(problem, codes: np.ndarray, scales: np.ndarray, pos: np.ndarray):
+    """The problem with each row's new key written into its cache: row r's codes[r] and
+    scales[r] at logical position pos[r] (-1: none), physical slot page_table[r][pos //
+    page] * page + pos % page.  Returns a copy; the input is unchanged."""
+    import copy
+    out = copy.copy(problem)
+    kc = problem.k_cache.copy().reshape(-1, problem.dim)
+    ks = problem.k_scale.copy().reshape(-1)
+    for r in range(problem.rows):
+        p = int(pos[r])
+        if p < 0:
+            continue
+        slot = int(problem.page_table[r][p // problem.page_size]) * problem.page_size + p % problem.page_size
+        kc[slot] = codes[r]
+        ks[slot] = scales[r]
+    out.k_cache = kc.reshape(problem.k_cache.shape)
+    out.k_scale = ks.reshape(problem.k_scale.shape)
+    return out

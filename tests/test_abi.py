@@ -221,3 +221,22 @@ def test_prep_query_validation(L):
         a = dict(ok, **over)
         rc = L.idx_prep_query(a["q"], a["c"], a["s"], a["rows"], a["rope"], a["il"], a["out"], None)
         assert rc == _lib.IDX_EINVAL, over
+
+
+def test_append_validation(L):
+    """idx_score_topk_append refuses a missing or misaligned new-key set and requests of
+    more than 16 rows before any launch."""
+    p, keep = make_problem()
+    need = ws_size(L, 6, 3200)
+    def call(nk, prob=p):
+        return L.idx_score_topk_append(ctypes.byref(prob), nk, 2048, FAKE, 3200, FAKE, FAKE, need, None)
+    good = dict(codes=FAKE, scales=FAKE, pos=FAKE)
+    assert call(None) == _lib.IDX_EINVAL
+    for over in (dict(codes=None), dict(scales=None), dict(pos=None), dict(codes=FAKE + 4), dict(scales=FAKE + 2),
+                 dict(pos=FAKE + 1)):
+        nk = _lib.IdxNewKeys(**dict(good, **over))
+        assert call(ctypes.byref(nk)) == _lib.IDX_EINVAL, over
+    ip = (ctypes.c_int32 * 2)(0, 17)
+    p17, keep17 = make_problem(rows=17, num_req=1, req_indptr=ctypes.cast(ip, ctypes.POINTER(ctypes.c_int32)))
+    nk = _lib.IdxNewKeys(**good)
+    assert call(ctypes.byref(nk), p17) == _lib.IDX_EUNSUPPORTED
