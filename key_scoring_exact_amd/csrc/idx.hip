@@ -738,6 +738,9 @@ __device__ int select_explicit(const uint64_t* cand, int E, int n, int k, uint32
 // The result is (Tge, rem): every key >= Tge is selected, and the first rem keys equal to
 // Tge - 1.  An ordered emission (16 consecutive positions a thread, one block scan a
 // round) writes the list and stops once k positions are out.  Every thread must call.
+__device__ __forceinline__ void emit_ordered(const float* row, int n, int k, uint32_t Tge, int trem, int32_t* out,
+                                             int* misc);
+
 __device__ __forceinline__ void global_select_row(const float* row, int n, int k, int32_t* out, uint32_t* hist, int* misc) {
   const int tid = threadIdx.x;
   __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (int64_t)n * 4);
@@ -799,6 +802,16 @@ __device__ __forceinline__ void global_select_row(const float* row, int n, int k
     rem = r;
     __syncthreads();
   }
+  emit_ordered(row, n, k, Tge, trem, out, misc);
+}
+
+// Ordered emission over a row's scores in memory: every key >= Tge and the first trem
+// keys equal to Tge - 1, in position order, into out[0 .. k); stops once k are out.
+// Every thread must call.
+__device__ __forceinline__ void emit_ordered(const float* row, int n, int k, uint32_t Tge, int trem, int32_t* out,
+                                             int* misc) {
+  const int tid = threadIdx.x;
+  __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (int64_t)n * 4);
   const uint32_t Teq = Tge - 1u;
   int gt_carry = 0, eq_carry = 0;
   for (int base = 0; base < n; base += NT * 16) {
@@ -1585,7 +1598,8 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
     const int nv = nr - chunk_base;
     if (nv > 0 && row_path(nr, k, shift) == PATH_CAND) {
       // the chunk's candidate block (32 G slots, staged in LDS, then stored coalesced):
-      // slot 0 = t_w | (overflow << 16 | count) << 32, slot 1 = the chunk's largest key,
+      // slot 0 = t_w | (overflow << 16 | count) << 32 (count = the keys >= t_w, published
+      // or not), slot 1 = the chunk's largest key,
       // slots 2 .. count + 1 = every key of the chunk >= t_w as key << 32 | position,
       // ascending in position, then zeros.  t_w is a lower bound of the chunk's m-th
       // largest key, so at least m keys are published.  thr0, a bound of the m-th largest
@@ -1653,7 +1667,7 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
           }
       }
       if (lane == 0) {
-        stg[0] = ((uint64_t)(fits ? (uint32_t)total : (1u << 16)) << 32) | thr;
+        stg[0] = ((uint64_t)((fits ? 0u : (1u << 16)) | (uint32_t)total) << 32) | thr;
         stg[1] = cmax;
       }
       // this wave's LDS writes before its reads (LDS executes a wave's operations in order)
@@ -1776,7 +1790,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
       if (w < wact) {
         const uint32_t tw = hv[u][0], flags = hv[u][1], cmax = hv[u][2];
         const bool ov = (flags >> 16) & 1u;
-        t4[0] += flags & 0xFFFFu;
+        t4[0] += ov ? 0u : (flags & 0xFFFFu);
         if (!ov) t4[1] = max(t4[1], tw);
         t4[2] = max(t4[2], cmax);
         t4[3] += ov ? 1u : 0u;
@@ -1789,40 +1803,62 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
     // gathered.  (0x00800000 is the smallest key of a finite score.)
     const uint32_t lo = t4[1] > 0x00800000u ? t4[1] : 0x00800000u;
     const uint32_t hi = t4[2] > lo ? t4[2] : lo;
-    // the keys >= t* (not every published key: from about 1,024 chunks a row, the
-    // published keys can pass the LDS capacity while those >= t* fit)
-    int E = 0;
-    bool fits = true;
-    const int per_batch = batch_chunks(G);
-    for (int b0 = 0; b0 < wact; b0 += per_batch) {
-      if (b0 > 0) issue(b0);
-      const int got = gather_place(e, lo, E, cand, misc);
-      if (got < 0) {
-        fits = false;
-        break;
-      }
-      E += got;
-    }
-    if (fits) {
-      pad_cand(cand, E);
-      __syncthreads();
-      if (t4[3] == 0u) {
-        int got = -1;
-        done = select_cand<FIN_ENT / NT>(cand, E, lo, hi, k, hist, misc, out, &got);
-        if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
-      }
-      if (!done && nr <= BITMAP_KEYS && (E >= k || (int)t4[0] <= FIN_ENT)) {
-        uint32_t glo = lo;
-        if (E < k) {
-          // fewer than k keys >= t*: every published key instead, chunk w held from its own t_w
-          glo = 0x00800000u;
-          E = 0;
-          for (int b0 = 0; b0 < wact; b0 += per_batch) {
-            issue(b0);
-            E += gather_place(e, glo, E, cand, misc);
-          }
+    if (t4[3] != 0u) {
+      // Mass ties at the top: V is the row's largest key.  When every chunk holding V has
+      // its threshold at V, its count is the number of its keys equal to V (none is
+      // larger); with k of them in all, the list is the first k positions holding V.
+      const uint32_t V = t4[2];
+      uint32_t t2[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        if (u >= upt) break;
+        if (tid + NT * u < wact && hv[u][2] == V) {
+          t2[0] += hv[u][1] & 0xFFFFu;
+          t2[1] |= hv[u][0] != V ? 1u : 0u;
         }
-        done = rare_select(ws, nr, k, wact, E, C, glo, hi, rs, cand, bm, hist, misc, out);
+      }
+      block_sum_max_max_sum(t2, misc);
+      if (t2[1] == 0u && (int)t2[0] >= k) {
+        emit_ordered(srow, nr, k, V + 1u, k, out, misc);
+        done = true;
+      }
+    }
+    if (!done) {
+      // the keys >= t* (not every published key: from about 1,024 chunks a row, the
+      // published keys can pass the LDS capacity while those >= t* fit)
+      int E = 0;
+      bool fits = true;
+      const int per_batch = batch_chunks(G);
+      for (int b0 = 0; b0 < wact; b0 += per_batch) {
+        if (b0 > 0) issue(b0);
+        const int got = gather_place(e, lo, E, cand, misc);
+        if (got < 0) {
+          fits = false;
+          break;
+        }
+        E += got;
+      }
+      if (fits) {
+        pad_cand(cand, E);
+        __syncthreads();
+        if (t4[3] == 0u) {
+          int got = -1;
+          done = select_cand<FIN_ENT / NT>(cand, E, lo, hi, k, hist, misc, out, &got);
+          if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
+        }
+        if (!done && nr <= BITMAP_KEYS && (E >= k || (int)t4[0] <= FIN_ENT)) {
+          uint32_t glo = lo;
+          if (E < k) {
+            // fewer than k keys >= t*: every published key instead, chunk w held from its own t_w
+            glo = 0x00800000u;
+            E = 0;
+            for (int b0 = 0; b0 < wact; b0 += per_batch) {
+              issue(b0);
+              E += gather_place(e, glo, E, cand, misc);
+            }
+          }
+          done = rare_select(ws, nr, k, wact, E, C, glo, hi, rs, cand, bm, hist, misc, out);
+        }
       }
     }
   }
