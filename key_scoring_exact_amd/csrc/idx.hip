@@ -100,7 +100,6 @@ struct KArgs {
   const int32_t* nk;        // int32 [rows]
   float* scores;            // [rows][ld]: written (MODE_SCORE) or read
   int32_t* topk;            // [rows][k]
-  int32_t* slots;           // [rows][k] or null: the lists as physical cache slots
   uint8_t* ws;
   int64_t ld;
   int32_t rows, max_pages, max_keys, num_pages, k;
@@ -109,6 +108,10 @@ struct KArgs {
   int32_t mode;
   int32_t ent_stride;       // candidate blocks per row (>= chunks of a row that selects from candidates)
   uint64_t off_ent;
+  uint32_t grp[IDX_MAX_REQ];// row0 | nrows << 24
+  int32_t gmax[IDX_MAX_REQ];// host bound on the keys of each group's rows
+  uint32_t req[IDX_MAX_REQ];// the group's request: its first row | its rows << 24 (with nw_pos)
+  int32_t* slots;           // [rows][k] or null: the lists as physical cache slots
   // keys written in this launch (null nw_pos: none): row r's key (codes nw_codes[r],
   // scale nw_scales[r]) takes logical position nw_pos[r] (-1: none) of its request
   const uint8_t* nw_codes;  // E4M3 [rows][128]
@@ -116,9 +119,6 @@ struct KArgs {
   const int32_t* nw_pos;    // int32 [rows]
   uint8_t* kc_w;            // the cache, written
   float* ks_w;
-  uint32_t grp[IDX_MAX_REQ];// row0 | nrows << 24
-  int32_t gmax[IDX_MAX_REQ];// host bound on the keys of each group's rows
-  uint32_t req[IDX_MAX_REQ];// the group's request: its first row | its rows << 24 (with nw_pos)
 };
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -958,7 +958,7 @@ struct Patches {
   float nscl;
 };
 
-template <int P, int TS>
+template <int P, int TS, bool PATCH>
 __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R, int c, const int* phys,
                                             const Patches& pt) {
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
@@ -1095,7 +1095,9 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
     if (issued < x + 1) issued = x + 1;
     wait_pages_through(x, issued);
     __syncthreads();
-    if (pt.hit != 0ull) patch_pages(x);
+    if constexpr (PATCH) {
+      if (pt.hit != 0ull) patch_pages(x);
+    }
 #pragma unroll
     for (int j = 0; j < P; j++)
       if (j >= issued && j <= x + LOOKAHEAD) issue_page(j);
@@ -1431,7 +1433,9 @@ __host__ __device__ inline int row_path(int n, int k, int shift) {
 // Launch 1: workgroup (c, g) scores chunk c (keys [c C, c C + C)) of request g's rows
 // and, per row that selects from candidates, publishes the chunk's candidates.
 // ---------------------------------------------------------------------------
-template <int P>
+// PATCH: keys written in this launch (idx_score_topk_append) are patched in; a separate
+// instantiation, so that other calls carry none of it.
+template <int P, bool PATCH>
 __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
@@ -1469,7 +1473,7 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
   // keys written in this launch: the request's rows' codes into L_PATCH (wave 0, two
   // DMAs: lane l of DMA i copies chunk l % 8 of row 8 i + l / 8), their positions and
   // scales with the key counts below (lanes [0, request rows))
-  const uint32_t rq = a.nw_pos != nullptr ? a.req[g] : 0u;
+  const uint32_t rq = PATCH ? a.req[g] : 0u;
   const int rq0 = (int)(rq & 0xFFFFFFu), rqn = (int)(rq >> 24);
   if (do_score && rqn > 0 && wv == 0) {
 #pragma unroll
@@ -1550,7 +1554,7 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
     // the request's new keys in this chunk; a position outside [-1, the row's key
     // count) is reported and ignored (each row's key is within what the row sees)
     Patches pt = {0ull, 0ull, ld_np, ld_ns};
-    if (rqn > 0) {
+    if (PATCH && rqn > 0) {
       const int own = lane - (row0 - rq0);           // this lane's row within the group
       int nown = 0;
 #pragma unroll
@@ -1561,9 +1565,9 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
       pt.hit = __ballot(inr && !bad && ld_np >= chunk_base && ld_np < chunk_base + C && ld_np < nmax);
       pt.mine = __ballot(inr && own >= 0 && own < R);
     }
-    if (R == 1) score_chunk<P, 8>(a, smem, R, c, phys, pt);
-    else if (R == 2) score_chunk<P, 4>(a, smem, R, c, phys, pt);
-    else score_chunk<P, 2>(a, smem, R, c, phys, pt);
+    if (R == 1) score_chunk<P, 8, PATCH>(a, smem, R, c, phys, pt);
+    else if (R == 2) score_chunk<P, 4, PATCH>(a, smem, R, c, phys, pt);
+    else score_chunk<P, 2, PATCH>(a, smem, R, c, phys, pt);
   } else {
 #pragma unroll
     for (int i = 0; i < GR; i++) {
@@ -1874,9 +1878,10 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
 // slots through the row's own page-table row: slot = page_table[row][p / 64] * 64 +
 // p % 64, and -1 for -1 padding (or for a page id outside the pool, which the scoring
 // launch has already reported).
+template <bool SLOTS>
 __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  if (!select_row(a, smem) || a.slots == nullptr) return;
+  if (!select_row(a, smem) || !SLOTS) return;
   __syncthreads();                                   // the list's stores, visible to the workgroup
   const uint32_t ge = a.grp[blockIdx.y];
   const int grow = (int)(ge & 0xFFFFFFu) + (int)blockIdx.x;
@@ -2060,11 +2065,14 @@ constexpr int SELECT_LDS = L_FIN_END;
 
 int set_attrs() {
   if (g_attr_done) return IDX_OK;
-  const void* fs[5] = {(const void*)score_kernel<1>, (const void*)score_kernel<2>, (const void*)score_kernel<4>,
-                       (const void*)score_kernel<8>, (const void*)select_kernel};
-  for (int i = 0; i < 5; i++) {
+  const void* fs[10] = {(const void*)score_kernel<1, false>, (const void*)score_kernel<2, false>,
+                        (const void*)score_kernel<4, false>, (const void*)score_kernel<8, false>,
+                        (const void*)score_kernel<1, true>,  (const void*)score_kernel<2, true>,
+                        (const void*)score_kernel<4, true>,  (const void*)score_kernel<8, true>,
+                        (const void*)select_kernel<false>,   (const void*)select_kernel<true>};
+  for (int i = 0; i < 10; i++) {
     const hipError_t e =
-        hipFuncSetAttribute(fs[i], hipFuncAttributeMaxDynamicSharedMemorySize, i < 4 ? SCORE_LDS : SELECT_LDS);
+        hipFuncSetAttribute(fs[i], hipFuncAttributeMaxDynamicSharedMemorySize, i < 8 ? SCORE_LDS : SELECT_LDS);
     if (e != hipSuccess) return hip_fail(e);
   }
   g_attr_done = true;
@@ -2077,17 +2085,25 @@ int launch(const KArgs& args, int P, dim3 grid, bool score_launch, bool select_l
   int rc = set_attrs();
   if (rc) return rc;
   if (score_launch) {
-    switch (P) {
-      case 1: hipLaunchKernelGGL(score_kernel<1>, grid, dim3(NT), SCORE_LDS, st, args); break;
-      case 2: hipLaunchKernelGGL(score_kernel<2>, grid, dim3(NT), SCORE_LDS, st, args); break;
-      case 4: hipLaunchKernelGGL(score_kernel<4>, grid, dim3(NT), SCORE_LDS, st, args); break;
-      default: hipLaunchKernelGGL(score_kernel<8>, grid, dim3(NT), SCORE_LDS, st, args); break;
+    const bool patch = args.nw_pos != nullptr;
+    switch (P + (patch ? 16 : 0)) {
+      case 1: hipLaunchKernelGGL((score_kernel<1, false>), grid, dim3(NT), SCORE_LDS, st, args); break;
+      case 2: hipLaunchKernelGGL((score_kernel<2, false>), grid, dim3(NT), SCORE_LDS, st, args); break;
+      case 4: hipLaunchKernelGGL((score_kernel<4, false>), grid, dim3(NT), SCORE_LDS, st, args); break;
+      case 8: hipLaunchKernelGGL((score_kernel<8, false>), grid, dim3(NT), SCORE_LDS, st, args); break;
+      case 17: hipLaunchKernelGGL((score_kernel<1, true>), grid, dim3(NT), SCORE_LDS, st, args); break;
+      case 18: hipLaunchKernelGGL((score_kernel<2, true>), grid, dim3(NT), SCORE_LDS, st, args); break;
+      case 20: hipLaunchKernelGGL((score_kernel<4, true>), grid, dim3(NT), SCORE_LDS, st, args); break;
+      default: hipLaunchKernelGGL((score_kernel<8, true>), grid, dim3(NT), SCORE_LDS, st, args); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e);
   }
   if (select_launch) {
-    hipLaunchKernelGGL(select_kernel, dim3(IDX_GROUP_ROWS, grid.y), dim3(NT), SELECT_LDS, st, args);
+    if (args.slots)
+      hipLaunchKernelGGL(select_kernel<true>, dim3(IDX_GROUP_ROWS, grid.y), dim3(NT), SELECT_LDS, st, args);
+    else
+      hipLaunchKernelGGL(select_kernel<false>, dim3(IDX_GROUP_ROWS, grid.y), dim3(NT), SELECT_LDS, st, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e);
   }
