@@ -53,7 +53,7 @@ constexpr int NT = 512;                 // threads per workgroup: 8 waves, two p
 constexpr int NWAVE = NT / 64;
 constexpr int PMAX = 8;                 // pages per workgroup at most
 constexpr int CMAX = PMAX * PS;         // keys per chunk at most (512)
-constexpr int LOOKAHEAD = PMAX - 1;     // pages in flight ahead of the page being scored (all of them)
+constexpr int LOOKAHEAD = 3;            // pages in flight ahead of the page being scored
 constexpr int ALL_MAX = 24576;          // rows up to this many keys select from all scores at once
 constexpr int FIN_ENT = 12288;          // candidate capacity of a selecting workgroup
 constexpr int BITMAP_KEYS = 131072;     // positions covered by the finisher's LDS bitmap
