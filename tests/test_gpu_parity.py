@@ -164,3 +164,22 @@ def test_slot_output(contexts, rows):
     assert np.array_equal(sl, O.list_slots(prob, ls))
     res = dict(scores=sc.cpu().numpy(), lists=ls, scores_only=sc.cpu().numpy(), lists_topk=ls, code=0, detail=0)
     check_against_oracle(prob, res)
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_sweep(case):
+    """Seeded random problems: 1-4 requests of 1-8 rows, 0-60,000 keys a request, every
+    key cache kind, k from 1 to 2048, chains or full-context rows, spare pool pages."""
+    rng = np.random.default_rng(12345 + case)
+    nreq = int(rng.integers(1, 5))
+    contexts = [int(rng.choice([0, 1, 63, 64, 65, 2047, 2048, 2049]) if rng.random() < 0.3
+                    else rng.integers(1, 60000)) for _ in range(nreq)]
+    rows = [int(rng.integers(1, 9)) for _ in range(nreq)]
+    k = int(rng.choice([1, 7, 64, 300, 1024, 2048]))
+    keys = str(rng.choice(["normal", "normal", "ties", "zeros", "recent"]))
+    chain = bool(rng.random() < 0.7)
+    prob = make_problem(contexts, rows, seed=50000 + case, k=k, keys=keys, recent=int(rng.integers(64, 8192)),
+                        chain=chain, pad_pages=int(rng.integers(0, 5)), name=f"sweep{case}")
+    print(f"case sweep{case} contexts={contexts} rows={rows} k={k} keys={keys} chain={chain}", flush=True)
+    bounds = [int(prob.n_keys[a:b].max()) for a, b in zip(prob.req_indptr[:-1], prob.req_indptr[1:])]
+    check_against_oracle(prob, run_all(prob, req_max_keys=bounds if case % 2 else None))
