@@ -82,6 +82,7 @@ constexpr int L_FIN_END = L_BM + BITMAP_KEYS / 8;
 static_assert(BITMAP_KEYS / 8 >= 4 * NT * 8, "the failing-chunk list (2 words a chunk) fits the bitmap");
 static_assert(ALL_MAX % (4 * NT) == 0 && FIN_ENT % (4 * NT) == 0, "register segments of whole slot groups");
 static_assert(ALL_MAX * 4 <= FIN_ENT * 8, "all-keys rows fit the candidate area");
+static_assert(IDX_KMAX <= 4 * NT && IDX_KMAX <= BITMAP_KEYS / 32, "a list is four entries a thread and fits the bitmap area");
 static_assert(L_CAND % 16 == 0, "16-byte candidate reads");
 static_assert(CAP_MAX == 128, "a chunk's candidate block has at most four 32-slot groups");
 static_assert(L_SCORE_END <= 160 * 1024 && L_FIN_END <= 160 * 1024, "LDS budget");
@@ -1323,6 +1324,85 @@ __device__ __forceinline__ bool select_all(uint32_t* fk, int n, uint32_t lo, uin
   return true;
 }
 
+// The list of the keys >= Tge among cand[0 .. E1), when cand[0 .. E0) and cand[E0 .. E1)
+// each hold distinct positions in ascending order (and no position is in both): each
+// run's kept positions are compacted in order into buf (wave ballots, one block scan),
+// then the two sorted runs are merged, thread t writing list entries [4 t, 4 t + 4)
+// from the split a binary search finds on its diagonal (merge path).  The work is
+// spread over the entries however the kept ones crowd together.  buf holds k words.
+// Returns the number kept.  Every thread must call.
+__device__ __forceinline__ int emit_merged(const uint64_t* cand, int E0, int E1, uint32_t Tge, int k, uint32_t* buf,
+                                           int* misc, int32_t* out) {
+  constexpr int SR = FIN_ENT / NT;
+  static_assert(SR * 64 * NWAVE == FIN_ENT, "the waves' ranges tile the candidate area");
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  // wave wv takes entries [wv L, wv L + L), L = 64 nj
+  const int nj = __builtin_amdgcn_readfirstlane((E1 + 64 * NWAVE - 1) / (64 * NWAVE));
+  const int e0 = wv * nj * 64;
+  int rk[SR];
+  uint32_t ps[SR];
+  int cnt = 0, cntA = 0;
+  // every load first (e < NWAVE nj 64 + SR 64 <= FIN_ENT stays in the candidate area;
+  // entries past the wave's range or E1 are masked), then the ballots
+  uint64_t cv[SR];
+#pragma unroll
+  for (int j = 0; j < SR; j++) cv[j] = cand[e0 + j * 64 + lane];
+#pragma unroll
+  for (int j = 0; j < SR; j++) {
+    const int e = e0 + j * 64 + lane;
+    const bool keep = (j < nj) & (e < E1) & ((uint32_t)(cv[j] >> 32) >= Tge);
+    const uint64_t m = __ballot(keep);
+    const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    rk[j] = keep ? cnt + below : -1;
+    ps[j] = (uint32_t)cv[j];
+    cnt += (int)__popcll(m);
+    cntA += (int)__popcll(m & __ballot(e < E0));
+  }
+  __syncthreads();                                    // misc may still be read by the caller's last step
+  if (lane == 0) {
+    misc[wv] = cnt;
+    misc[NWAVE + wv] = cntA;
+  }
+  __syncthreads();
+  int off = 0, tot = 0, ka = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; i++) {
+    off += i < wv ? misc[i] : 0;
+    tot += misc[i];
+    ka += misc[NWAVE + i];
+  }
+  // a dropped entry writes a dummy word past the k the list takes
+#pragma unroll
+  for (int j = 0; j < SR; j++) buf[rk[j] >= 0 && off + rk[j] < k ? off + rk[j] : IDX_KMAX + lane] = ps[j];
+  __syncthreads();
+  const int kept = tot < k ? tot : k;
+  const int kA = ka < kept ? ka : kept, kB = kept - kA;
+  const uint32_t* A = buf;
+  const uint32_t* B = buf + kA;
+  const int d = min(4 * tid, kept);
+  // ia = how many of the first d list entries come from A
+  int lo = max(0, d - kB), hi = min(d, kA);
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (A[mid] < B[d - 1 - mid]) lo = mid + 1;
+    else hi = mid;
+  }
+  int ia = lo, ib = d - lo;
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    if (d + u < kept) {
+      const uint32_t va = ia < kA ? A[ia] : 0xFFFFFFFFu;
+      const uint32_t vb = ib < kB ? B[ib] : 0xFFFFFFFFu;
+      const bool fromA = va < vb;
+      out[d + u] = (int32_t)(fromA ? va : vb);
+      ia += fromA ? 1 : 0;
+      ib += fromA ? 0 : 1;
+    }
+  }
+  __syncthreads();
+  return tot;
+}
+
 // Candidate path when the certificate fails.  cand[0 .. E) holds every published key >=
 // lo (chunk w published its keys >= bm[w]; bm[w] = 0xFFFFFFFF marks an overflowed chunk,
 // which published none), so chunk w holds its keys >= held(w) = max(bm[w], lo); every key
@@ -1338,11 +1418,25 @@ __device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact
   const int tid = threadIdx.x;
   constexpr int SR = FIN_ENT / NT;
   uint32_t kr[SR];
+  // the keys into registers, and their range: lo is only a floor (the smallest finite
+  // score's key when every published key is taken), and the linear pass of kth_select
+  // resolves only over a range close to that of the keys
+  uint32_t kmn, kmx;
   auto load_keys = [&](int n_ent) {
     const int S = slots_for(n_ent);
-    const uint64_t* src = cand + tid * S;
+    kmn = 0xFFFFFFFFu;
+    kmx = 0u;
+    uint64_t cv[SR];
 #pragma unroll
-    for (int j = 0; j < SR; j++) kr[j] = j < S ? (uint32_t)(src[j] >> 32) : 0u;
+    for (int j = 0; j < SR; j++) cv[j] = cand[j * NT + tid];   // within the candidate area
+#pragma unroll
+    for (int j = 0; j < SR; j++) {
+      // kth_select takes the keys in any arrangement: slot j of thread t is entry j NT + t
+      kr[j] = j < S ? (uint32_t)(cv[j] >> 32) : 0u;
+      kmn = min(kmn, kr[j] != 0u ? kr[j] : 0xFFFFFFFFu);
+      kmx = max(kmx, kr[j]);
+    }
+    block_min_max(kmn, kmx, misc);
     return S;
   };
   uint32_t T = 0;
@@ -1351,7 +1445,7 @@ __device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact
   clear_hist(hist);
   __syncthreads();
   const int S0 = load_keys(E);
-  const bool full = E >= k && kth_select<SR>(kr, S0, E, lo, hi, k, hist, misc, &T, &rem);
+  const bool full = E >= k && kth_select<SR>(kr, S0, E, kmn, kmx, k, hist, misc, &T, &rem);
   // the k-th largest candidate is Tge - 1 when ties are cut, else at least Tge
   const uint32_t lowT = full ? (rem > 0 ? T - 1u : T) : 0u;
   // failing chunks listed in bm[4 NT ...] (the thresholds occupy bm[0 .. 4 NT))
@@ -1370,8 +1464,9 @@ __device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact
     nfail += tot;
   }
   __syncthreads();
-  // the failing chunks' keys in [lowT, held(w)), in one pass over all of them (8 keys a
-  // thread a round; the candidate order is free, the emission goes through a bitmap).
+  // the failing chunks' keys in [lowT, held(w)), in one pass over all of them: 8
+  // consecutive keys a thread a round (a chunk holds a multiple of 8), appended in
+  // thread order, so that cand[E .. Ecur) is in position order as cand[0 .. E) is.
   // Give up once they overflow the candidate area, or at once without a T0 (every key
   // of every chunk would be taken) when the chunks hold too many keys.
   if (!full && E + nfail * C > FIN_ENT) return false;
@@ -1382,13 +1477,23 @@ __device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact
   for (int base = 0; base < tot_keys; base += NT * 8) {
     uint32_t raw[8];
     int pos[8];
+    const int f0 = base + tid * 8;
+    const int p0 = f0 < tot_keys ? ((int)fl[f0 >> cshift] << cshift) + (f0 & (C - 1)) : nr;
+    if (p0 + 8 <= nr) {
+      const v4u x = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, p0 * 4, 0, 0));
+      const v4u y = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, p0 * 4 + 16, 0, 0));
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const int f = base + j * NT + tid;
-      const int w = f < tot_keys ? (int)fl[f >> cshift] : 0;
-      pos[j] = f < tot_keys ? (w << cshift) + (f & (C - 1)) : nr;
-      raw[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, pos[j] < nr ? pos[j] * 4 : 0x7FFFFFF0, 0, 0);
+      for (int j = 0; j < 4; j++) {
+        raw[j] = x[j];
+        raw[4 + j] = y[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; j++)
+        raw[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, p0 + j < nr ? (p0 + j) * 4 : 0x7FFFFFF0, 0, 0);
     }
+#pragma unroll
+    for (int j = 0; j < 8; j++) pos[j] = p0 + j;
     uint32_t key[8];
     int cnt = 0;
 #pragma unroll
@@ -1411,10 +1516,11 @@ __device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact
   clear_hist(hist);
   __syncthreads();
   const int S1 = load_keys(Ecur);
-  const uint32_t lo2 = min(lo, max(lowT, 0x00800000u));   // every candidate is >= lo2
-  if (!kth_select<SR>(kr, S1, Ecur, lo2, hi, k, hist, misc, &T, &rem)) return false;
-  // select_explicit takes keys > Tge - 1 and the first rem keys equal to Tge - 1
-  const int got = select_explicit(cand, Ecur, nr, k, T - 1u, rem, bm, misc, out);
+  if (!kth_select<SR>(kr, S1, Ecur, kmn, kmx, k, hist, misc, &T, &rem)) return false;
+  // without ties to cut, a merge of the two runs in position order; else select_explicit
+  // (keys > Tge - 1 and the first rem keys equal to Tge - 1)
+  const int got = rem == 0 ? emit_merged(cand, E, Ecur, T, k, bm, misc, out)
+                           : select_explicit(cand, Ecur, nr, k, T - 1u, rem, bm, misc, out);
   if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
   return true;
 }
@@ -1857,7 +1963,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
             glo = 0x00800000u;
             E = 0;
             for (int b0 = 0; b0 < wact; b0 += per_batch) {
-              issue(b0);
+              if (wact > per_batch) issue(b0);         // else e still holds the one batch
               E += gather_place(e, glo, E, cand, misc);
             }
           }
