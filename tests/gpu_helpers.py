@@ -9,16 +9,17 @@ from oracle import check as C
 from oracle import indexer as O
 
 
-def device_problem(prob, req_max_keys=None):
+def device_problem(prob, req_max_keys=None, max_keys=None):
     B.ensure_built()
     return idx.DeviceProblem.from_arrays(prob.q, prob.w, prob.k_cache, prob.k_scale, prob.page_table,
-                                         prob.n_keys, prob.req_indptr, max_keys=prob.max_keys,
+                                         prob.n_keys, prob.req_indptr,
+                                         max_keys=prob.max_keys if max_keys is None else max_keys,
                                          req_max_keys=req_max_keys)
 
 
-def run_all(prob, ws=None, req_max_keys=None):
+def run_all(prob, ws=None, req_max_keys=None, max_keys=None):
     """Fused call, score-only call and top-k over the fused call's scores."""
-    dp = device_problem(prob, req_max_keys)
+    dp = device_problem(prob, req_max_keys, max_keys)
     if ws is None:
         ws = idx.Workspace(prob.rows, dp.max_keys, prob.k)
     ld = max(1, dp.max_keys)

@@ -127,6 +127,23 @@ def test_stale_workspace_contents_are_ignored():
         check_against_oracle(prob, res)
 
 
+@pytest.mark.parametrize("cut", [11072, 31072])
+def test_rows_below_the_call_bound_ignore_older_blocks(cut):
+    """Rows shorter than the call's key bound (no per-request bound) read only the
+    candidate blocks of their own chunks: the workspace first holds the blocks of a call
+    over the full rows, which look valid past the short rows (cut 11,072: 119,997..
+    120,000 keys, the block size of the bound; cut 31,072: a larger block)."""
+    import key_scoring_exact_amd as idx
+    full = make_problem([131072], [4], seed=21, name="full")
+    ws = idx.Workspace(full.rows, full.max_keys, full.k)
+    check_against_oracle(full, run_all(full, ws=ws))
+    short = make_problem([131072], [4], seed=21, name=f"short{cut}")
+    short.n_keys = (full.n_keys - cut).astype(np.int32)
+    print(f"case cut={cut} n={short.n_keys.tolist()}", flush=True)
+    res = run_all(short, ws=ws, max_keys=full.max_keys)
+    check_against_oracle(short, res)
+
+
 @pytest.mark.parametrize("rows,n", [(5, 3000), (8, 9000), (8, 40000), (6, 131072)])
 def test_long_verify_chains(rows, n):
     """More than four verify rows in a request: the rows are scored in groups of at most
