@@ -73,6 +73,33 @@ def test_ties_zeros_and_recent_small():
                     assert res["lists"][r].tolist() == list(range(prob.k))
 
 
+@pytest.mark.parametrize("distinct", [15, 31])
+def test_recent_region_of_repeated_keys(distinct):
+    """The last 4,096 positions of a 131,072-key request (scaled x8, as in the recent
+    cache) repeat `distinct` key vectors, position p taking the vector of p mod
+    `distinct`.  The 8 chunks there overflow their caps and publish nothing, so every
+    row re-reads them.  With this seed, rows 1 and 2 cut a tie at the k-th key among
+    the re-read keys (273 or 132 positions share it, some selected): the list goes
+    through the position bitmap.  Rows 0 and 3 end with no tie to cut: the two
+    position-ordered runs are merged."""
+    prob = make_problem([131072], [4], seed=31, keys="recent", name=f"recent_rep{distinct}")
+    n, lo = 131072, 131072 - 4096
+    pt = prob.page_table[0]
+    pos = np.arange(lo, n)
+    src = lo + (pos - lo) % distinct
+    prob.k_cache[pt[pos // 64], pos % 64] = prob.k_cache[pt[src // 64], src % 64]
+    prob.k_scale[pt[pos // 64], pos % 64] = prob.k_scale[pt[src // 64], src % 64]
+    print(f"case recent_rep distinct={distinct}", flush=True)
+    res = run_all(prob)
+    check_against_oracle(prob, res)
+    g = res["scores"]
+    for r in (1, 2):
+        # the k-th score (GPU's own) is shared by positions in and out of the list
+        s = g[r, : int(prob.n_keys[r])].astype(np.float64)
+        kth = np.sort(s)[::-1][prob.k - 1]
+        assert np.sum(s == kth) > 1 and np.sum(s > kth) < prob.k - 1, (distinct, r)
+
+
 @pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4a", "c4b", "c4c"])
 def test_full_config(name):
     prob = make_config(name)
