@@ -82,7 +82,8 @@ constexpr int L_FIN_END = L_BM + BITMAP_KEYS / 8;
 static_assert(BITMAP_KEYS / 8 >= 4 * NT * 8, "the failing-chunk list (2 words a chunk) fits the bitmap");
 static_assert(ALL_MAX % (4 * NT) == 0 && FIN_ENT % (4 * NT) == 0, "register segments of whole slot groups");
 static_assert(ALL_MAX * 4 <= FIN_ENT * 8, "all-keys rows fit the candidate area");
-static_assert(IDX_KMAX <= 4 * NT && IDX_KMAX <= BITMAP_KEYS / 32, "a list is four entries a thread and fits the bitmap area");
+static_assert(IDX_KMAX <= 4 * NT && IDX_KMAX + 64 <= BITMAP_KEYS / 32,
+              "a list is four entries a thread; it and 64 dummy words fit the bitmap area");
 static_assert(L_CAND % 16 == 0, "16-byte candidate reads");
 static_assert(CAP_MAX == 128, "a chunk's candidate block has at most four 32-slot groups");
 static_assert(L_SCORE_END <= 160 * 1024 && L_FIN_END <= 160 * 1024, "LDS budget");
@@ -1405,15 +1406,16 @@ __device__ __forceinline__ int emit_merged(const uint64_t* cand, int E0, int E1,
 
 // Candidate path when the certificate fails.  cand[0 .. E) holds every published key >=
 // lo (chunk w published its keys >= bm[w]; bm[w] = 0xFFFFFFFF marks an overflowed chunk,
-// which published none), so chunk w holds its keys >= held(w) = max(bm[w], lo); every key
-// of the row is <= hi.  T0 = the k-th candidate (if there are k), at most the row's k-th
-// key; every chunk whose held range does not reach down to T0 is re-read from the row's
-// scores for its keys in [T0, held(w)), after which every key >= T0 of the row is a
-// candidate, and the top k is taken from that set through a position bitmap.  Returns
-// true when it selected, false to fall back to the multi-pass select over memory.  Every
-// thread must call.
+// which published none), so chunk w holds its keys >= held(w) = max(bm[w], lo).  T0 =
+// the k-th candidate (if there are k), at most the row's k-th key; every chunk whose
+// held range does not reach down to T0 is re-read from the row's scores for its keys in
+// [T0, held(w)), after which every key >= T0 of the row is a candidate, and the top k is
+// taken from that set: by merging the two position-ordered runs (emit_merged), or
+// through a position bitmap when a tie at the k-th key is cut (select_explicit).
+// Returns true when it selected, false to fall back to the multi-pass select over
+// memory.  Every thread must call.
 __device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact, int E, int C, uint32_t lo,
-                                            uint32_t hi, __amdgpu_buffer_rsrc_t rs, uint64_t* cand, uint32_t* bm,
+                                            __amdgpu_buffer_rsrc_t rs, uint64_t* cand, uint32_t* bm,
                                             uint32_t* hist, int* misc, int32_t* out) {
   const int tid = threadIdx.x;
   constexpr int SR = FIN_ENT / NT;
@@ -1967,7 +1969,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
               E += gather_place(e, glo, E, cand, misc);
             }
           }
-          done = rare_select(ws, nr, k, wact, E, C, glo, hi, rs, cand, bm, hist, misc, out);
+          done = rare_select(ws, nr, k, wact, E, C, glo, rs, cand, bm, hist, misc, out);
         }
       }
     }
