@@ -869,20 +869,34 @@ __device__ inline void candidate_params(int n, int C, int k, int* m, int* cap, i
   *groups = G;
 }
 
-// A chunk's local threshold from one histogram, with no bisection: the 512 scores of a
-// full chunk (8 a lane, fv / their radix keys kr, every key present) are counted into
-// 128 bins linear in the score over [smallest lane maximum, largest score], which holds
-// at least the 64 lane maxima, so at least m keys (m <= 64).  Bin b* is the first, from
-// the top, whose running count reaches m.  The bin index is a monotone function of the
-// score, so the keys of bins <= b* are exactly the keys >= the smallest of them, which
-// becomes t.  Returns false (the caller bisects instead) when the chunk is partial, all
-// lane maxima are equal, the span is not finite, or more than cap keys would publish.
+// A chunk's local threshold from one histogram, with no bisection: the chunk's scores
+// (8 a lane, fv / their radix keys kr, 0 where no key) are counted into 128 bins linear
+// in the score over [lo, largest score].  lo is the smallest lane maximum when every
+// lane holds keys (the range then holds at least the 64 lane maxima, so at least m keys,
+// m <= 64), else the smallest key present (every key is counted).  Bin b* is the first,
+// from the top, whose running count reaches m.  The bin index is a monotone function of
+// the score, so the keys of bins <= b* are exactly the keys >= the smallest of them,
+// which becomes t.  Returns false (the caller bisects instead) when all keys in range
+// are equal, the span is not finite, fewer than m keys are counted, or more than cap
+// keys would publish.
 // hst: 128 words of LDS owned by this wave.  All 64 lanes must call.
 __device__ __forceinline__ bool chunk_bound_linear(const float (&fv)[8], const uint32_t (&kr)[8], uint32_t lmax,
                                                    uint32_t cmax, int m, int cap, uint32_t* hst, uint32_t* t) {
   const int lane = lane_id();
-  if (__ballot(lmax == 0u) != 0ull) return false;
-  const uint32_t lmin = wave_min_u32(lmax);
+  // The range starts at the smallest lane maximum when every lane holds keys (at least
+  // 64 keys lie at or above it).  A lane without keys (a row's last chunk, or a chunk
+  // of fewer than 512 keys, whose keys sit in the low lanes) would make that bound 0:
+  // then the range starts at the smallest key present, so every key is counted.
+  uint32_t lmin;
+  if (__ballot(lmax == 0u) == 0ull) {
+    lmin = wave_min_u32(lmax);
+  } else {
+    uint32_t kmn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < 8; j++) kmn = kr[j] != 0u ? min(kmn, kr[j]) : kmn;
+    lmin = wave_min_u32(kmn);
+    if (lmin == 0xFFFFFFFFu) return false;          // no key at all
+  }
   if (lmin == cmax) return false;
   const float hf = key_float(cmax), lf = key_float(lmin);
   const float span = hf - lf;
