@@ -878,7 +878,7 @@ __device__ inline void candidate_params(int n, int C, int k, int* m, int* cap, i
 // the score, so the keys of bins <= b* are exactly the keys >= the smallest of them,
 // which becomes t.  Returns false (the caller bisects instead) when all keys in range
 // are equal, the span is not finite, fewer than m keys are counted, or more than cap
-// keys would publish.
+// keys would publish and not all of them equal the chunk's maximum.
 // hst: 128 words of LDS owned by this wave.  All 64 lanes must call.
 __device__ __forceinline__ bool chunk_bound_linear(const float (&fv)[8], const uint32_t (&kr)[8], uint32_t lmax,
                                                    uint32_t cmax, int m, int cap, uint32_t* hst, uint32_t* t) {
@@ -924,12 +924,13 @@ __device__ __forceinline__ bool chunk_bound_linear(const float (&fv)[8], const u
   const bool first = ((__ballot(incl - c1 >= m) >> f) & 1ull) != 0ull;
   const uint32_t bstar = 2u * (uint32_t)f + (first ? 0u : 1u);
   const int count = __builtin_amdgcn_readlane(first ? incl - c1 : incl, f);
-  if (count > cap) return false;
   uint32_t mn = 0xFFFFFFFFu;
 #pragma unroll
   for (int j = 0; j < 8; j++) mn = bn[j] <= bstar ? min(mn, kr[j]) : mn;
   *t = wave_min_u32(mn);
-  return true;
+  // past cap, a bisection may find a tighter bound, unless every key counted equals the
+  // chunk's maximum (a tie at the top): then t is exact and the chunk overflows with it
+  return count <= cap || *t == cmax;
 }
 
 // Whether any / every thread of the workgroup holds p (misc[48 .. 56) as scratch).
@@ -1930,21 +1931,19 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
     const uint32_t lo = t4[1] > 0x00800000u ? t4[1] : 0x00800000u;
     const uint32_t hi = t4[2] > lo ? t4[2] : lo;
     if (t4[3] != 0u) {
-      // Mass ties at the top: V is the row's largest key.  When every chunk holding V has
-      // its threshold at V, its count is the number of its keys equal to V (none is
-      // larger); with k of them in all, the list is the first k positions holding V.
+      // Mass ties at the top: V is the row's largest key.  A chunk whose threshold is V
+      // counts exactly its keys equal to V (none is larger).  When such chunks hold k of
+      // them in all, the list is the first k positions holding V, whatever the other
+      // chunks hold (the ordered emission reads every position).
       const uint32_t V = t4[2];
       uint32_t t2[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int u = 0; u < 4; u++) {
         if (u >= upt) break;
-        if (tid + NT * u < wact && hv[u][2] == V) {
-          t2[0] += hv[u][1] & 0xFFFFu;
-          t2[1] |= hv[u][0] != V ? 1u : 0u;
-        }
+        if (tid + NT * u < wact && hv[u][0] == V) t2[0] += hv[u][1] & 0xFFFFu;
       }
       block_sum_max_max_sum(t2, misc);
-      if (t2[1] == 0u && (int)t2[0] >= k) {
+      if ((int)t2[0] >= k) {
         emit_ordered(srow, nr, k, V + 1u, k, out, misc);
         done = true;
       }
