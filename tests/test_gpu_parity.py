@@ -73,6 +73,23 @@ def test_ties_zeros_and_recent_small():
                     assert res["lists"][r].tolist() == list(range(prob.k))
 
 
+@pytest.mark.parametrize("n", [30000, 40000, 60000])
+def test_ties_with_small_chunks(n):
+    """The ties cache (4 key vectors, position p carries vector p mod 4) on rows that use
+    128- or 256-key chunks, the last one partial: the list is the first k positions
+    holding the row's largest score (a closed form over the GPU's own scores)."""
+    prob = make_problem([n], [4], seed=9100 + n, keys="ties", name=f"ties{n}")
+    print(f"case ties n={n}", flush=True)
+    res = run_all(prob)
+    check_against_oracle(prob, res)
+    for r in range(prob.rows):
+        v = res["scores"][r]
+        nr = int(prob.n_keys[r])
+        best = max(v[j] for j in range(4))
+        J = [j for j in range(4) if v[j] == best]
+        assert res["lists"][r].tolist() == [p for p in range(nr) if p % 4 in J][: prob.k], (n, r)
+
+
 @pytest.mark.parametrize("distinct", [15, 31])
 def test_recent_region_of_repeated_keys(distinct):
     """The last 4,096 positions of a 131,072-key request (scaled x8, as in the recent
