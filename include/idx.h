@@ -130,15 +130,16 @@ int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys,
 int idx_score_topk(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores,
                    int32_t* topk, void* ws, size_t ws_bytes, void* stream);
 
-/* Keys written in the same launch (the indexer page, Modifications item 2, "keys this
- * launch writes": each verify row publishes its own new index key as FP8 values and a
- * scale, and a scoring pass holding that position patches it in from those pairs, for
- * every row of the request, since the cache store need not be visible yet).  Row r's
- * key, codes[r][0..128) (E4M3FN) and scales[r] (f32, finite, >= 0), takes logical
- * position pos[r] of its request: physical slot page_table[r][pos / 64] * 64 + pos % 64.
- * pos[r] = -1: the row writes no key.  0 <= pos[r] < n_keys[r] otherwise (a row sees
- * its own key); other values raise IDX_DERR_NKEYS and are ignored.  Device pointers;
- * codes 16-byte aligned. */
+/* Keys written in the same launch (the indexer page, Modifications item 2, on the keys a
+ * launch writes: each verify row hands over its new index key as FP8 codes plus a scale,
+ * and every scoring pass whose pages hold that position substitutes the key from that
+ * hand-over for every row of the request, because the store to the cache may not have
+ * reached memory when another pass reads the page).  Row r's key, codes[r][0..128)
+ * (E4M3FN) and scales[r] (f32, finite, >= 0), takes logical position pos[r] of its
+ * request: physical slot page_table[r][pos / 64] * 64 + pos % 64.  pos[r] = -1: the row
+ * writes no key.  0 <= pos[r] < n_keys[r] otherwise (a row sees its own key); other
+ * values raise IDX_DERR_NKEYS and the key is dropped by every row group of the request.
+ * Device pointers; codes 16-byte aligned. */
 typedef struct idx_new_keys {
   const uint8_t* codes;    /* E4M3FN [rows][128] */
   const float* scales;     /* f32 [rows] */

@@ -2,21 +2,22 @@
 
 TEST INFRASTRUCTURE ONLY (see oracle/indexer.py).
 
-Follows the checks of the GLM-5.3 indexer page (sgl-amd-mono-upstream pull
-request 18), Modifications item 0:
+The checks restate those of the GLM-5.3 indexer page (sgl-amd-mono-upstream pull
+request 18), Modifications item 0, in this project's terms:
 
-* scores: the error against the f64 reference, taken over the row's largest
-  reference score, must stay within 1e-4.  "Largest" is read as the largest
-  in magnitude, M_r = max_p |v[p]|; when M_r is 0 the scores must be exactly 0;
-* the list: entry by entry against the exact selection of the launch's own
-  scores (so a key within rounding of the threshold cannot make a correct
-  kernel fail);
-* "missed": how many keys of the exact top-k of the reference scores the
-  list lacks (reported, not gated);
-* negative controls on copies of each row's result (a selected entry
-  replaced by the best unselected key, two entries swapped, one score's bits
-  flipped) must each fail;
-* SHA-256 digests of every row's scores and list.
+* scores: compared with the f64 oracle; the largest absolute difference over a row,
+  divided by the row's largest oracle score, may not exceed 1e-4.  "Largest" is read
+  as the largest in magnitude, M_r = max_p |v[p]|; a row with M_r = 0 must match
+  exactly;
+* the list: compared entry by entry with the exact selection computed from the GPU's
+  own scores, so a key that rounding puts on either side of the threshold cannot fail
+  a correct kernel;
+* "missed": the number of positions of the exact top-k of the oracle's scores that
+  the GPU list does not contain (reported only);
+* negative controls: three deliberately damaged copies of a row's result (one chosen
+  position traded for the best position left out, two list entries exchanged, one
+  bit of one score inverted), each of which the checks above must reject;
+* SHA-256 digests of each row's scores and list, for comparing runs.
 """
 from __future__ import annotations
 

@@ -3,10 +3,11 @@
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or execute
 this module; only tests use it.  It shares no code with the GPU library.
 
-What is computed (the GLM-5.3 indexer page, Modifications item 2, "the query once a
-row": each row's index query is roped and Hadamard-transformed once and published in
-bf16; Modifications item 0 builds its f64 reference from that query, rotated and
-transformed in f32 as the kernel does, then rounded to bf16).  The page gives no
+What is computed (the GLM-5.3 indexer page, Modifications item 2, on preparing the
+query once a row: each row's index query gets its rotary embedding and the Hadamard
+transform a single time and is stored as bf16; Modifications item 0 derives its f64
+score reference from that prepared query, whose arithmetic is f32 with one final
+rounding to bf16).  The page gives no
 formula; the plain reading taken here, per row r and head h, with x = q_pre[r, h, :]:
 
 * RoPE on the first ``rope_dim`` dimensions (rope_dim even), with the caller's

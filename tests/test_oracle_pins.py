@@ -235,3 +235,73 @@ def test_list_slots_identity_and_permutation():
     got = O.list_slots(prob, lists)
     assert got[0, 0] == 3 * 64 and got[0, 2] == 3 * 64 + 63 and got[0, 3] == 0 and got[0, 5] == 2 * 64 + 43
     assert got[0, 6] == -1 and got[1, 2] == 4 * 64
+
+
+def _hand_problem():
+    """Three rows in two requests over a pool of four pages of two keys (D = 3, H = 1):
+    rows 0 and 1 (request 0) map logical pages 0, 1 to physical pages 2, 0; row 2
+    (request 1) maps its one logical page to physical page 1.  Page 3 is spare."""
+    from workloads.synth import Problem
+    kc = np.zeros((4, 2, 3), dtype=np.uint8)
+    kc[...] = np.arange(24, dtype=np.uint8).reshape(4, 2, 3)   # distinct finite codes
+    ks = (np.arange(8, dtype=np.float32).reshape(4, 2) + 1) / 4
+    pt = np.array([[2, 0], [2, 0], [1, 1]], dtype=np.int32)
+    return Problem(name="hand", q=_bf16(np.ones((3, 1, 3))), w=_bf16(np.ones((3, 1))), k_cache=kc, k_scale=ks,
+                   page_table=pt, n_keys=np.array([4, 4, 2], dtype=np.int32),
+                   req_indptr=np.array([0, 2, 3], dtype=np.int32), k=2, seed=0, heads=1, dim=3, page_size=2)
+
+
+def test_with_new_keys_hand_worked():
+    """Row 0 writes logical position 3: logical page 1 of its table is physical page 0,
+    so flat slot 0 * 2 + 1 = 1.  Row 1 writes nothing (pos = -1).  Row 2 writes logical
+    position 0 through its own table: physical page 1, flat slot 2.  Nothing else
+    changes, and the inputs are left as they were."""
+    prob = _hand_problem()
+    kc0, ks0, pt0 = prob.k_cache.copy(), prob.k_scale.copy(), prob.page_table.copy()
+    codes = np.array([[0x38, 0x40, 0x30], [0x01, 0x02, 0x03], [0xB8, 0x48, 0x00]], dtype=np.uint8)
+    scales = np.array([0.5, 9.0, 2.0], dtype=np.float32)
+    pos = np.array([3, -1, 0], dtype=np.int32)
+    out = O.with_new_keys(prob, codes, scales, pos)
+    flat_c = out.k_cache.reshape(-1, 3)
+    flat_s = out.k_scale.reshape(-1)
+    want_c = kc0.reshape(-1, 3).copy()
+    want_s = ks0.reshape(-1).copy()
+    want_c[1], want_s[1] = codes[0], 0.5
+    want_c[2], want_s[2] = codes[2], 2.0
+    assert np.array_equal(flat_c, want_c) and np.array_equal(flat_s, want_s)
+    assert out.k_cache.shape == kc0.shape and out.k_scale.shape == ks0.shape
+    # the input problem is unchanged
+    assert np.array_equal(prob.k_cache, kc0) and np.array_equal(prob.k_scale, ks0)
+    assert np.array_equal(prob.page_table, pt0)
+    # a slot written from row 0's page-table row for row 2 (slot 4) or from the
+    # logical position taken as a flat slot (slot 3 for row 0) stays untouched
+    assert np.array_equal(flat_c[3], kc0.reshape(-1, 3)[3]) and np.array_equal(flat_c[4], kc0.reshape(-1, 3)[4])
+
+
+def test_with_new_keys_scores_the_written_key():
+    """Invariant: after the write, the score a row gives its written position equals
+    (to f64 rounding) the score of a one-key cache holding just that key (codes,
+    scale), and every other position of every row keeps its score bit for bit."""
+    from workloads import make_problem
+    from workloads.synth import quantize_keys
+    prob = make_problem([300, 150], [3, 2], seed=23, k=8, name="nk")
+    rng = np.random.default_rng(4)
+    codes, scales = quantize_keys(rng.standard_normal((prob.rows, prob.dim), dtype=np.float32))
+    pos = np.array([10, -1, 297, 0, 148], dtype=np.int32)
+    before = O.scores(prob)
+    after = O.scores(O.with_new_keys(prob, codes, scales, pos))
+    for r in range(prob.rows):
+        n = int(prob.n_keys[r])
+        # positions a row's request writes (this row's and its request mates')
+        a, b = [(s, e) for s, e in zip(prob.req_indptr[:-1], prob.req_indptr[1:]) if s <= r < e][0]
+        written = {int(pos[j]) for j in range(a, b) if pos[j] >= 0}
+        for p in range(n):
+            if p not in written:
+                assert after[r][p] == before[r][p], (r, p)
+        for j in range(a, b):
+            p = int(pos[j])
+            if 0 <= p < n:
+                one = O.row_scores(prob.q[r], prob.w[r], codes[j].reshape(1, 1, -1),
+                                   np.array([[scales[j]]], dtype=np.float32), np.array([0], dtype=np.int32), 1)
+                # equal up to f64 summation order (a misplaced key differs at O(1))
+                assert abs(after[r][p] - one[0]) <= 1e-12 * max(1.0, abs(one[0])), (r, j, p)
