@@ -53,12 +53,14 @@ extern "C" {
 #define IDX_KMAX 2048
 #define IDX_GROUP_ROWS 4
 #define IDX_MAX_REQ 256
-#define IDX_ABI_VERSION 2
+#define IDX_MAX_KEYS (1 << 28)               /* keys a row at most (selection offsets stay 32-bit) */
+#define IDX_ABI_VERSION 3
 
 /* Return codes. */
 #define IDX_OK 0
 #define IDX_EINVAL 1       /* null pointer, bad size/stride/alignment, k out of [1, IDX_KMAX], bad req_indptr */
-#define IDX_EUNSUPPORTED 2 /* heads/dim/page size not the compiled ones, > IDX_MAX_REQ row groups */
+#define IDX_EUNSUPPORTED 2 /* heads/dim/page size not the compiled ones, > IDX_MAX_REQ row groups,
+                              max_keys > IDX_MAX_KEYS */
 #define IDX_EWORKSPACE 3   /* workspace null or smaller than idx_workspace_bytes() */
 #define IDX_EHIP 4         /* a HIP runtime call or launch failed; see idx_last_hip_error() */
 #define IDX_EDEVICE 5      /* a sticky device-side error was found by idx_device_status() */
@@ -82,7 +84,8 @@ typedef struct idx_problem {
   int32_t page_size;         /* must be IDX_PAGE_SIZE */
   int32_t num_pages;         /* pages in the cache pool, >= 1 */
   int32_t max_pages;         /* columns of page_table, >= 1 */
-  int32_t max_keys;          /* host bound on every n_keys[r]; 0 <= max_keys <= max_pages * page_size */
+  int32_t max_keys;          /* host bound on every n_keys[r]; 0 <= max_keys <= max_pages * page_size,
+                                and max_keys <= IDX_MAX_KEYS (else IDX_EUNSUPPORTED) */
   const void* q;             /* bf16 [rows][heads][dim], contiguous, 16-byte aligned */
   const void* w;             /* bf16 [rows][heads], contiguous, 4-byte aligned */
   const uint8_t* k_cache;    /* E4M3FN codes [num_pages][page_size][dim], 16-byte aligned */
@@ -100,33 +103,54 @@ typedef struct idx_problem {
 /* ABI version (IDX_ABI_VERSION). */
 int idx_abi_version(void);
 
-/* Bytes of workspace any entry point needs for up to `rows` rows of up to
- * `max_keys` keys and top-k size k.  Returns IDX_OK and sets *bytes, or
- * IDX_EINVAL. */
+/* Workspace size.  The selection's scratch is owned by the caller and allocated once,
+ * outside the call path, as the indexer page sizes its select buffers once per runtime
+ * (GLM-5.3 indexer page, Modifications item 3, "Scratch").  Sets *bytes to what every
+ * entry point below needs for up to `rows` rows of up to `max_keys` keys and top-k size
+ * k (one candidate block per row and chunk, plus a 256-byte header); the size grows
+ * with rows and with max_keys, so one workspace serves every smaller call.
+ * Returns IDX_OK; IDX_EINVAL (null bytes, rows outside [1, 2^24), max_keys < 0, k
+ * outside [1, IDX_KMAX]); IDX_EUNSUPPORTED (max_keys > IDX_MAX_KEYS). */
 int idx_workspace_bytes(int32_t rows, int32_t max_keys, int32_t k, size_t* bytes);
 
-/* Zero the workspace and stamp it initialised (a device fill kernel on
- * `stream`; no host synchronisation).  ws must be 256-byte aligned and
- * ws_bytes a multiple of 256 and >= 256. */
+/* Zero the workspace and stamp it initialised (one device fill kernel on `stream`; no
+ * host synchronisation).  Needed once per workspace: calls never leave state a later
+ * call depends on, so it is not repeated between calls.  ws: device pointer, 256-byte
+ * aligned; ws_bytes a multiple of 256 and >= 256.  Returns IDX_OK, IDX_EINVAL or
+ * IDX_EHIP. */
 int idx_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
-/* Scores only: scores[r * ld_scores + p] for p < n_keys[r] (entries past
- * n_keys[r] are not written).  ld_scores >= max(1, max_keys). */
+/* Scores only (steps S1-S4 of the path): the GLM-5.3 indexer page, Modifications item
+ * 2 ("Scores": the bf16 query against every key of the request, scaled, ReLU'd and
+ * head-summed in f32, each key read once for the up to 4 rows of a group; "Runs of
+ * pages": the request's pages are streamed through LDS).  Writes scores[r * ld_scores + p]
+ * (f32) for p < n_keys[r]; entries past n_keys[r] are left untouched.
+ * ld_scores >= max(1, max_keys); scores 4-byte aligned, rows * ld_scores floats.
+ * One launch on `stream`.  Returns IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED,
+ * IDX_EWORKSPACE or IDX_EHIP; device-side errors are read with idx_device_status(). */
 int idx_score(const idx_problem* p, float* scores, int64_t ld_scores,
               void* ws, size_t ws_bytes, void* stream);
 
-/* Exact top-k over given scores: for each row r, topk[r * k + i] (i < k) is
- * the ascending list of the first k positions p < n_keys[r] by (score desc,
- * position asc), padded with -1; scores compare as real numbers (-0 == +0).
- * scores must be finite.  n_keys is a device array of `rows` entries. */
+/* Exact top-k over given scores (steps S5-S7): the GLM-5.3 indexer page, Modifications
+ * item 3 (every row's exact top-2048) with item 0's definition of exactness (score
+ * descending, then position).  For each row r, topk[r * k + i] (i < k) is the
+ * ascending list of the first k positions p < n_keys[r] in that order, padded with -1
+ * when n_keys[r] < k; scores compare as real numbers (-0 == +0) and must be finite.
+ * scores: device f32 [rows][ld_scores]; n_keys: device int32 [rows] (values outside
+ * [0, max_keys] are clamped and raise IDX_DERR_NKEYS); topk: device int32 [rows][k].
+ * Any number of rows: launches of up to 1,024 rows each, in order on `stream`.
+ * Returns IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED (max_keys > IDX_MAX_KEYS),
+ * IDX_EWORKSPACE or IDX_EHIP. */
 int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys,
              int32_t rows, int32_t max_keys, int32_t k, int32_t* topk,
              void* ws, size_t ws_bytes, void* stream);
 
-/* Scoring and exact top-k in one call (two launches on `stream`: scoring with
- * candidate publication, then one selection workgroup per row): writes the
- * scores exactly as idx_score() does and the lists exactly as idx_topk() over
- * those scores. */
+/* The whole path (S1-S7): the GLM-5.3 indexer page, Modifications items 2 and 3 (a
+ * request's rows scored together, then every row's exact top-k), exact in the sense
+ * of item 0.  Two launches on `stream`: scoring, which also publishes each chunk's
+ * candidates into the workspace, then one selection workgroup per row.  Writes the
+ * scores exactly as idx_score() does and the lists exactly as idx_topk() over those
+ * scores; 1 <= k <= IDX_KMAX; topk: device int32 [rows][k].  Returns as idx_score(). */
 int idx_score_topk(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores,
                    int32_t* topk, void* ws, size_t ws_bytes, void* stream);
 
@@ -149,24 +173,41 @@ typedef struct idx_new_keys {
 /* As idx_score_topk(), with every row's new key (idx_new_keys) in place: the scores are
  * those of the cache after the keys are written, and the launch also writes them into
  * p->k_cache and p->k_scale (which this call therefore modifies).  At most 16 rows a
- * request (else IDX_EUNSUPPORTED). */
+ * request (else IDX_EUNSUPPORTED); nk null or misaligned: IDX_EINVAL. */
 int idx_score_topk_append(const idx_problem* p, const idx_new_keys* nk, int32_t k, float* scores,
                           int64_t ld_scores, int32_t* topk, void* ws, size_t ws_bytes, void* stream);
 
 /* As idx_score_topk(), and also each list as physical cache slots, the form the sparse
- * attention reads (the indexer page's selection stages cache slots, Modifications
- * item 3): slots[r * k + i] = page_table[r][p / 64] * 64 + p % 64 for
- * the list entry p = topk[r * k + i] >= 0, and -1 where the list holds -1 (or where the
- * page id lies outside the pool, which also raises IDX_DERR_PAGE).  slots: device
- * int32 [rows][k], distinct from topk.  Same launches; the selection launch maps the
- * list after writing it. */
+ * attention reads (the indexer page's selection stages its keys with their cache slots,
+ * Modifications item 3, "Placing and resolving"): slots[r * k + i] =
+ * page_table[r][p / 64] * 64 + p % 64 for the list entry p = topk[r * k + i] >= 0, and -1
+ * where the list holds -1 (or where the page id lies outside the pool, which also raises
+ * IDX_DERR_PAGE).  slots: device int32 [rows][k], distinct from topk.  Same launches;
+ * the selection launch maps the list after writing it.  slots null or equal to topk:
+ * IDX_EINVAL. */
 int idx_score_topk_slots(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores,
                          int32_t* topk, int32_t* slots, void* ws, size_t ws_bytes, void* stream);
 
-/* Index-query preparation (the GLM-5.3 indexer page, Modifications item 2, "the query
- * once a row": each row's index query is roped and Hadamard-transformed once and
- * published in bf16; Modifications item 0: that transform runs in f32, then rounds to
- * bf16).  For every row r and head h, with x = q_pre[r][h][:] (bf16 [rows][64][128]):
+/* As idx_score_topk_slots(), with the slots handed over as tagged words (the
+ * GLM-5.3-Flash hand-offs page, Modifications item 3: the selection writes every
+ * selected token together with the launch's tag, so a consumer polls the tokens
+ * themselves, with no drain and no ready flag).  tagged[r * k + i] =
+ * ((uint64_t)tag << 32) | (uint32_t)slot, slot as in idx_score_topk_slots() (-1 stored as
+ * 0xFFFFFFFF), each word written by one 8-byte device-scope store after the row's list
+ * is final.  A consumer on the same device that polls a word with device-scope loads
+ * sees either an older word or the whole new one: a word is ready once its high half
+ * equals `tag`.  The caller picks a tag no word holds yet (for example a launch
+ * counter).  tagged: device uint64 [rows][k], 8-byte aligned.  topk is written as by
+ * idx_score_topk().  Returns as idx_score_topk(). */
+int idx_score_topk_tagged(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores,
+                          int32_t* topk, uint64_t* tagged, uint32_t tag, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Index-query preparation (the GLM-5.3 indexer page, Modifications item 2, on preparing
+ * the query once a row: each row's index query gets its rotary embedding and the
+ * Hadamard transform once and is stored in bf16; item 0's reference takes that query
+ * computed in f32 with one rounding to bf16).  For every row r and head h, with
+ * x = q_pre[r][h][:] (bf16 [rows][64][128]):
  *   1. RoPE on dimensions [0, rope_dim): pair i < rope_dim / 2 is (i, i + rope_dim / 2)
  *      (interleaved = 0) or (2 i, 2 i + 1) (interleaved = 1); its values (a, b) become
  *      (a c - b s, a s + b c) with c = cos_tab[r][i], s = sin_tab[r][i] (f32
@@ -181,9 +222,10 @@ int idx_score_topk_slots(const idx_problem* p, int32_t k, float* scores, int64_t
 int idx_prep_query(const void* q_pre, const float* cos_tab, const float* sin_tab, int32_t rows,
                    int32_t rope_dim, int32_t interleaved, void* q_out, void* stream);
 
-/* Synchronise `stream`, read and clear the workspace's sticky device error.
- * Returns IDX_OK, IDX_EDEVICE (with *detail = IDX_DERR_* bits when detail is
- * not NULL), or IDX_EHIP. */
+/* This library's device-side error channel (no page defines one): out-of-range n_keys
+ * or page ids, an uninitialised workspace, a failed selection invariant.  Synchronises `stream`, reads and clears the workspace's sticky
+ * error word.  Returns IDX_OK, IDX_EDEVICE (with *detail = IDX_DERR_* bits when detail
+ * is not NULL), IDX_EINVAL (ws null or ws_bytes < 256) or IDX_EHIP. */
 int idx_device_status(void* ws, size_t ws_bytes, void* stream, uint32_t* detail);
 
 /* Static description of a return code. */
@@ -191,6 +233,10 @@ const char* idx_strerror(int code);
 
 /* The last HIP error string seen by this thread (empty if none). */
 const char* idx_last_hip_error(void);
+
+/* SHA-256 (64 hex digits) of the sources and flags this library was built from, or
+ * "unknown" for a build made without it. */
+const char* idx_build_hash(void);
 
 #ifdef __cplusplus
 }

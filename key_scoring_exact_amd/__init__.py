@@ -19,8 +19,9 @@ from . import _lib
 from ._lib import (IDX_DIM, IDX_GROUP_ROWS, IDX_HEADS, IDX_KMAX, IDX_MAX_REQ,  # noqa: F401
                    IDX_PAGE_SIZE, IdxProblem)
 
-__all__ = ["IdxError", "DeviceProblem", "Workspace", "score", "topk", "score_topk",
-           "device_status", "workspace_bytes", "lib"]
+__all__ = ["IdxError", "DeviceProblem", "Workspace", "score", "topk", "score_topk", "score_topk_append",
+           "score_topk_slots", "score_topk_tagged", "prep_query", "device_status",
+           "workspace_bytes", "lib"]
 
 
 class IdxError(RuntimeError):
@@ -48,6 +49,18 @@ def _stream(stream) -> int:
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
+
+
+def _shape(t: torch.Tensor, want, name: str):
+    """Raise ValueError unless t has the given shape (None entries match any size)."""
+    got = tuple(t.shape)
+    if len(got) != len(want) or any(w is not None and g != w for g, w in zip(got, want)):
+        raise ValueError(f"{name}: expected shape {tuple('*' if w is None else w for w in want)}, got {got}")
+
+
+def _rows_at_least(t: torch.Tensor, rows: int, name: str):
+    if t.dim() != 2 or t.shape[0] < rows:
+        raise ValueError(f"{name}: expected a 2-D tensor of at least {rows} rows, got shape {tuple(t.shape)}")
 
 
 def _ptr(t: torch.Tensor, dtype=None) -> int:
@@ -119,8 +132,30 @@ class DeviceProblem:
                    max_keys=int(max_keys),
                    req_max_keys=None if req_max_keys is None else [int(x) for x in req_max_keys])
 
+    def check_shapes(self):
+        """Raise ValueError when the tensors' shapes disagree with each other: every
+        kernel indexes them by rows, heads, dim and page size, so a short tensor would
+        be read past its end."""
+        if self.q.dim() != 3:
+            raise ValueError(f"q: expected [rows, heads, dim], got shape {tuple(self.q.shape)}")
+        rows, heads, dim = (int(x) for x in self.q.shape)
+        _shape(self.w, (rows, heads), "w")
+        if self.k_cache.dim() != 3 or int(self.k_cache.shape[2]) != dim:
+            raise ValueError(f"k_cache: expected [num_pages, page_size, {dim}], got {tuple(self.k_cache.shape)}")
+        _shape(self.k_scale, tuple(int(x) for x in self.k_cache.shape[:2]), "k_scale")
+        _shape(self.page_table, (rows, None), "page_table")
+        _shape(self.n_keys, (rows,), "n_keys")
+        ip = list(self.req_indptr)
+        if len(ip) < 2 or ip[0] != 0 or ip[-1] != rows or any(b <= a for a, b in zip(ip[:-1], ip[1:])):
+            raise ValueError(f"req_indptr must rise strictly from 0 to rows={rows}, got {ip}")
+        if self.req_max_keys is not None and len(self.req_max_keys) != len(ip) - 1:
+            raise ValueError("req_max_keys: one bound a request expected")
+        if self.max_keys > int(self.page_table.shape[1]) * int(self.k_cache.shape[1]):
+            raise ValueError("max_keys exceeds the page table's capacity (max_pages * page_size)")
+
     def struct(self):
         """The idx_problem struct and the host arrays it points to (keep both alive)."""
+        self.check_shapes()
         ip = (ctypes.c_int32 * len(self.req_indptr))(*self.req_indptr)
         rm = None
         if self.req_max_keys is not None:
@@ -143,6 +178,7 @@ def score(p: DeviceProblem, ws: Workspace, scores: Optional[torch.Tensor] = None
     """f32 scores [rows, ld]; entries at positions >= n_keys[r] are left untouched."""
     if scores is None:
         scores = torch.empty((p.rows, max(1, p.max_keys)), dtype=torch.float32, device=p.q.device)
+    _rows_at_least(scores, p.rows, "scores")
     s, keep = p.struct()
     _check(lib().idx_score(ctypes.byref(s), ctypes.c_void_p(_ptr(scores, torch.float32)), scores.shape[1],
                            ctypes.c_void_p(ws.ptr), ws.nbytes, ctypes.c_void_p(_stream(stream))), "idx_score")
@@ -156,6 +192,8 @@ def score_topk(p: DeviceProblem, k: int, ws: Workspace, scores: Optional[torch.T
         scores = torch.empty((p.rows, max(1, p.max_keys)), dtype=torch.float32, device=p.q.device)
     if out is None:
         out = torch.empty((p.rows, k), dtype=torch.int32, device=p.q.device)
+    _rows_at_least(scores, p.rows, "scores")
+    _shape(out, (p.rows, k), "out")
     s, keep = p.struct()
     _check(lib().idx_score_topk(ctypes.byref(s), int(k), ctypes.c_void_p(_ptr(scores, torch.float32)),
                                 scores.shape[1], ctypes.c_void_p(_ptr(out, torch.int32)),
@@ -174,6 +212,11 @@ def score_topk_append(p: DeviceProblem, k: int, ws: Workspace, new_codes: torch.
         scores = torch.empty((p.rows, max(1, p.max_keys)), dtype=torch.float32, device=p.q.device)
     if out is None:
         out = torch.empty((p.rows, k), dtype=torch.int32, device=p.q.device)
+    _rows_at_least(scores, p.rows, "scores")
+    _shape(out, (p.rows, k), "out")
+    _shape(new_codes, (p.rows, int(p.q.shape[2])), "new_codes")
+    _shape(new_scales, (p.rows,), "new_scales")
+    _shape(new_pos, (p.rows,), "new_pos")
     s, keep = p.struct()
     nk = _lib.IdxNewKeys(_ptr(new_codes, torch.uint8), _ptr(new_scales, torch.float32), _ptr(new_pos, torch.int32))
     _check(lib().idx_score_topk_append(ctypes.byref(s), ctypes.byref(nk), int(k),
@@ -192,6 +235,9 @@ def score_topk_slots(p: DeviceProblem, k: int, ws: Workspace, scores: Optional[t
         out = torch.empty((p.rows, k), dtype=torch.int32, device=p.q.device)
     if slots is None:
         slots = torch.empty((p.rows, k), dtype=torch.int32, device=p.q.device)
+    _rows_at_least(scores, p.rows, "scores")
+    _shape(out, (p.rows, k), "out")
+    _shape(slots, (p.rows, k), "slots")
     s, keep = p.struct()
     _check(lib().idx_score_topk_slots(ctypes.byref(s), int(k), ctypes.c_void_p(_ptr(scores, torch.float32)),
                                       scores.shape[1], ctypes.c_void_p(_ptr(out, torch.int32)),
@@ -200,12 +246,39 @@ def score_topk_slots(p: DeviceProblem, k: int, ws: Workspace, scores: Optional[t
     return scores, out, slots
 
 
+def score_topk_tagged(p: DeviceProblem, k: int, ws: Workspace, tag: int, scores: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, tagged: Optional[torch.Tensor] = None, stream=None):
+    """(scores, lists, tagged): as score_topk, plus each list's cache slots as 64-bit words
+    tag << 32 | slot (int64 [rows, k]; slot -1 is stored as 0xFFFFFFFF)."""
+    if scores is None:
+        scores = torch.empty((p.rows, max(1, p.max_keys)), dtype=torch.float32, device=p.q.device)
+    if out is None:
+        out = torch.empty((p.rows, k), dtype=torch.int32, device=p.q.device)
+    if tagged is None:
+        tagged = torch.empty((p.rows, k), dtype=torch.int64, device=p.q.device)
+    _rows_at_least(scores, p.rows, "scores")
+    _shape(out, (p.rows, k), "out")
+    _shape(tagged, (p.rows, k), "tagged")
+    if not 0 <= int(tag) < (1 << 32):
+        raise ValueError("tag must fit 32 bits")
+    s, keep = p.struct()
+    _check(lib().idx_score_topk_tagged(ctypes.byref(s), int(k), ctypes.c_void_p(_ptr(scores, torch.float32)),
+                                       scores.shape[1], ctypes.c_void_p(_ptr(out, torch.int32)),
+                                       ctypes.c_void_p(_ptr(tagged, torch.int64)), int(tag), ctypes.c_void_p(ws.ptr),
+                                       ws.nbytes, ctypes.c_void_p(_stream(stream))), "idx_score_topk_tagged")
+    return scores, out, tagged
+
+
 def topk(scores: torch.Tensor, n_keys: torch.Tensor, k: int, max_keys: int, ws: Workspace,
          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Exact top-k lists [rows, k] int32 of given f32 scores [rows, ld]."""
+    if scores.dim() != 2:
+        raise ValueError(f"scores: expected [rows, ld], got shape {tuple(scores.shape)}")
     rows = int(scores.shape[0])
+    _shape(n_keys, (rows,), "n_keys")
     if out is None:
         out = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    _shape(out, (rows, k), "out")
     _check(lib().idx_topk(ctypes.c_void_p(_ptr(scores, torch.float32)), scores.shape[1],
                           ctypes.c_void_p(_ptr(n_keys, torch.int32)), rows, int(max_keys), int(k),
                           ctypes.c_void_p(_ptr(out, torch.int32)), ctypes.c_void_p(ws.ptr), ws.nbytes,
@@ -221,10 +294,13 @@ def prep_query(q_pre: torch.Tensor, cos: Optional[torch.Tensor], sin: Optional[t
     rows = int(q_pre.shape[0])
     if out is None:
         out = torch.empty_like(q_pre)
+    if q_pre.dim() != 3 or tuple(q_pre.shape[1:]) != (IDX_HEADS, IDX_DIM) or out.shape != q_pre.shape:
+        raise ValueError("expected q_pre and out of shape [rows, 64, 128]")
+    if rope_dim > 0:
+        _shape(cos, (rows, int(rope_dim) // 2), "cos")
+        _shape(sin, (rows, int(rope_dim) // 2), "sin")
     cp = ctypes.c_void_p(_ptr(cos, torch.float32)) if rope_dim > 0 else None
     sp = ctypes.c_void_p(_ptr(sin, torch.float32)) if rope_dim > 0 else None
-    if tuple(q_pre.shape[1:]) != (IDX_HEADS, IDX_DIM) or out.shape != q_pre.shape:
-        raise ValueError("expected q_pre and out of shape [rows, 64, 128]")
     bf = (torch.bfloat16, torch.int16)
     _check(lib().idx_prep_query(ctypes.c_void_p(_ptr(q_pre, bf)), cp, sp, rows, int(rope_dim),
                                 1 if interleaved else 0, ctypes.c_void_p(_ptr(out, bf)),

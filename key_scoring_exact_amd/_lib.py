@@ -13,6 +13,8 @@ IDX_PAGE_SIZE = 64
 IDX_KMAX = 2048
 IDX_GROUP_ROWS = 4
 IDX_MAX_REQ = 256
+IDX_MAX_KEYS = 1 << 28
+IDX_ABI_VERSION = 3
 
 IDX_OK = 0
 IDX_EINVAL = 1
@@ -65,10 +67,13 @@ SIGNATURES = {
     "idx_score_topk_append": (ctypes.c_int, [ctypes.POINTER(IdxProblem), ctypes.POINTER(IdxNewKeys), _i32, _vp, _i64,
                                              _vp, _vp, _sz, _vp]),
     "idx_score_topk_slots": (ctypes.c_int, [ctypes.POINTER(IdxProblem), _i32, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "idx_score_topk_tagged": (ctypes.c_int, [ctypes.POINTER(IdxProblem), _i32, _vp, _i64, _vp, _vp, ctypes.c_uint32,
+                                             _vp, _sz, _vp]),
     "idx_prep_query": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "idx_device_status": (ctypes.c_int, [_vp, _sz, _vp, ctypes.POINTER(ctypes.c_uint32)]),
     "idx_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "idx_last_hip_error": (ctypes.c_char_p, []),
+    "idx_build_hash": (ctypes.c_char_p, []),
 }
 
 _lib = None

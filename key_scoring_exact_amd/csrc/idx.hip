@@ -121,6 +121,8 @@ struct KArgs {
   const int32_t* nw_pos;    // int32 [rows]
   uint8_t* kc_w;            // the cache, written
   float* ks_w;
+  uint64_t* tagged;         // [rows][k] or null: the slots as tagged words, tag << 32 | slot
+  uint32_t tag;
 };
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -1605,11 +1607,12 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
       if (b < rqn) dma16(a.nw_codes + (int64_t)(rq0 + b) * D + (lane & 7) * 16, lds0 + L_PATCH + i2 * 1024);
     }
   }
-  int ld_np = -1;
+  int ld_np = -1, ld_rn = 0;
   float ld_ns = 0.f;
   if (do_score && lane < rqn) {
     ld_np = a.nw_pos[rq0 + lane];
     ld_ns = a.nw_scales[rq0 + lane];
+    ld_rn = a.nk[rq0 + lane];                     // every request row's key count, for the position check
   }
   // n_keys of the group's rows, the chunk's page ids of every row and the workspace's
   // magic word, in one load (lanes [0, R): n_keys; lanes [8, 8 + R*P):
@@ -1675,15 +1678,16 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
     }
     if (perr && tid == 0) raise_error(ws, perr);
     // the request's new keys in this chunk; a position outside [-1, the row's key
-    // count) is reported and ignored (each row's key is within what the row sees)
+    // count) is reported and ignored (each row's key is within what the row sees).
+    // Every row group of the request takes the same decision: it checks each request
+    // row's position against that row's own key count, clamped to the request's bound
+    // as the row's own group clamps it.
     Patches pt = {0ull, 0ull, ld_np, ld_ns};
     if (PATCH && rqn > 0) {
       const int own = lane - (row0 - rq0);           // this lane's row within the group
-      int nown = 0;
-#pragma unroll
-      for (int i2 = 0; i2 < GR; i2++) nown = (own == i2) ? n[i2] : nown;
+      const int nrow = ld_rn < 0 ? 0 : (ld_rn > gbound ? gbound : ld_rn);
       const bool inr = lane < rqn;
-      const bool bad = inr && (ld_np < -1 || (own >= 0 && own < R && ld_np >= nown));
+      const bool bad = inr && (ld_np < -1 || ld_np >= nrow);
       if (__ballot(bad) != 0ull && tid == 0) raise_error(ws, IDX_DERR_NKEYS);
       pt.hit = __ballot(inr && !bad && ld_np >= chunk_base && ld_np < chunk_base + C && ld_np < nmax);
       pt.mine = __ballot(inr && own >= 0 && own < R);
@@ -1995,19 +1999,21 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
   return true;
 }
 
-// Launch 2.  With a slot array, each written list is then mapped to physical cache
-// slots through the row's own page-table row: slot = page_table[row][p / 64] * 64 +
-// p % 64, and -1 for -1 padding (or for a page id outside the pool, which the scoring
-// launch has already reported).
-template <bool SLOTS>
+// Launch 2.  OUT_SLOTS: each written list is then mapped to physical cache slots
+// through the row's own page-table row: slot = page_table[row][p / 64] * 64 + p % 64,
+// and -1 for -1 padding (or for a page id outside the pool, which the scoring launch has
+// already reported).  OUT_TAGGED: the same slots, each stored as one 8-byte word
+// tag << 32 | slot with a device-scope store, so that a consumer polling the word sees
+// the old word or the whole new one.
+constexpr int OUT_LIST = 0, OUT_SLOTS = 1, OUT_TAGGED = 2;
+template <int OUT>
 __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  if (!select_row(a, smem) || !SLOTS) return;
+  if (!select_row(a, smem) || OUT == OUT_LIST) return;
   __syncthreads();                                   // the list's stores, visible to the workgroup
   const uint32_t ge = a.grp[blockIdx.y];
   const int grow = (int)(ge & 0xFFFFFFu) + (int)blockIdx.x;
   const int32_t* lst = a.topk + (int64_t)grow * a.k;
-  int32_t* sl = a.slots + (int64_t)grow * a.k;
   const int32_t* ptr = a.pt + (int64_t)grow * a.max_pages;
   for (int i = threadIdx.x; i < a.k; i += NT) {
     const int p = lst[i];
@@ -2016,7 +2022,12 @@ __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
       const int ph = ptr[p / PS];
       v = (ph >= 0 && ph < a.num_pages) ? ph * PS + (p % PS) : -1;
     }
-    sl[i] = v;
+    if constexpr (OUT == OUT_SLOTS) {
+      a.slots[(int64_t)grow * a.k + i] = v;
+    } else {
+      const uint64_t word = ((uint64_t)a.tag << 32) | (uint32_t)v;
+      __hip_atomic_store(a.tagged + (int64_t)grow * a.k + i, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -2174,7 +2185,7 @@ int validate_problem(const idx_problem* p) {
     for (int j = 0; j < p->num_req; j++)
       if (p->req_max_keys[j] < 0 || p->req_max_keys[j] > p->max_keys) return IDX_EINVAL;
   if ((int64_t)p->max_keys > (int64_t)p->max_pages * IDX_PAGE_SIZE) return IDX_EINVAL;
-  if (p->max_keys > (1 << 30)) return IDX_EUNSUPPORTED;
+  if (p->max_keys > IDX_MAX_KEYS) return IDX_EUNSUPPORTED;
   if (check_ptr(p->q, 16) || check_ptr(p->w, 4) || check_ptr(p->k_cache, 16) || check_ptr(p->k_scale, 16) ||
       check_ptr(p->page_table, 4) || check_ptr(p->n_keys, 4))
     return IDX_EINVAL;
@@ -2186,12 +2197,13 @@ constexpr int SELECT_LDS = L_FIN_END;
 
 int set_attrs() {
   if (g_attr_done) return IDX_OK;
-  const void* fs[10] = {(const void*)score_kernel<1, false>, (const void*)score_kernel<2, false>,
-                        (const void*)score_kernel<4, false>, (const void*)score_kernel<8, false>,
-                        (const void*)score_kernel<1, true>,  (const void*)score_kernel<2, true>,
-                        (const void*)score_kernel<4, true>,  (const void*)score_kernel<8, true>,
-                        (const void*)select_kernel<false>,   (const void*)select_kernel<true>};
-  for (int i = 0; i < 10; i++) {
+  const void* fs[11] = {(const void*)score_kernel<1, false>,      (const void*)score_kernel<2, false>,
+                        (const void*)score_kernel<4, false>,      (const void*)score_kernel<8, false>,
+                        (const void*)score_kernel<1, true>,       (const void*)score_kernel<2, true>,
+                        (const void*)score_kernel<4, true>,       (const void*)score_kernel<8, true>,
+                        (const void*)select_kernel<OUT_LIST>,     (const void*)select_kernel<OUT_SLOTS>,
+                        (const void*)select_kernel<OUT_TAGGED>};
+  for (int i = 0; i < 11; i++) {
     const hipError_t e =
         hipFuncSetAttribute(fs[i], hipFuncAttributeMaxDynamicSharedMemorySize, i < 8 ? SCORE_LDS : SELECT_LDS);
     if (e != hipSuccess) return hip_fail(e);
@@ -2221,10 +2233,13 @@ int launch(const KArgs& args, int P, dim3 grid, bool score_launch, bool select_l
     if (e != hipSuccess) return hip_fail(e);
   }
   if (select_launch) {
-    if (args.slots)
-      hipLaunchKernelGGL(select_kernel<true>, dim3(IDX_GROUP_ROWS, grid.y), dim3(NT), SELECT_LDS, st, args);
+    const dim3 sg(IDX_GROUP_ROWS, grid.y);
+    if (args.tagged)
+      hipLaunchKernelGGL(select_kernel<OUT_TAGGED>, sg, dim3(NT), SELECT_LDS, st, args);
+    else if (args.slots)
+      hipLaunchKernelGGL(select_kernel<OUT_SLOTS>, sg, dim3(NT), SELECT_LDS, st, args);
     else
-      hipLaunchKernelGGL(select_kernel<false>, dim3(IDX_GROUP_ROWS, grid.y), dim3(NT), SELECT_LDS, st, args);
+      hipLaunchKernelGGL(select_kernel<OUT_LIST>, sg, dim3(NT), SELECT_LDS, st, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -2238,7 +2253,8 @@ void fill_common(KArgs& args, const WsLayout& L, void* ws) {
 }
 
 int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int32_t* topk, int32_t* slots,
-                void* ws, size_t ws_bytes, void* stream, bool select, const idx_new_keys* nk = nullptr) {
+                void* ws, size_t ws_bytes, void* stream, bool select, const idx_new_keys* nk = nullptr,
+                uint64_t* tagged = nullptr, uint32_t tag = 0) {
   int rc = validate_problem(p);
   if (rc) return rc;
   if (!scores || ld < 1 || ld < (int64_t)p->max_keys) return IDX_EINVAL;
@@ -2263,6 +2279,8 @@ int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int3
   args.scores = scores;
   args.topk = topk;
   args.slots = slots;
+  args.tagged = tagged;
+  args.tag = tag;
   args.ld = ld;
   args.rows = p->rows;
   args.max_pages = p->max_pages;
@@ -2304,8 +2322,8 @@ extern "C" {
 int idx_abi_version(void) { return IDX_ABI_VERSION; }
 
 int idx_workspace_bytes(int32_t rows, int32_t max_keys, int32_t k, size_t* bytes) {
-  if (!bytes || rows < 1 || rows > (1 << 24) - 1 || max_keys < 0 || max_keys > (1 << 30) || k < 1 || k > IDX_KMAX)
-    return IDX_EINVAL;
+  if (!bytes || rows < 1 || rows > (1 << 24) - 1 || max_keys < 0 || k < 1 || k > IDX_KMAX) return IDX_EINVAL;
+  if (max_keys > IDX_MAX_KEYS) return IDX_EUNSUPPORTED;
   *bytes = (size_t)layout_for(rows, max_keys).total;
   return IDX_OK;
 }
@@ -2348,10 +2366,16 @@ int idx_score_topk_slots(const idx_problem* p, int32_t k, float* scores, int64_t
   return run_problem(p, k, scores, ld_scores, topk, slots, ws, ws_bytes, stream, true);
 }
 
+int idx_score_topk_tagged(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores, int32_t* topk,
+                          uint64_t* tagged, uint32_t tag, void* ws, size_t ws_bytes, void* stream) {
+  if (!tagged || (reinterpret_cast<uintptr_t>(tagged) & 7)) return IDX_EINVAL;
+  return run_problem(p, k, scores, ld_scores, topk, nullptr, ws, ws_bytes, stream, true, nullptr, tagged, tag);
+}
+
 int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys, int32_t rows, int32_t max_keys,
              int32_t k, int32_t* topk, void* ws, size_t ws_bytes, void* stream) {
-  if (!scores || !n_keys || !topk || rows < 1 || rows > (1 << 24) - 1 || max_keys < 0 || max_keys > (1 << 30))
-    return IDX_EINVAL;
+  if (!scores || !n_keys || !topk || rows < 1 || rows > (1 << 24) - 1 || max_keys < 0) return IDX_EINVAL;
+  if (max_keys > IDX_MAX_KEYS) return IDX_EUNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(scores) & 3) || (reinterpret_cast<uintptr_t>(n_keys) & 3)) return IDX_EINVAL;
   if (ld_scores < 1 || ld_scores < (int64_t)max_keys || (int64_t)rows > INT64_MAX / ld_scores) return IDX_EINVAL;
   if (k < 1 || k > IDX_KMAX) return IDX_EINVAL;
@@ -2440,5 +2464,13 @@ const char* idx_strerror(int code) {
 }
 
 const char* idx_last_hip_error(void) { return g_hip_err; }
+
+#ifndef IDX_SOURCE_HASH
+#define IDX_SOURCE_HASH "unknown"
+#endif
+// the marker string lets a build script read the hash from the file without loading it
+static const char g_build_marker[] = "idx-source-sha256:" IDX_SOURCE_HASH;
+
+const char* idx_build_hash(void) { return g_build_marker + 18; }
 
 }  // extern "C"

@@ -41,9 +41,15 @@ def test_exports_every_declared_function(L):
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ["IDX_HEADS", "IDX_DIM", "IDX_PAGE_SIZE", "IDX_KMAX", "IDX_GROUP_ROWS", "IDX_MAX_REQ",
-                 "IDX_OK", "IDX_EINVAL", "IDX_EUNSUPPORTED", "IDX_EWORKSPACE", "IDX_EHIP", "IDX_EDEVICE"]:
+                 "IDX_OK", "IDX_EINVAL", "IDX_EUNSUPPORTED", "IDX_EWORKSPACE", "IDX_EHIP", "IDX_EDEVICE",
+                 "IDX_ABI_VERSION"]:
         m = re.search(r"#define " + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == getattr(_lib, name), name
+    for name, expr in [("IDX_MAX_KEYS", r"\(1 << (\d+)\)")]:
+        m = re.search(r"#define " + name + r"\s+" + expr, text)
+        assert m, name
+        v = (1 << int(m.group(1))) if name == "IDX_MAX_KEYS" else int(m.group(1)) << 20
+        assert v == getattr(_lib, name), name
     # the struct mirrors the header's field order
     body = re.search(r"typedef struct idx_problem \{(.*?)\} idx_problem;", text, flags=re.S).group(1)
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
@@ -52,8 +58,8 @@ def test_header_constants_match_binding():
 
 
 def test_abi_version_and_strerror(L):
-    assert L.idx_abi_version() == 2
-    for c in range(6):
+    assert L.idx_abi_version() == 3
+    for c in range(7):
         assert len(L.idx_strerror(c)) > 0
     assert b"unknown" in L.idx_strerror(99)
     assert L.idx_last_hip_error() is not None
@@ -240,3 +246,32 @@ def test_append_validation(L):
     p17, keep17 = make_problem(rows=17, num_req=1, req_indptr=ctypes.cast(ip, ctypes.POINTER(ctypes.c_int32)))
     nk = _lib.IdxNewKeys(**good)
     assert call(ctypes.byref(nk), p17) == _lib.IDX_EUNSUPPORTED
+
+
+def test_max_keys_limit(L):
+    """Rows above IDX_MAX_KEYS keys are refused before any launch (the selection's score
+    offsets are 32-bit)."""
+    out = ctypes.c_size_t(0)
+    assert L.idx_workspace_bytes(4, _lib.IDX_MAX_KEYS, 2048, ctypes.byref(out)) == 0
+    assert L.idx_workspace_bytes(4, _lib.IDX_MAX_KEYS + 1, 2048, ctypes.byref(out)) == _lib.IDX_EUNSUPPORTED
+    big = _lib.IDX_MAX_KEYS + 1
+    p, keep = make_problem(max_pages=(big + 63) // 64, max_keys=big)
+    assert call_all(L, p, ld=big, ws_bytes=1 << 40) == (_lib.IDX_EUNSUPPORTED, _lib.IDX_EUNSUPPORTED)
+    rc = L.idx_topk(FAKE, big, FAKE, 4, big, 2048, FAKE, FAKE, 1 << 40, None)
+    assert rc == _lib.IDX_EUNSUPPORTED
+
+
+def test_build_hash_matches_sources(L):
+    """The loaded library was built from the current sources and flags."""
+    assert L.idx_build_hash().decode() == B.source_hash() == B.library_hash()
+
+
+def test_tagged_validation(L):
+    p, keep = make_problem()
+    need = ws_size(L, 6, 3200)
+    call = lambda tg: L.idx_score_topk_tagged(ctypes.byref(p), 2048, FAKE, 3200, FAKE, tg, 7, FAKE, need, None)
+    assert call(None) == _lib.IDX_EINVAL
+    assert call(FAKE + 4) == _lib.IDX_EINVAL
+    bad, keep2 = make_problem(heads=32)
+    assert L.idx_score_topk_tagged(ctypes.byref(bad), 2048, FAKE, 3200, FAKE, FAKE, 7, FAKE, need, None) == \
+        _lib.IDX_EUNSUPPORTED

@@ -79,3 +79,31 @@ def test_append_bad_position_reported():
                           torch.from_numpy(pos).cuda())
     code, detail = idx.device_status(ws)
     assert code == idx._lib.IDX_EDEVICE and detail & idx._lib.IDX_DERR_NKEYS
+
+
+def test_append_bad_position_dropped_by_every_group():
+    """An 8-row chain (two row groups).  Row 1 (first group) brings a key at a position
+    past its own key count that only the second group's rows see; rows 4-7 write no key.
+    The first group reports and drops it; the second group must drop it too and score
+    the key the cache holds there.  Every row then matches the oracle on the cache with
+    the valid keys written, and that slot is left as it was."""
+    prob = make_problem([9000], [8], seed=9711, name="append_bad8")
+    codes, scales, pos = new_keys(prob, 17, skip=(4, 5, 6, 7))
+    pos[1] = int(prob.n_keys[1]) + 3                          # seen by rows 4..7 only
+    assert pos[1] >= prob.n_keys[3] and pos[1] < prob.n_keys[4]
+    good = pos.copy()
+    good[1] = -1
+    bad = poisoned(prob, good)                                 # the valid keys' slots only
+    print(f"case append bad pos {int(pos[1])}", flush=True)
+    dp = device_problem(bad)
+    ws = idx.Workspace(prob.rows, dp.max_keys, prob.k)
+    sc, ls = idx.score_topk_append(dp, prob.k, ws, torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                                   torch.from_numpy(pos).cuda())
+    code, detail = idx.device_status(ws)
+    assert code == idx._lib.IDX_EDEVICE and detail == idx._lib.IDX_DERR_NKEYS, hex(detail)
+    want = O.with_new_keys(prob, codes, scales, good)
+    assert np.array_equal(dp.k_cache.cpu().numpy().view(np.uint8), want.k_cache)
+    assert np.array_equal(dp.k_scale.cpu().numpy(), want.k_scale)
+    s = sc.cpu().numpy()
+    res = dict(scores=s, lists=ls.cpu().numpy(), scores_only=s, lists_topk=ls.cpu().numpy(), code=0, detail=0)
+    check_against_oracle(want, res)

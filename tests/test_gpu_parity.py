@@ -244,3 +244,89 @@ def test_random_sweep(case):
     print(f"case sweep{case} contexts={contexts} rows={rows} k={k} keys={keys} chain={chain}", flush=True)
     bounds = [int(prob.n_keys[a:b].max()) for a, b in zip(prob.req_indptr[:-1], prob.req_indptr[1:])]
     check_against_oracle(prob, run_all(prob, req_max_keys=bounds if case % 2 else None))
+
+
+@pytest.mark.parametrize("n", [40000, 131072])
+def test_ties_at_random_positions(n):
+    """The ties cache with the 4 vectors laid out at seeded random positions: each block of
+    512 positions draws its vectors from its own Dirichlet(0.3) mix, so a row's best
+    vector is dense in some chunks and sparse (fewer copies than the chunk's candidate
+    rank) in others.  The list is the first k positions holding the row's largest score
+    (a closed form over the GPU's own scores), and the oracle check holds."""
+    prob = make_problem([n], [4], seed=9800 + n, keys="ties", name=f"ties_rand{n}")
+    rng = np.random.default_rng(9900 + n)
+    pt = prob.page_table[0]
+    reps = [(pt[j // 64], j % 64) for j in range(4)]             # positions 0..3 hold vectors 0..3
+    vc = [prob.k_cache[a, b].copy() for a, b in reps]
+    vs = [prob.k_scale[a, b] for a, b in reps]
+    vec = np.empty(n, dtype=np.int64)
+    for b0 in range(0, n, 512):
+        mix = rng.dirichlet([0.3] * 4)
+        vec[b0:b0 + 512] = rng.choice(4, size=min(512, n - b0), p=mix)
+    vec[:4] = np.arange(4)
+    for p in range(n):
+        prob.k_cache[pt[p // 64], p % 64] = vc[vec[p]]
+        prob.k_scale[pt[p // 64], p % 64] = vs[vec[p]]
+    print(f"case ties at random positions n={n}", flush=True)
+    res = run_all(prob)
+    check_against_oracle(prob, res)
+    for r in range(prob.rows):
+        v = res["scores"][r]
+        nr = int(prob.n_keys[r])
+        best = max(v[j] for j in range(4))
+        hold = [p for p in range(nr) if v[p] == best]
+        assert len(hold) >= prob.k, (n, r, len(hold))
+        assert res["lists"][r].tolist() == hold[: prob.k], (n, r)
+
+
+def test_many_requests_to_the_group_limit():
+    """256 row groups in one call, the ABI's limit: 214 one-row requests, 30 two-row
+    chains, 6 five-row chains (two groups each), contexts 0 to 40,000 keys, with and
+    without per-request key bounds; through idx_score_topk, idx_topk and the slot map."""
+    rng = np.random.default_rng(424242)
+    rows = [1] * 214 + [2] * 30 + [5] * 6
+    order = rng.permutation(len(rows))
+    rows = [rows[i] for i in order]
+    contexts = []
+    for i in range(len(rows)):
+        u = rng.random()
+        contexts.append(int(rng.choice([0, 1, 2047, 2048, 2049])) if u < 0.1 else
+                        int(rng.integers(25000, 40001)) if u < 0.2 else int(rng.integers(1, 12000)))
+    groups = sum((r + 3) // 4 for r in rows)
+    assert groups == 256
+    prob = make_problem(contexts, rows, seed=4243, chain=True, name="groups256")
+    print(f"case 256 groups: rows={prob.rows} key_rows={prob.key_rows()}", flush=True)
+    bounds = [int(prob.n_keys[a:b].max()) for a, b in zip(prob.req_indptr[:-1], prob.req_indptr[1:])]
+    ref = O.scores(prob)
+    check_against_oracle(prob, run_all(prob, req_max_keys=bounds), ref=ref)
+    check_against_oracle(prob, run_all(prob), ref=ref)
+    import key_scoring_exact_amd as idx
+    dp = device_problem(prob, req_max_keys=bounds)
+    ws = idx.Workspace(prob.rows, dp.max_keys, prob.k)
+    _, ls, sl = idx.score_topk_slots(dp, prob.k, ws)
+    assert idx.device_status(ws)[0] == 0
+    assert np.array_equal(sl.cpu().numpy(), O.list_slots(prob, ls.cpu().numpy()))
+
+
+def test_topk_over_more_than_1024_rows():
+    """idx_topk over 1,100 rows of given scores runs two launches of row groups; rows of
+    0 to 30,000 keys (some past the all-keys bound, which publish candidates first), with
+    ties at the k-th score in some rows.  Each list is exact over its row's scores."""
+    import key_scoring_exact_amd as idx
+    rng = np.random.default_rng(77)
+    rows, ld, k = 1100, 30000, 2048
+    n = rng.integers(0, 6000, size=rows).astype(np.int32)
+    long_rows = rng.choice(rows, size=40, replace=False)
+    n[long_rows] = rng.integers(24577, ld + 1, size=40)
+    n[:3] = [0, 2048, 2049]
+    sc = rng.standard_normal((rows, ld)).astype(np.float32)
+    sc[10::7, :] = np.round(sc[10::7, :] * 4) / 4            # coarse values: ties at the threshold
+    s_d = torch.from_numpy(sc).cuda()
+    n_d = torch.from_numpy(n).cuda()
+    ws = idx.Workspace(rows, ld, k)
+    print(f"case topk rows={rows} ld={ld}", flush=True)
+    out = idx.topk(s_d, n_d, k, ld, ws).cpu().numpy()
+    assert idx.device_status(ws)[0] == 0
+    for r in range(rows):
+        want = O.select(sc[r].astype(np.float64), int(n[r]), k)
+        assert np.array_equal(out[r], want), (r, int(n[r]))
