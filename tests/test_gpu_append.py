@@ -89,7 +89,7 @@ def test_append_bad_position_dropped_by_every_group():
     the valid keys written, and that slot is left as it was."""
     prob = make_problem([9000], [8], seed=9711, name="append_bad8")
     codes, scales, pos = new_keys(prob, 17, skip=(4, 5, 6, 7))
-    pos[1] = int(prob.n_keys[1]) + 3                          # seen by rows 4..7 only
+    pos[1] = int(prob.n_keys[1]) + 2                          # seen by rows 4..7 only
     assert pos[1] >= prob.n_keys[3] and pos[1] < prob.n_keys[4]
     good = pos.copy()
     good[1] = -1
