@@ -54,6 +54,7 @@ extern "C" {
 #define IDX_GROUP_ROWS 4
 #define IDX_MAX_REQ 256
 #define IDX_MAX_KEYS (1 << 28)               /* keys a row at most (selection offsets stay 32-bit) */
+#define IDX_NOALLOC_SCRATCH_BYTES (16u << 20) /* static scratch of idx_score_topk_noalloc, per device */
 #define IDX_ABI_VERSION 3
 
 /* Return codes. */
@@ -64,6 +65,7 @@ extern "C" {
 #define IDX_EWORKSPACE 3   /* workspace null or smaller than idx_workspace_bytes() */
 #define IDX_EHIP 4         /* a HIP runtime call or launch failed; see idx_last_hip_error() */
 #define IDX_EDEVICE 5      /* a sticky device-side error was found by idx_device_status() */
+#define IDX_ESCRATCH 6     /* idx_score_topk_noalloc: the call needs more than IDX_NOALLOC_SCRATCH_BYTES */
 
 /* Sticky device error bits (idx_device_status(), *detail). */
 #define IDX_DERR_NKEYS 0x1u       /* an n_keys entry was outside [0, max_keys] */
@@ -202,6 +204,22 @@ int idx_score_topk_slots(const idx_problem* p, int32_t k, float* scores, int64_t
 int idx_score_topk_tagged(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores,
                           int32_t* topk, uint64_t* tagged, uint32_t tag, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): idx_score_topk() with the candidate
+ * blocks in a static scratch array of the library instead of a caller's workspace.
+ * Each device holds its own IDX_NOALLOC_SCRATCH_BYTES-byte copy until the process
+ * ends; the call allocates nothing and frees nothing.  The call's workspace need
+ * (idx_workspace_bytes(rows, max_keys, k)) must fit it, else IDX_ESCRATCH.  Uses the
+ * current device's scratch: `stream` must belong to the current device.  Calls on one
+ * device share its scratch: calls whose executions overlap (other streams, other
+ * threads) race and give undefined lists; calls in stream order are safe.  Nothing in
+ * the scratch has to start at zero: every call writes every candidate word it reads.
+ * Device-side errors (n_keys or page ids out of range) are clamped exactly as in
+ * idx_score_topk() but not reported: there is no workspace for idx_device_status().
+ * Returns IDX_OK, IDX_EINVAL, IDX_EUNSUPPORTED, IDX_ESCRATCH or IDX_EHIP. */
+int idx_score_topk_noalloc(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores,
+                           int32_t* topk, void* stream);
 
 /* Index-query preparation (the GLM-5.3 indexer page, Modifications item 2, on preparing
  * the query once a row: each row's index query gets its rotary embedding and the

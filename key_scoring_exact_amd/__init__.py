@@ -20,7 +20,7 @@ from ._lib import (IDX_DIM, IDX_GROUP_ROWS, IDX_HEADS, IDX_KMAX, IDX_MAX_REQ,  #
                    IDX_PAGE_SIZE, IdxProblem)
 
 __all__ = ["IdxError", "DeviceProblem", "Workspace", "score", "topk", "score_topk", "score_topk_append",
-           "score_topk_slots", "score_topk_tagged", "prep_query", "device_status",
+           "score_topk_slots", "score_topk_tagged", "score_topk_noalloc", "prep_query", "device_status",
            "workspace_bytes", "lib"]
 
 
@@ -267,6 +267,18 @@ def score_topk_tagged(p: DeviceProblem, k: int, ws: Workspace, tag: int, scores:
                                        ctypes.c_void_p(_ptr(tagged, torch.int64)), int(tag), ctypes.c_void_p(ws.ptr),
                                        ws.nbytes, ctypes.c_void_p(_stream(stream))), "idx_score_topk_tagged")
     return scores, out, tagged
+
+
+def score_topk_noalloc(p: DeviceProblem, k: int, scores: torch.Tensor, out: torch.Tensor, stream=None):
+    """idx_score_topk_noalloc: as score_topk, with the library's static per-device scratch in
+    place of a workspace; the caller passes the output tensors (nothing is allocated)."""
+    _rows_at_least(scores, p.rows, "scores")
+    _shape(out, (p.rows, k), "out")
+    s, keep = p.struct()
+    _check(lib().idx_score_topk_noalloc(ctypes.byref(s), int(k), ctypes.c_void_p(_ptr(scores, torch.float32)),
+                                        scores.shape[1], ctypes.c_void_p(_ptr(out, torch.int32)),
+                                        ctypes.c_void_p(_stream(stream))), "idx_score_topk_noalloc")
+    return scores, out
 
 
 def topk(scores: torch.Tensor, n_keys: torch.Tensor, k: int, max_keys: int, ws: Workspace,

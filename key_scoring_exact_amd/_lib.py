@@ -14,6 +14,7 @@ IDX_KMAX = 2048
 IDX_GROUP_ROWS = 4
 IDX_MAX_REQ = 256
 IDX_MAX_KEYS = 1 << 28
+IDX_NOALLOC_SCRATCH_BYTES = 16 << 20
 IDX_ABI_VERSION = 3
 
 IDX_OK = 0
@@ -22,6 +23,7 @@ IDX_EUNSUPPORTED = 2
 IDX_EWORKSPACE = 3
 IDX_EHIP = 4
 IDX_EDEVICE = 5
+IDX_ESCRATCH = 6
 
 IDX_DERR_NKEYS = 0x1
 IDX_DERR_PAGE = 0x2
@@ -69,6 +71,7 @@ SIGNATURES = {
     "idx_score_topk_slots": (ctypes.c_int, [ctypes.POINTER(IdxProblem), _i32, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "idx_score_topk_tagged": (ctypes.c_int, [ctypes.POINTER(IdxProblem), _i32, _vp, _i64, _vp, _vp, ctypes.c_uint32,
                                              _vp, _sz, _vp]),
+    "idx_score_topk_noalloc": (ctypes.c_int, [ctypes.POINTER(IdxProblem), _i32, _vp, _i64, _vp, _vp]),
     "idx_prep_query": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "idx_device_status": (ctypes.c_int, [_vp, _sz, _vp, ctypes.POINTER(ctypes.c_uint32)]),
     "idx_strerror": (ctypes.c_char_p, [ctypes.c_int]),

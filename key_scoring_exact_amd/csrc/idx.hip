@@ -41,7 +41,16 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "idx.h"
+
+// Scratch of idx_score_topk_noalloc: the candidate blocks of one call, in place of a
+// caller's workspace.  Each device that runs the library holds its own copy until the
+// process ends.  Host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device (g_scratch below): in host code this name stands for a
+// host-side shadow, not device memory.
+static __device__ __align__(256) uint8_t scratch[IDX_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -62,6 +71,7 @@ constexpr uint32_t WS_MAGIC = 0x1D5C0DE5u;
 
 constexpr int MODE_SCORE = 1;           // compute scores (else read them from args.scores)
 constexpr int MODE_PUBLISH = 2;         // publish each chunk's candidates for the selection launch
+constexpr int MODE_NOMAGIC = 4;         // the workspace is the library's static scratch: no magic word to check
 
 // LDS layout, scoring phase (bytes)
 constexpr int L_KEYS = 0;                                   // [PMAX][64 keys][128 B], swizzled
@@ -1627,7 +1637,7 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
   if (lane == 63) ld_mg = *reinterpret_cast<const int*>(ws + WS_MAGIC_OFF);
   wait_vmcnt<0>();
   const int ld_lane = ld_nk | ld_pt | ld_mg;   // disjoint lanes
-  if ((uint32_t)__builtin_amdgcn_readlane(ld_lane, 63) != WS_MAGIC) {
+  if (!(a.mode & MODE_NOMAGIC) && (uint32_t)__builtin_amdgcn_readlane(ld_lane, 63) != WS_MAGIC) {
     if (tid == 0 && c == 0 && g == 0) raise_error(ws, IDX_DERR_WS);
     return;
   }
@@ -1821,7 +1831,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
   const int wv = wave_id();
   const uint32_t ge = a.grp[blockIdx.y];
   scalars_ready(ge, a.gmax[blockIdx.y], a.ws, a.nk, a.k, a.chunk, a.chunk_shift, a.topk, a.scores, a.ld,
-                a.ent_stride, a.off_ent);
+                a.ent_stride, a.off_ent, a.mode);
   const int R = (int)(ge >> 24);
   const int i = blockIdx.x;
   const int grow = (int)(ge & 0xFFFFFFu) + (i < R ? i : R - 1);   // a row of the group either way
@@ -1831,7 +1841,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
   int nr = __builtin_amdgcn_readfirstlane(a.nk[grow]);
   asm volatile("" ::"s"(magic), "s"(nr));          // both loads issued before the branches below
   if (i >= R) return false;
-  if (magic != WS_MAGIC) {
+  if (!(a.mode & MODE_NOMAGIC) && magic != WS_MAGIC) {
     if (tid == 0 && i == 0 && blockIdx.y == 0) raise_error(ws, IDX_DERR_WS);
     return false;
   }
@@ -2254,7 +2264,7 @@ void fill_common(KArgs& args, const WsLayout& L, void* ws) {
 
 int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int32_t* topk, int32_t* slots,
                 void* ws, size_t ws_bytes, void* stream, bool select, const idx_new_keys* nk = nullptr,
-                uint64_t* tagged = nullptr, uint32_t tag = 0) {
+                bool scratch = false, uint64_t* tagged = nullptr, uint32_t tag = 0) {
   int rc = validate_problem(p);
   if (rc) return rc;
   if (!scores || ld < 1 || ld < (int64_t)p->max_keys) return IDX_EINVAL;
@@ -2289,7 +2299,7 @@ int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int3
   args.k = k;
   args.chunk = pl.chunk;
   args.chunk_shift = 31 - __builtin_clz((unsigned)pl.chunk);
-  args.mode = select ? (MODE_SCORE | MODE_PUBLISH) : MODE_SCORE;
+  args.mode = (select ? (MODE_SCORE | MODE_PUBLISH) : MODE_SCORE) | (scratch ? MODE_NOMAGIC : 0);
   fill_common(args, L, ws);
   if (nk) {
     args.nw_codes = nk->codes;
@@ -2315,11 +2325,48 @@ int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int3
   return launch(args, pl.pages_per_wg, dim3(pl.wg, groups), true, select, static_cast<hipStream_t>(stream));
 }
 
+// Per-device address of `scratch`, looked up once per device with that device current.
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[MAX_DEVICES] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= MAX_DEVICES) return IDX_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 255)) return IDX_EHIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return IDX_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int idx_abi_version(void) { return IDX_ABI_VERSION; }
+
+int idx_score_topk_noalloc(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores, int32_t* topk,
+                           void* stream) {
+  // every host-side check of idx_score_topk first, then the size against the scratch
+  int rc = validate_problem(p);
+  if (rc) return rc;
+  if (k < 1 || k > IDX_KMAX || !topk || !scores) return IDX_EINVAL;
+  if (ld_scores < 1 || ld_scores < (int64_t)p->max_keys || (int64_t)p->rows > INT64_MAX / ld_scores) return IDX_EINVAL;
+  if (layout_for(p->rows, p->max_keys).total > (uint64_t)IDX_NOALLOC_SCRATCH_BYTES) return IDX_ESCRATCH;
+  void* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc) return rc;
+  return run_problem(p, k, scores, ld_scores, topk, nullptr, ws, IDX_NOALLOC_SCRATCH_BYTES, stream, true, nullptr,
+                     true);
+}
 
 int idx_workspace_bytes(int32_t rows, int32_t max_keys, int32_t k, size_t* bytes) {
   if (!bytes || rows < 1 || rows > (1 << 24) - 1 || max_keys < 0 || k < 1 || k > IDX_KMAX) return IDX_EINVAL;
@@ -2369,7 +2416,7 @@ int idx_score_topk_slots(const idx_problem* p, int32_t k, float* scores, int64_t
 int idx_score_topk_tagged(const idx_problem* p, int32_t k, float* scores, int64_t ld_scores, int32_t* topk,
                           uint64_t* tagged, uint32_t tag, void* ws, size_t ws_bytes, void* stream) {
   if (!tagged || (reinterpret_cast<uintptr_t>(tagged) & 7)) return IDX_EINVAL;
-  return run_problem(p, k, scores, ld_scores, topk, nullptr, ws, ws_bytes, stream, true, nullptr, tagged, tag);
+  return run_problem(p, k, scores, ld_scores, topk, nullptr, ws, ws_bytes, stream, true, nullptr, false, tagged, tag);
 }
 
 int idx_topk(const float* scores, int64_t ld_scores, const int32_t* n_keys, int32_t rows, int32_t max_keys,
@@ -2459,6 +2506,7 @@ const char* idx_strerror(int code) {
     case IDX_EWORKSPACE: return "workspace missing, misaligned or too small";
     case IDX_EHIP: return "HIP runtime error";
     case IDX_EDEVICE: return "device-side error recorded in the workspace";
+    case IDX_ESCRATCH: return "problem too large for the static scratch of idx_score_topk_noalloc";
     default: return "unknown error code";
   }
 }

@@ -42,10 +42,10 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ["IDX_HEADS", "IDX_DIM", "IDX_PAGE_SIZE", "IDX_KMAX", "IDX_GROUP_ROWS", "IDX_MAX_REQ",
                  "IDX_OK", "IDX_EINVAL", "IDX_EUNSUPPORTED", "IDX_EWORKSPACE", "IDX_EHIP", "IDX_EDEVICE",
-                 "IDX_ABI_VERSION"]:
+                 "IDX_ESCRATCH", "IDX_ABI_VERSION"]:
         m = re.search(r"#define " + name + r"\s+(\d+)", text)
         assert m and int(m.group(1)) == getattr(_lib, name), name
-    for name, expr in [("IDX_MAX_KEYS", r"\(1 << (\d+)\)")]:
+    for name, expr in [("IDX_MAX_KEYS", r"\(1 << (\d+)\)"), ("IDX_NOALLOC_SCRATCH_BYTES", r"\((\d+)u << 20\)")]:
         m = re.search(r"#define " + name + r"\s+" + expr, text)
         assert m, name
         v = (1 << int(m.group(1))) if name == "IDX_MAX_KEYS" else int(m.group(1)) << 20
@@ -275,3 +275,27 @@ def test_tagged_validation(L):
     bad, keep2 = make_problem(heads=32)
     assert L.idx_score_topk_tagged(ctypes.byref(bad), 2048, FAKE, 3200, FAKE, FAKE, 7, FAKE, need, None) == \
         _lib.IDX_EUNSUPPORTED
+
+
+def test_noalloc_validation(L):
+    """idx_score_topk_noalloc checks its arguments like idx_score_topk, and refuses a problem
+    whose workspace need exceeds the static scratch, before any HIP call."""
+    p, keep = make_problem()
+    call = lambda prob, k=2048, sc=FAKE, tk=FAKE, ld=3200: L.idx_score_topk_noalloc(ctypes.byref(prob), k, sc, ld, tk,
+                                                                                     None)
+    assert call(p, k=0) == _lib.IDX_EINVAL
+    assert call(p, tk=None) == _lib.IDX_EINVAL
+    assert call(p, sc=None) == _lib.IDX_EINVAL
+    assert call(p, ld=3199) == _lib.IDX_EINVAL
+    bad, keep2 = make_problem(q=None)
+    assert call(bad) == _lib.IDX_EINVAL
+    # 64 rows of 131,072 keys need 16 MiB + 256 B of candidate blocks: one header too many
+    rows = 64
+    ip = (ctypes.c_int32 * 17)(*range(0, rows + 1, 4))
+    big, keep3 = make_problem(rows=rows, num_req=16, req_indptr=ctypes.cast(ip, ctypes.POINTER(ctypes.c_int32)),
+                              max_pages=2048, max_keys=131072, num_pages=2048)
+    assert ws_size(L, rows, 131072) > _lib.IDX_NOALLOC_SCRATCH_BYTES
+    assert call(big, ld=131072) == _lib.IDX_ESCRATCH
+    rows = 60
+    ip = (ctypes.c_int32 * 16)(*range(0, rows + 1, 4))
+    assert ws_size(L, rows, 131072) <= _lib.IDX_NOALLOC_SCRATCH_BYTES

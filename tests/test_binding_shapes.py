@@ -54,6 +54,8 @@ def test_output_shapes():
     with pytest.raises(ValueError, match="tag"):
         idx.score_topk_tagged(p, 16, ws, 1 << 32, scores=torch.zeros((4, 256)),
                               out=torch.zeros((4, 16), dtype=torch.int32), tagged=torch.zeros((4, 16), dtype=torch.int64))
+    with pytest.raises(ValueError, match="out"):
+        idx.score_topk_noalloc(p, 16, torch.zeros((4, 256)), torch.zeros((4, 8), dtype=torch.int32))
 
 
 def test_append_shapes():
