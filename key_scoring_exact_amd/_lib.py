@@ -82,11 +82,8 @@ SIGNATURES = {
 _lib = None
 
 
-def load(path: str = LIB_PATH):
-    """Load libidx.so (built by key_scoring_exact_amd.build); raise if it is missing."""
-    global _lib
-    if _lib is not None:
-        return _lib
+def load_file(path: str):
+    """Load a build of the library from `path` with every signature declared (uncached)."""
     if not os.path.exists(path):
         raise ImportError(f"libidx.so is not built ({path}); run key_scoring_exact_amd.build.build()")
     lib = ctypes.CDLL(path)
@@ -94,5 +91,12 @@ def load(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
     return lib
+
+
+def load(path: str = LIB_PATH):
+    """Load libidx.so (built by key_scoring_exact_amd.build); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        _lib = load_file(path)
+    return _lib

@@ -103,6 +103,29 @@ constexpr int WS_MAGIC_OFF = 0;
 constexpr int WS_ERR_OFF = 4;
 constexpr int WS_HDR = 256;
 
+// Stage timestamps (a build with -DIDX_STAMPS only): thread 0 of a workgroup writes the
+// 100 MHz real-time counter at stage ends into 16 slots of its own record, in an area
+// past the candidate blocks.  Scoring workgroup (x, y) owns record y * gridDim.x + x;
+// selecting workgroup (x, y) owns record STAMP_SELECT + y * 4 + x.  Nothing else reads
+// the area; the ordinary build compiles the stamps out.
+constexpr int STAMP_SLOTS = 16;
+constexpr int STAMP_SELECT = 8192;
+constexpr int STAMP_RECORDS = STAMP_SELECT + 4 * IDX_MAX_REQ;
+#ifdef IDX_STAMPS
+constexpr uint64_t STAMP_BYTES = (uint64_t)STAMP_RECORDS * STAMP_SLOTS * 8;
+#define STAMP(a, rec, id)                                                                              \
+  do {                                                                                                 \
+    if (threadIdx.x == 0)                                                                              \
+      reinterpret_cast<uint64_t*>((a).ws + (a).off_stamps)[(uint64_t)(rec) * STAMP_SLOTS + (id)] =    \
+          __builtin_amdgcn_s_memrealtime();                                                            \
+  } while (0)
+#else
+constexpr uint64_t STAMP_BYTES = 0;
+#define STAMP(a, rec, id) \
+  do {                    \
+  } while (0)
+#endif
+
 struct KArgs {
   const uint8_t* q;         // bf16 [rows][64][128]
   const uint8_t* w;         // bf16 [rows][64]
@@ -133,6 +156,7 @@ struct KArgs {
   float* ks_w;
   uint64_t* tagged;         // [rows][k] or null: the slots as tagged words, tag << 32 | slot
   uint32_t tag;
+  uint64_t off_stamps;      // stage timestamps (IDX_STAMPS builds only)
 };
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -152,20 +176,6 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   int64_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : (bytes < 0 ? 0 : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
-}
-
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// 16-byte global -> LDS DMA per lane: lane l writes LDS bytes [lds + 16 l, lds + 16 l + 16).
-// Written as inline assembly so that the compiler neither tracks it nor inserts its own
-// conservative waits before LDS reads; callers wait with explicit vmcnt counts.
-__device__ inline void dma16(const void* gptr, uint32_t lds_wave_base) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base))
-               : "memory");
 }
 
 __device__ inline void raise_error(uint8_t* ws, uint32_t bits) {
@@ -957,22 +967,6 @@ __device__ __forceinline__ bool block_any(bool p, int* misc) {
   return (a[0] | a[1] | a[2] | a[3] | b[0] | b[1] | b[2] | b[3]) != 0;
 }
 
-// wait until this wave's DMAs of pages [0, x] are done, pages [0, issued) having
-// been issued in page order, 2 DMA instructions per page per wave
-__device__ inline void wait_pages_through(int x, int issued) {
-  switch (2 * (issued - 1 - x)) {
-    case 0: wait_vmcnt<0>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    default: wait_vmcnt<0>(); break;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // scoring of one chunk: scores of the group's rows land in sc_lds[row][0..C)
 // TS = tile stride = waves per row (8 / R, 2 for R = 3); each wave scores one row.
@@ -987,11 +981,17 @@ struct Patches {
   float nscl;
 };
 
+// The group's queries, head weights and (with PATCH) the request's new key codes, as
+// 16-byte pieces in registers: thread t holds pieces t, t + NT, ... of each array.
+struct Staged {
+  v4u q[2 * GR];
+  v4u w, codes;
+};
+
 template <int P, int TS, bool PATCH>
 __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R, int c, const int* phys,
-                                            const Patches& pt) {
+                                            const Patches& pt, int srec, const Staged& sg) {
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
-  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   float* const sc_lds = LDS_PTR(float, L_SC);
   constexpr int T = (2 * P + TS - 1) / TS;      // tiles of 32 keys per wave
   const int lr = wv / TS;                       // this wave's row (>= R: an idle wave)
@@ -1000,19 +1000,40 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
   const int lrr = live ? lr : 0;
   const int g2 = lane >> 5;
 
+  // Key pages stream through registers: thread t loads bytes [16 t, 16 t + 16) of a page
+  // (key t / 8, 16-byte chunk t % 8; one coalesced 8 KiB read a page), and threads [0, 64)
+  // one key scale each.  Ordinary vector loads: the compiler counts them and waits for
+  // exactly the page being staged.  Staging writes chunk g of key kn to LDS slot
+  // g ^ ((kn / 2) % 8), so the operand reads below hit distinct banks.
+  v4u pgv[P];
+  uint32_t psv[P];
   auto issue_page = [&](int j) {
-    const uint8_t* pg = a.kc + (int64_t)phys[j] * (PS * D);
-    const int kn = tid >> 3, cs = tid & 7;
-    const int ch = cs ^ ((kn >> 1) & 7);
-    dma16(pg + kn * D + ch * 16, lds0 + L_KEYS + j * (PS * D) + wv * 1024);
-    // every wave issues the scale DMA (2 active lanes) so that all waves count alike
-    if (lane < 2) dma16(a.ks + (int64_t)phys[j] * PS + wv * 8 + lane * 4, lds0 + L_KSC + j * (PS * 4) + wv * 32);
+    pgv[j] = *reinterpret_cast<const v4u*>(a.kc + (int64_t)phys[j] * (PS * D) + tid * 16);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.ks + (int64_t)phys[j] * PS, PS * 4);
+    psv[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, tid < PS ? tid * 4 : 0x7FFFFFF0, 0, 0);
   };
-  constexpr int L0 = (P < LOOKAHEAD) ? P : LOOKAHEAD;
+  auto stage_page = [&](int j) {
+    const int kn = tid >> 3, g = tid & 7;
+    *reinterpret_cast<v4u*>(smem + L_KEYS + j * (PS * D) + kn * D + ((g ^ ((kn >> 1) & 7)) << 4)) = pgv[j];
+    if (tid < PS) LDS_PTR(uint32_t, L_KSC)[j * PS + tid] = psv[j];
+  };
+  constexpr int L0 = (P < LOOKAHEAD + 1) ? P : LOOKAHEAD + 1;
 #pragma unroll
   for (int j = 0; j < L0; j++) issue_page(j);
-  // queries and head weights (issued first, waited for with the key counts) are in LDS
-  __syncthreads();
+  // the queries, head weights and new key codes into LDS (their loads were issued before
+  // the pages', so waiting for them leaves the pages in flight)
+  {
+#pragma unroll
+    for (int u = 0; u < 2 * GR; u++) {
+      const int off = (u * NT + tid) * 16;                 // byte offset in the group's queries
+      const int rr = off >> 14, h = (off >> 8) & (H - 1), cpos = (off >> 4) & 15;
+      if (u < 2 * R)
+        *reinterpret_cast<v4u*>(smem + L_Q + rr * (H * D * 2) + h * (D * 2) + ((cpos ^ (h & 15)) << 4)) = sg.q[u];
+    }
+    if (tid < R * (H * 2 / 16)) *reinterpret_cast<v4u*>(smem + L_W + tid * 16) = sg.w;
+    if (PATCH && tid < NEW_MAX * (D / 16)) *reinterpret_cast<v4u*>(smem + L_PATCH + tid * 16) = sg.codes;
+  }
+  __syncthreads();                              // the queries and head weights are in LDS
 
   // A operands: bf16 MFMA 32x32x16, lane l supplies row l % 32 and 8 consecutive k of
   // its half l / 32.  K step s of half g covers d = 64 g + 8 s .. +8 (the keys use the
@@ -1083,6 +1104,7 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
   auto page_of_iter = [&](int i) { return ((i * TS + TS - 1) >> 1) < P - 1 ? ((i * TS + TS - 1) >> 1) : P - 1; };
 
   int issued = L0;
+  int staged = -1;                              // pages [0, staged] are in LDS
   int patched = -1;                             // pages [0, patched] hold this launch's new keys
   const int cbase = c * (P * PS);
   // the new keys of pages (patched, x] into the landed pages (wave 0: 8 lanes of codes,
@@ -1117,23 +1139,23 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
     __syncthreads();
   };
   auto ensure_page = [&](int x) {
-    // pages [0, x] issued and landed (all waves' parts), then LOOKAHEAD more in flight
-#pragma unroll
-    for (int j = 0; j < P; j++)
-      if (j >= issued && j <= x) issue_page(j);
-    if (issued < x + 1) issued = x + 1;
-    wait_pages_through(x, issued);
-    __syncthreads();
-    if constexpr (PATCH) {
-      if (pt.hit != 0ull) patch_pages(x);
-    }
+    // pages through x + LOOKAHEAD issued, pages [0, x] staged by every thread, a barrier
 #pragma unroll
     for (int j = 0; j < P; j++)
       if (j >= issued && j <= x + LOOKAHEAD) issue_page(j);
     if (issued < x + LOOKAHEAD + 1) issued = (x + LOOKAHEAD + 1 < P) ? x + LOOKAHEAD + 1 : P;
+#pragma unroll
+    for (int j = 0; j < P; j++)
+      if (j > staged && j <= x) stage_page(j);
+    if (staged < x) staged = x;
+    __syncthreads();
+    if constexpr (PATCH) {
+      if (pt.hit != 0ull) patch_pages(x);
+    }
   };
 
   ensure_page(page_of_iter(0));
+  STAMP(a, srec, 2);
   uint32_t kw_cur[16], kw_nxt[16];
   load_raw(0, kw_cur);
   v16f accp0 = {}, accp1 = {};
@@ -1578,6 +1600,8 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
   const int wv = wave_id();
   const int c = blockIdx.x;
   const int g = blockIdx.y;
+  const int srec = g * gridDim.x + c;
+  STAMP(a, srec, 0);
   const uint32_t ge = a.grp[g];
   const int row0 = (int)(ge & 0xFFFFFFu);
   const int R = (int)(ge >> 24);
@@ -1590,33 +1614,10 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
   if (c > 0 && chunk_base >= gbound) return;      // beyond every row of this group
   const bool do_score = (a.mode & MODE_SCORE) != 0;
   const bool do_pub = (a.mode & MODE_PUBLISH) != 0;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  if (do_score) {
-    // Queries and head weights of the group's rows into LDS first (2R + 1 DMA per
-    // wave); their latency overlaps the n_keys / page-table load below.  Head h's 16
-    // chunks of 16 bytes sit at chunk positions c ^ (h & 15), so the A-operand reads
-    // (16 lanes on 16 heads, same chunk) hit distinct banks.
-    for (int ii = wv * 2 * R; ii < (wv + 1) * 2 * R; ii++) {
-      const int rr = ii >> 4;
-      const int s16 = (ii & 15) * 64 + lane;
-      const int h = s16 >> 4, cpos = s16 & 15;
-      const int ch = cpos ^ (h & 15);
-      dma16(a.q + ((int64_t)(row0 + rr) * H * D + h * D) * 2 + ch * 16, lds0 + L_Q + rr * (H * D * 2) + (ii & 15) * 1024);
-    }
-    if (lane < 8) dma16(a.w + (int64_t)(row0 + (wv % R)) * H * 2 + lane * 16, lds0 + L_W + (wv % R) * (H * 2));
-  }
-  // keys written in this launch: the request's rows' codes into L_PATCH (wave 0, two
-  // DMAs: lane l of DMA i copies chunk l % 8 of row 8 i + l / 8), their positions and
-  // scales with the key counts below (lanes [0, request rows))
+  // keys written in this launch: their positions and scales load with the key counts
+  // below (lanes [0, request rows)), their codes with the queries
   const uint32_t rq = PATCH ? a.req[g] : 0u;
   const int rq0 = (int)(rq & 0xFFFFFFu), rqn = (int)(rq >> 24);
-  if (do_score && rqn > 0 && wv == 0) {
-#pragma unroll
-    for (int i2 = 0; i2 < 2; i2++) {
-      const int b = i2 * 8 + (lane >> 3);
-      if (b < rqn) dma16(a.nw_codes + (int64_t)(rq0 + b) * D + (lane & 7) * 16, lds0 + L_PATCH + i2 * 1024);
-    }
-  }
   int ld_np = -1, ld_rn = 0;
   float ld_ns = 0.f;
   if (do_score && lane < rqn) {
@@ -1635,12 +1636,31 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
     if (c * P + j < a.max_pages) ld_pt = a.pt[(int64_t)(row0 + i) * a.max_pages + c * P + j];
   }
   if (lane == 63) ld_mg = *reinterpret_cast<const int*>(ws + WS_MAGIC_OFF);
-  wait_vmcnt<0>();
+  // The group's queries (R rows of 16 KiB), head weights and the request's new key codes
+  // into registers, issued after the loads above so that their wait covers only those:
+  // the page loads need the page ids, not the queries.  Pieces outside each array's range
+  // read zeros from outside the buffer resource (no memory traffic).
+  __builtin_amdgcn_sched_barrier(0);
+  Staged sg;
+  if (do_score) {
+    const __amdgpu_buffer_rsrc_t rq_ = make_rsrc(a.q + (int64_t)row0 * (H * D * 2), (int64_t)R * (H * D * 2));
+#pragma unroll
+    for (int u = 0; u < 2 * GR; u++)
+      sg.q[u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rq_, (u * NT + tid) * 16, 0, 0));
+    const __amdgpu_buffer_rsrc_t rw_ = make_rsrc(a.w + (int64_t)row0 * (H * 2), (int64_t)R * (H * 2));
+    sg.w = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rw_, tid * 16, 0, 0));
+    if (PATCH) {
+      const __amdgpu_buffer_rsrc_t rc_ = make_rsrc(a.nw_codes + (int64_t)rq0 * D, (int64_t)rqn * D);
+      sg.codes = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rc_, tid * 16, 0, 0));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   const int ld_lane = ld_nk | ld_pt | ld_mg;   // disjoint lanes
   if (!(a.mode & MODE_NOMAGIC) && (uint32_t)__builtin_amdgcn_readlane(ld_lane, 63) != WS_MAGIC) {
     if (tid == 0 && c == 0 && g == 0) raise_error(ws, IDX_DERR_WS);
     return;
   }
+  STAMP(a, srec, 1);
 
   int n[GR];
   int nmax = 0, rmax = 0;
@@ -1702,9 +1722,10 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
       pt.hit = __ballot(inr && !bad && ld_np >= chunk_base && ld_np < chunk_base + C && ld_np < nmax);
       pt.mine = __ballot(inr && own >= 0 && own < R);
     }
-    if (R == 1) score_chunk<P, 8, PATCH>(a, smem, R, c, phys, pt);
-    else if (R == 2) score_chunk<P, 4, PATCH>(a, smem, R, c, phys, pt);
-    else score_chunk<P, 2, PATCH>(a, smem, R, c, phys, pt);
+    if (R == 1) score_chunk<P, 8, PATCH>(a, smem, R, c, phys, pt, srec, sg);
+    else if (R == 2) score_chunk<P, 4, PATCH>(a, smem, R, c, phys, pt, srec, sg);
+    else score_chunk<P, 2, PATCH>(a, smem, R, c, phys, pt, srec, sg);
+    STAMP(a, srec, 3);
   } else {
 #pragma unroll
     for (int i = 0; i < GR; i++) {
@@ -1732,6 +1753,7 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
     }
   }
 
+  STAMP(a, srec, 4);
   // ---------------- publish (wave i handles row i) -----------------------------------
   if (do_pub && wv < R) {
     const int i = wv;
@@ -1819,6 +1841,7 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
       for (int q = lane; q < SL; q += 64) blk[q] = stg[q];
     }
   }
+  STAMP(a, srec, 5);
 }
 
 // ---------------------------------------------------------------------------
@@ -1835,6 +1858,8 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
   const int R = (int)(ge >> 24);
   const int i = blockIdx.x;
   const int grow = (int)(ge & 0xFFFFFFu) + (i < R ? i : R - 1);   // a row of the group either way
+  const int qrec = STAMP_SELECT + blockIdx.y * 4 + i;
+  STAMP(a, qrec, 0);
   uint8_t* const ws = a.ws;
   // the magic word and the row's key count in flight together, before any branch
   const uint32_t magic = *reinterpret_cast<const uint32_t*>(ws + WS_MAGIC_OFF);
@@ -1939,6 +1964,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
       }
     }
     block_sum_max_max_sum(t4, misc);
+    STAMP(a, qrec, 1);
     // keys >= t* are all published (t* is at least every chunk's t_w): if k of them are
     // here, the k-th is among them and no chunk hides a key of the top k.  Only they are
     // gathered.  (0x00800000 is the smallest key of a finite score.)
@@ -1977,6 +2003,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
         }
         E += got;
       }
+      STAMP(a, qrec, 2);
       if (fits) {
         pad_cand(cand, E);
         __syncthreads();
@@ -2006,6 +2033,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
     __syncthreads();
     global_select_row(srow, nr, k, out, hist, misc);
   }
+  STAMP(a, qrec, 4);
   return true;
 }
 
@@ -2151,7 +2179,7 @@ Plan plan_topk(int max_keys) {
 }
 
 struct WsLayout {
-  uint64_t off_ent, total;
+  uint64_t off_ent, off_stamps, total;
   int ent_stride;
 };
 
@@ -2168,7 +2196,8 @@ WsLayout layout_for(int rows, int max_keys) {
   WsLayout L;
   L.ent_stride = stride < 4 * NT ? stride : 4 * NT;     // rows with more chunks never publish
   L.off_ent = WS_HDR;
-  L.total = align256(L.off_ent + (uint64_t)rows * L.ent_stride * CAP_MAX * 8);
+  L.off_stamps = align256(L.off_ent + (uint64_t)rows * L.ent_stride * CAP_MAX * 8);
+  L.total = align256(L.off_stamps + STAMP_BYTES);
   return L;
 }
 
@@ -2260,6 +2289,7 @@ void fill_common(KArgs& args, const WsLayout& L, void* ws) {
   args.ws = static_cast<uint8_t*>(ws);
   args.ent_stride = L.ent_stride;
   args.off_ent = L.off_ent;
+  args.off_stamps = L.off_stamps;
 }
 
 int run_problem(const idx_problem* p, int32_t k, float* scores, int64_t ld, int32_t* topk, int32_t* slots,
