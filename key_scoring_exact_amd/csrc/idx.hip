@@ -62,7 +62,9 @@ constexpr int NT = 512;                 // threads per workgroup: 8 waves, two p
 constexpr int NWAVE = NT / 64;
 constexpr int PMAX = 8;                 // pages per workgroup at most
 constexpr int CMAX = PMAX * PS;         // keys per chunk at most (512)
-constexpr int LOOKAHEAD = 3;            // pages in flight ahead of the page being scored
+// pages in flight beyond the ones an iteration of the tile loop stages (TS / 2 pages an
+// iteration, TS = waves a row): about four pages in registers in every case
+__host__ __device__ constexpr int lookahead(int TS) { return TS == 2 ? 2 : 1; }
 constexpr int ALL_MAX = 24576;          // rows up to this many keys select from all scores at once
 constexpr int FIN_ENT = 12288;          // candidate capacity of a selecting workgroup
 constexpr int BITMAP_KEYS = 131072;     // positions covered by the finisher's LDS bitmap
@@ -74,14 +76,25 @@ constexpr int MODE_PUBLISH = 2;         // publish each chunk's candidates for t
 constexpr int MODE_NOMAGIC = 4;         // the workspace is the library's static scratch: no magic word to check
 
 // LDS layout, scoring phase (bytes)
-constexpr int L_KEYS = 0;                                   // [PMAX][64 keys][128 B], swizzled
-constexpr int L_KSC = PMAX * PS * D;                        // [PMAX][64] f32 key scales
-constexpr int L_SC = L_KSC + PMAX * PS * 4;                 // [GR][CMAX] f32 scores of the chunk
-constexpr int L_Q = L_SC + GR * CMAX * 4;                   // [GR][64 heads][256 B] bf16 queries, swizzled
-constexpr int L_W = L_Q + GR * H * D * 2;                   // [GR][64] bf16 head weights
 constexpr int NEW_MAX = 16;                                 // rows a request, when keys are written in the launch
+constexpr int L_SC = 0;                                     // [GR][CMAX] f32 scores of the chunk
+constexpr int L_KSC = L_SC + GR * CMAX * 4;                 // [PMAX][64] f32 key scales
+constexpr int L_W = L_KSC + PMAX * PS * 4;                  // [GR][64] bf16 head weights
 constexpr int L_PATCH = L_W + GR * H * 2;                   // [NEW_MAX][128 B] the request's new key codes
-constexpr int L_SCORE_END = L_PATCH + NEW_MAX * D;
+constexpr int L_KEYS = L_PATCH + NEW_MAX * D;               // ring of key pages widened to bf16, [slot][64 keys][256 B]
+constexpr int PAGE16 = PS * D * 2;                          // one page in bf16
+// The ring holds the pages of two iterations of the tile loop (TS / 2 pages an
+// iteration, TS = waves a row), and the queries follow it: 8 / TS rows of 16 KiB.
+__host__ __device__ constexpr int key_slots(int P, int TS) { return P < TS ? P : TS; }
+__host__ __device__ constexpr int l_q(int P, int TS) { return L_KEYS + key_slots(P, TS) * PAGE16; }
+__host__ __device__ constexpr int l_end(int P, int TS) { return l_q(P, TS) + (8 / TS) * H * D * 2; }
+constexpr int L_SCORE_END = l_end(PMAX, 8) > l_end(PMAX, 2) ? l_end(PMAX, 8) : l_end(PMAX, 2);
+// the publication's scratch, in the ring once the tile loop is done
+constexpr int L_STG = L_KEYS;                               // [GR][CAP_MAX] u64 staged candidate blocks
+constexpr int L_PHIST = L_STG + GR * CAP_MAX * 8;           // [GR][128] u32 chunk histograms
+constexpr int L_KST = L_PHIST + GR * 128 * 4;               // [GR][64] u32 keys of a bisection
+static_assert(L_KST + GR * 64 * 4 <= L_KEYS + PAGE16, "publication scratch fits one ring slot");
+static_assert(L_KEYS % 16 == 0 && l_end(PMAX, 4) <= L_SCORE_END, "layout");
 // LDS layout, finishing phase
 constexpr int HIST_WORDS = 4096 + 64;                       // one histogram: 4096 bins + 64 per-lane dummies
 constexpr int L_HIST = 0;                                   // 2 histograms (low addresses: offsets fold into ds_add)
@@ -119,10 +132,30 @@ constexpr uint64_t STAMP_BYTES = (uint64_t)STAMP_RECORDS * STAMP_SLOTS * 8;
       reinterpret_cast<uint64_t*>((a).ws + (a).off_stamps)[(uint64_t)(rec) * STAMP_SLOTS + (id)] =    \
           __builtin_amdgcn_s_memrealtime();                                                            \
   } while (0)
+// the same through a record pointer (null: no stamp), for helpers without the arguments
+#define STAMPP(p, id)                                                            \
+  do {                                                                           \
+    if (threadIdx.x == 0 && (p)) (p)[id] = __builtin_amdgcn_s_memrealtime();     \
+  } while (0)
+// the shader clock (s_memtime) and the real-time counter together, into slots id, id + 2
+#define STAMPCLK(a, rec, id)                                                                      \
+  do {                                                                                            \
+    if (threadIdx.x == 0) {                                                                       \
+      uint64_t* r_ = reinterpret_cast<uint64_t*>((a).ws + (a).off_stamps) + (uint64_t)(rec) * STAMP_SLOTS; \
+      r_[id] = __builtin_amdgcn_s_memtime();                                                      \
+      r_[(id) + 2] = __builtin_amdgcn_s_memrealtime();                                            \
+    }                                                                                             \
+  } while (0)
 #else
+#define STAMPCLK(a, rec, id) \
+  do {                       \
+  } while (0)
 constexpr uint64_t STAMP_BYTES = 0;
 #define STAMP(a, rec, id) \
   do {                    \
+  } while (0)
+#define STAMPP(p, id) \
+  do {                \
   } while (0)
 #endif
 
@@ -413,6 +446,17 @@ __device__ __forceinline__ void block_min_max(uint32_t& mn, uint32_t& mx, int* m
   __syncthreads();
 }
 
+// Sum over the workgroup (wave-uniform result).  Every thread must call.
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, int* misc) {
+  v = wave_sum_u32(v);
+  if (lane_id() == 0) misc[wave_id()] = (int)v;
+  __syncthreads();
+  const v4i a = reinterpret_cast<const v4i*>(misc)[0];
+  const v4i b = reinterpret_cast<const v4i*>(misc)[1];
+  __syncthreads();
+  return (uint32_t)(a[0] + a[1] + a[2] + a[3] + b[0] + b[1] + b[2] + b[3]);
+}
+
 // zero the 4096 bins of both histogram buffers (no barrier)
 __device__ __forceinline__ void clear_hist(uint32_t* hist) {
   const v4i z = {0, 0, 0, 0};
@@ -427,10 +471,17 @@ __device__ __forceinline__ void clear_hist(uint32_t* hist) {
 
 template <int SMAX>
 __device__ __forceinline__ bool kth_select(const uint32_t (&kr)[SMAX], int S, int cnt, uint32_t lo, uint32_t hi,
-                                           int k, uint32_t* hist, int* misc, uint32_t* Tge_out, int* rem_out) {
+                                           int k, uint32_t* hist, int* misc, uint32_t* Tge_out, int* rem_out,
+                                           uint64_t* stp = nullptr) {
   static_assert(SMAX % 4 == 0, "slot groups of 4");
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
-  if (cnt < k) return false;
+  if (cnt < 0 && lo == hi) {                          // an unknown count is needed here: count the keys
+    uint32_t c0 = 0;
+#pragma unroll
+    for (int j = 0; j < SMAX; j++) c0 += (j < S && kr[j] != 0u) ? 1u : 0u;
+    cnt = (int)block_sum(c0, misc);
+  }
+  if (cnt >= 0 && cnt < k) return false;
   if (lo == hi) {  // every key equal: the first k of them (all of them when cnt == k)
     *Tge_out = cnt == k ? lo : lo + 1u;
     *rem_out = cnt == k ? 0 : k;
@@ -440,14 +491,20 @@ __device__ __forceinline__ bool kth_select(const uint32_t (&kr)[SMAX], int S, in
   uint32_t klo = lo, khi = hi;                        // keys in play: [klo, khi]
   int rem = k, buf = 0;
 
-  // ---- linear pass
+  // ---- linear pass: 4096 bins linear in the score over [lo, hi], bin(key) =
+  // floor(score * s - lo_score * s) with s = 4096 / (hi_score - lo_score), the product and
+  // difference rounded once (an fma), clamped to [0, 4095]: a once-rounded monotone function
+  // of the score, so every key of a higher bin is larger than every key of a lower one
   const float fmin = key_float(lo);
   const float span = key_float(hi) - fmin;
   const float scale = 4096.0f / span;
   if (span <= 3.0e38f && scale <= 3.0e38f) {          // both finite (false for inf, NaN)
     const float off = -fmin * scale;
     uint32_t idx[SMAX];
-    if (tid == 0) misc[11] = 0;                       // list counter
+    if (tid == 0) {
+      misc[10] = -1;                                  // no bin found (fewer than k keys)
+      misc[11] = 0;                                   // list counter
+    }
 #pragma unroll
     for (int g = 0; g < SMAX / 4; g++) {
       if (g * 4 < S) {
@@ -465,10 +522,13 @@ __device__ __forceinline__ bool kth_select(const uint32_t (&kr)[SMAX], int S, in
       }
     }
     __syncthreads();
+    STAMPP(stp, 6);
     find_digit(hist, 4096, rem, misc);
+    STAMPP(stp, 7);
     const uint32_t d = (uint32_t)misc[8];
     const int r = misc[9];
     const int c = misc[10];
+    if (c < 0) return false;                          // fewer than k keys
     if (c == 1) {
       // bin d holds one key, the k-th: every key above it and it are in (r == 1)
 #pragma unroll
@@ -638,6 +698,9 @@ __device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], const u
   int tot;
   const int packed = block_excl_scan(gt | (eq << 16), misc, &tot);
   const int before_gt = packed & 0xFFFF, before_eq = packed >> 16;
+  // stores without branches: an unselected slot stores past the buffer resource, which
+  // drops it
+  const __amdgpu_buffer_rsrc_t rout = make_rsrc(out, (int64_t)k * 4);
   if (rem == 0) {
     int o = before_gt;
 #pragma unroll
@@ -646,7 +709,7 @@ __device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], const u
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
         const bool sel = kr[g * 4 + jj] >= Tge;
-        if (sel && o < k) out[o] = (int32_t)pr[g * 4 + jj];
+        __builtin_amdgcn_raw_buffer_store_b32(pr[g * 4 + jj], rout, sel ? o * 4 : 0x7FFFFFF0, 0, 0);
         o += sel ? 1 : 0;
       }
     }
@@ -662,7 +725,7 @@ __device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], const u
         const bool e = key == T;
         const bool sel = key >= Tge || (e && er < rem);
         er += e ? 1 : 0;
-        if (sel && o < k) out[o] = (int32_t)pr[g * 4 + jj];
+        __builtin_amdgcn_raw_buffer_store_b32(pr[g * 4 + jj], rout, sel ? o * 4 : 0x7FFFFFF0, 0, 0);
         o += sel ? 1 : 0;
       }
     }
@@ -762,10 +825,10 @@ __device__ int select_explicit(const uint64_t* cand, int E, int n, int k, uint32
 // The result is (Tge, rem): every key >= Tge is selected, and the first rem keys equal to
 // Tge - 1.  An ordered emission (16 consecutive positions a thread, one block scan a
 // round) writes the list and stops once k positions are out.  Every thread must call.
-__device__ __forceinline__ void emit_ordered(const float* row, int n, int k, uint32_t Tge, int trem, int32_t* out,
-                                             int* misc);
+__device__ __noinline__ void emit_ordered(const float* row, int n, int k, uint32_t Tge, int trem, int32_t* out,
+                                          int* misc);
 
-__device__ __forceinline__ void global_select_row(const float* row, int n, int k, int32_t* out, uint32_t* hist, int* misc) {
+__device__ __noinline__ void global_select_row(const float* row, int n, int k, int32_t* out, uint32_t* hist, int* misc) {
   const int tid = threadIdx.x;
   __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (int64_t)n * 4);
   constexpr int U = 8;                                // 16-byte loads a thread per round
@@ -832,8 +895,8 @@ __device__ __forceinline__ void global_select_row(const float* row, int n, int k
 // Ordered emission over a row's scores in memory: every key >= Tge and the first trem
 // keys equal to Tge - 1, in position order, into out[0 .. k); stops once k are out.
 // Every thread must call.
-__device__ __forceinline__ void emit_ordered(const float* row, int n, int k, uint32_t Tge, int trem, int32_t* out,
-                                             int* misc) {
+__device__ __noinline__ void emit_ordered(const float* row, int n, int k, uint32_t Tge, int trem, int32_t* out,
+                                          int* misc) {
   const int tid = threadIdx.x;
   __amdgpu_buffer_rsrc_t rs = make_rsrc(row, (int64_t)n * 4);
   const uint32_t Teq = Tge - 1u;
@@ -994,6 +1057,8 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   float* const sc_lds = LDS_PTR(float, L_SC);
   constexpr int T = (2 * P + TS - 1) / TS;      // tiles of 32 keys per wave
+  constexpr int KS = key_slots(P, TS);          // page slots of the LDS ring
+  constexpr int LQ = l_q(P, TS);                // the queries, after the ring
   const int lr = wv / TS;                       // this wave's row (>= R: an idle wave)
   const int toff = wv % TS;
   const bool live = lr < R;
@@ -1003,8 +1068,10 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
   // Key pages stream through registers: thread t loads bytes [16 t, 16 t + 16) of a page
   // (key t / 8, 16-byte chunk t % 8; one coalesced 8 KiB read a page), and threads [0, 64)
   // one key scale each.  Ordinary vector loads: the compiler counts them and waits for
-  // exactly the page being staged.  Staging writes chunk g of key kn to LDS slot
-  // g ^ ((kn / 2) % 8), so the operand reads below hit distinct banks.
+  // exactly the page being staged.  Staging widens the 16 E4M3 codes to bf16 (exact: every
+  // finite E4M3 value is a bf16 value) once for all the waves that read them, and writes
+  // 16-byte chunk e (8 dimensions) of key kn at position e ^ (kn % 16) of the key's 256
+  // bytes, so that the operand reads below (32 keys, one chunk each) hit distinct banks.
   v4u pgv[P];
   uint32_t psv[P];
   auto issue_page = [&](int j) {
@@ -1012,12 +1079,28 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.ks + (int64_t)phys[j] * PS, PS * 4);
     psv[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rk, tid < PS ? tid * 4 : 0x7FFFFFF0, 0, 0);
   };
+  // 16 E4M3 codes (4 words) to 16 bf16 (two 16-byte chunks), and their place in a key row
+  auto widen16 = [](const v4u x, v4u& lo, v4u& hi) {
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, false));
+      const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[w], 1.0f, true));
+      if (w < 2) { lo[2 * w] = p0; lo[2 * w + 1] = p1; }
+      else { hi[2 * (w - 2)] = p0; hi[2 * (w - 2) + 1] = p1; }
+    }
+  };
+  auto key_row = [&](int j, int kn) { return smem + L_KEYS + (j % KS) * PAGE16 + kn * (D * 2); };
   auto stage_page = [&](int j) {
-    const int kn = tid >> 3, g = tid & 7;
-    *reinterpret_cast<v4u*>(smem + L_KEYS + j * (PS * D) + kn * D + ((g ^ ((kn >> 1) & 7)) << 4)) = pgv[j];
+    const int kn = tid >> 3, e = tid & 7;
+    v4u lo, hi;
+    widen16(pgv[j], lo, hi);
+    uint8_t* kb = key_row(j, kn);
+    *reinterpret_cast<v4u*>(kb + (((2 * e) ^ (kn & 15)) << 4)) = lo;
+    *reinterpret_cast<v4u*>(kb + (((2 * e + 1) ^ (kn & 15)) << 4)) = hi;
     if (tid < PS) LDS_PTR(uint32_t, L_KSC)[j * PS + tid] = psv[j];
   };
-  constexpr int L0 = (P < LOOKAHEAD + 1) ? P : LOOKAHEAD + 1;
+  constexpr int LA = lookahead(TS);
+  constexpr int L0 = (P < LA + 1) ? P : LA + 1;
 #pragma unroll
   for (int j = 0; j < L0; j++) issue_page(j);
   // the queries, head weights and new key codes into LDS (their loads were issued before
@@ -1028,7 +1111,7 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
       const int off = (u * NT + tid) * 16;                 // byte offset in the group's queries
       const int rr = off >> 14, h = (off >> 8) & (H - 1), cpos = (off >> 4) & 15;
       if (u < 2 * R)
-        *reinterpret_cast<v4u*>(smem + L_Q + rr * (H * D * 2) + h * (D * 2) + ((cpos ^ (h & 15)) << 4)) = sg.q[u];
+        *reinterpret_cast<v4u*>(smem + LQ + rr * (H * D * 2) + h * (D * 2) + ((cpos ^ (h & 15)) << 4)) = sg.q[u];
     }
     if (tid < R * (H * 2 / 16)) *reinterpret_cast<v4u*>(smem + L_W + tid * 16) = sg.w;
     if (PATCH && tid < NEW_MAX * (D / 16)) *reinterpret_cast<v4u*>(smem + L_PATCH + tid * 16) = sg.codes;
@@ -1041,7 +1124,7 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
   v8bf aq[2][8];
   float wr[2][16];
   {
-    const uint8_t* qrow = smem + L_Q + lrr * (H * D * 2);
+    const uint8_t* qrow = smem + LQ + lrr * (H * D * 2);
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
       const int h = mt * 32 + (lane & 31);
@@ -1060,43 +1143,31 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
   }
   const float* ksl = LDS_PTR(const float, L_KSC);
 
-  // raw E4M3 words of this wave's tile i: key kn = (t & 1) * 32 + lane % 32, bytes
-  // d = 64 g .. 64 g + 64 (4 swizzled 16-byte chunks)
-  auto load_raw = [&](int i, uint32_t* kw) {
+  // B operand of K step st of this wave's tile i: key kn = (t & 1) * 32 + lane % 32 of
+  // page t / 2 (t = toff + i TS), dimensions 64 g2 + 8 st .. + 8, in bf16
+  auto load_b = [&](int i, int st) -> v8bf {
     const int t = toff + i * TS;
-    const int j = t >> 1;
     const int kn = (t & 1) * 32 + (lane & 31);
-    const uint8_t* kb = smem + L_KEYS + j * (PS * D) + kn * D;
-    const int swz = (kn >> 1) & 7;
+    const uint8_t* kb = key_row(t >> 1, kn);
+    return __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(kb + (((g2 * 8 + st) ^ (kn & 15)) << 4)));
+  };
+  // the head-weighted ReLU sum of one M tile's 16 accumulator rows
+  auto head_sum = [&](int mt, const v16f& acc) {
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < 4; cc++) {
-      const v4i x = *reinterpret_cast<const v4i*>(kb + (((4 * g2 + cc) ^ swz) << 4));
-      kw[4 * cc + 0] = (uint32_t)x[0];
-      kw[4 * cc + 1] = (uint32_t)x[1];
-      kw[4 * cc + 2] = (uint32_t)x[2];
-      kw[4 * cc + 3] = (uint32_t)x[3];
+    for (int q = 0; q < 16; q += 2) {
+      s0 = fmaf(wr[mt][q], relu(acc[q]), s0);
+      s1 = fmaf(wr[mt][q + 1], relu(acc[q + 1]), s1);
     }
+    return s0 + s1;
   };
-  // 8 E4M3 codes of K step st, widened exactly to bf16
-  auto widen = [&](const uint32_t* kw, int st) -> v8bf {
-    const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st], 1.0f, false);
-    const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st], 1.0f, true);
-    const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st + 1], 1.0f, false);
-    const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kw[2 * st + 1], 1.0f, true);
-    return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-  };
-  auto epilogue = [&](int i, const v16f& acc0, const v16f& acc1) {
+  // tile i's score: both M tiles' sums, the two lane halves, then x s (canonical +0)
+  auto finish = [&](int i, float part0, float part1) {
     const int t = toff + i * TS;
     const int j = t >> 1;
     const int kn = (t & 1) * 32 + (lane & 31);
     const float ksv = ksl[j * PS + kn];
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int q = 0; q < 16; q++) {
-      s0 = fmaf(wr[0][q], relu(acc0[q]), s0);
-      s1 = fmaf(wr[1][q], relu(acc1[q]), s1);
-    }
-    float sum = s0 + s1;
+    float sum = part0 + part1;
     sum += __shfl_xor(sum, 32);
     if (live && lane < 32) sc_lds[lr * CMAX + t * 32 + lane] = sum * ksv + 0.0f;
   };
@@ -1104,11 +1175,12 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
   auto page_of_iter = [&](int i) { return ((i * TS + TS - 1) >> 1) < P - 1 ? ((i * TS + TS - 1) >> 1) : P - 1; };
 
   int issued = L0;
-  int staged = -1;                              // pages [0, staged] are in LDS
+  int staged = -1;                              // pages [0, staged] are in the ring
   int patched = -1;                             // pages [0, patched] hold this launch's new keys
   const int cbase = c * (P * PS);
-  // the new keys of pages (patched, x] into the landed pages (wave 0: 8 lanes of codes,
-  // one of scale), and into the cache for this group's rows; then a barrier
+  // the new keys of pages (patched, x] into the staged pages (wave 0: 8 lanes of codes,
+  // widened as the pages are, one lane of scale), and into the cache for this group's
+  // rows; then a barrier
   auto patch_pages = [&](int x) {
     uint64_t todo = 0;
     for (uint64_t m = pt.hit; m != 0; m &= m - 1) {
@@ -1126,9 +1198,13 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
         const bool store = (pt.mine >> b) & 1ull;
         const int64_t slot = (int64_t)phys[j] * PS + kn;
         if (lane < 8) {
-          const v4i v = *reinterpret_cast<const v4i*>(smem + L_PATCH + b * D + lane * 16);
-          *reinterpret_cast<v4i*>(smem + L_KEYS + j * (PS * D) + kn * D + ((lane ^ ((kn >> 1) & 7)) << 4)) = v;
-          if (store) *reinterpret_cast<v4i*>(a.kc_w + slot * D + lane * 16) = v;
+          const v4u v = *reinterpret_cast<const v4u*>(smem + L_PATCH + b * D + lane * 16);
+          v4u lo, hi;
+          widen16(v, lo, hi);
+          uint8_t* kb = key_row(j, kn);
+          *reinterpret_cast<v4u*>(kb + (((2 * lane) ^ (kn & 15)) << 4)) = lo;
+          *reinterpret_cast<v4u*>(kb + (((2 * lane + 1) ^ (kn & 15)) << 4)) = hi;
+          if (store) *reinterpret_cast<v4u*>(a.kc_w + slot * D + lane * 16) = v;
         } else if (lane == 8) {
           const float sv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pt.nscl), b));
           LDS_PTR(float, L_KSC)[j * PS + kn] = sv;
@@ -1139,11 +1215,11 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
     __syncthreads();
   };
   auto ensure_page = [&](int x) {
-    // pages through x + LOOKAHEAD issued, pages [0, x] staged by every thread, a barrier
+    // pages through x + LA issued, pages [0, x] staged by every thread, a barrier
 #pragma unroll
     for (int j = 0; j < P; j++)
-      if (j >= issued && j <= x + LOOKAHEAD) issue_page(j);
-    if (issued < x + LOOKAHEAD + 1) issued = (x + LOOKAHEAD + 1 < P) ? x + LOOKAHEAD + 1 : P;
+      if (j >= issued && j <= x + LA) issue_page(j);
+    if (issued < x + LA + 1) issued = (x + LA + 1 < P) ? x + LA + 1 : P;
 #pragma unroll
     for (int j = 0; j < P; j++)
       if (j > staged && j <= x) stage_page(j);
@@ -1156,53 +1232,53 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
 
   ensure_page(page_of_iter(0));
   STAMP(a, srec, 2);
-  uint32_t kw_cur[16], kw_nxt[16];
-  load_raw(0, kw_cur);
-  v16f accp0 = {}, accp1 = {};
+  STAMPCLK(a, srec, 12);
+  // B operands of the tile being computed; each K step's registers take the next tile's
+  // operand once that step's second MFMA is issued.  The two M tiles run as two MFMA
+  // chains, each overlapped with the other tile's head sum, so that two accumulators
+  // are live at a time: chain 0 of tile i with the M tile 1 sum of tile i - 1, chain 1
+  // of tile i with the M tile 0 sum of tile i.
+  v8bf bq[8];
+#pragma unroll
+  for (int st = 0; st < 8; st++) bq[st] = load_b(0, st);
+  v16f accp1 = {};
+  float part0 = 0.f;
 #pragma unroll
   for (int i = 0; i < T; i++) {
+    // the ring slot the next tile's page takes was last read two iterations ago: this
+    // barrier orders those reads before the staging writes
     if (i + 1 < T) ensure_page(page_of_iter(i + 1));
-    // one scheduling region: this tile's MFMAs, the previous tile's epilogue and the
-    // next tile's raw loads, interleaved so the VALU runs while the matrix core works
-    if (i + 1 < T) load_raw(i + 1, kw_nxt);
-    v16f acc0 = {}, acc1 = {};
+    v16f acc0 = {};
+#pragma unroll
+    for (int st = 0; st < 8; st++) acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0][st], bq[st], acc0, 0, 0, 0);
+    if (i > 0) finish(i - 1, part0, head_sum(1, accp1));
 #pragma unroll
     for (int st = 0; st < 8; st++) {
-      const v8bf b = widen(kw_cur, st);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0][st], b, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[1][st], b, acc1, 0, 0, 0);
-    }
-    if (i > 0) epilogue(i - 1, accp0, accp1);
-#pragma unroll
-    for (int q = 0; q < 4; q++) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS reads first
-#pragma unroll
-    for (int q = 0; q < 16; q++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                             // 6 VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);                             // 5 VALU
     }
-    accp0 = acc0;
-    accp1 = acc1;
+    v16f acc1 = {};
 #pragma unroll
-    for (int q = 0; q < 16; q++) kw_cur[q] = kw_nxt[q];
+    for (int st = 0; st < 8; st++) {
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[1][st], bq[st], acc1, 0, 0, 0);
+      if (i + 1 < T) bq[st] = load_b(i + 1, st);
+    }
+    part0 = head_sum(0, acc0);
+#pragma unroll
+    for (int st = 0; st < 8; st++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);                             // 4 VALU
+      if (i + 1 < T) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // 1 DS read
+    }
+    accp1 = acc1;
   }
-  epilogue(T - 1, accp0, accp1);
+  finish(T - 1, part0, head_sum(1, accp1));
   __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-// Sum over the workgroup (wave-uniform result).  Every thread must call.
-__device__ __forceinline__ uint32_t block_sum(uint32_t v, int* misc) {
-  v = wave_sum_u32(v);
-  if (lane_id() == 0) misc[wave_id()] = (int)v;
-  __syncthreads();
-  const v4i a = reinterpret_cast<const v4i*>(misc)[0];
-  const v4i b = reinterpret_cast<const v4i*>(misc)[1];
-  __syncthreads();
-  return (uint32_t)(a[0] + a[1] + a[2] + a[3] + b[0] + b[1] + b[2] + b[3]);
-}
-
 // t[0] and t[3] summed, t[1] and t[2] maxed over the workgroup.  Every thread must call.
 __device__ __forceinline__ void block_sum_max_max_sum(uint32_t (&t)[4], int* misc) {
   const uint32_t a = wave_sum_u32(t[0]), b = wave_max_u32(t[1]), c = wave_max_u32(t[2]), d = wave_sum_u32(t[3]);
@@ -1325,7 +1401,7 @@ __device__ __forceinline__ void pad_cand(uint64_t* cand, int E) {
 // Returns false (writing nothing) when fewer than k are present.  Every thread must call.
 template <int SMAX>
 __device__ __forceinline__ bool select_cand(uint64_t* cand, int E, uint32_t lo, uint32_t hi, int k, uint32_t* hist,
-                                            int* misc, int32_t* out, int* got) {
+                                            int* misc, int32_t* out, int* got, uint64_t* stp = nullptr) {
   const int S = slots_for(E);
   const v4u* src = reinterpret_cast<const v4u*>(cand + threadIdx.x * S);
   uint32_t kr[SMAX], pr[SMAX];
@@ -1344,7 +1420,9 @@ __device__ __forceinline__ bool select_cand(uint64_t* cand, int E, uint32_t lo, 
   }
   uint32_t Tge;
   int rem;
-  if (!kth_select<SMAX>(kr, S, E, lo, hi, k, hist, misc, &Tge, &rem)) return false;
+  STAMPP(stp, 5);
+  if (!kth_select<SMAX>(kr, S, E, lo, hi, k, hist, misc, &Tge, &rem, stp)) return false;
+  STAMPP(stp, 3);
   *got = emit_segments<SMAX>(kr, pr, S, Tge, rem, out, k, misc);
   return true;
 }
@@ -1353,7 +1431,7 @@ __device__ __forceinline__ bool select_cand(uint64_t* cand, int E, uint32_t lo, 
 // slots_for(n)), keys within [lo, hi].  As select_cand otherwise.
 template <int SMAX>
 __device__ __forceinline__ bool select_all(uint32_t* fk, int n, uint32_t lo, uint32_t hi, int k, uint32_t* hist,
-                                           int* misc, int32_t* out, int* got) {
+                                           int* misc, int32_t* out, int* got, uint64_t* stp = nullptr) {
   const int S = slots_for(n);
   const int e0 = threadIdx.x * S;
   const v4u* src = reinterpret_cast<const v4u*>(fk + e0);
@@ -1369,7 +1447,9 @@ __device__ __forceinline__ bool select_all(uint32_t* fk, int n, uint32_t lo, uin
   }
   uint32_t Tge;
   int rem;
-  if (!kth_select<SMAX>(kr, S, n, lo, hi, k, hist, misc, &Tge, &rem)) return false;
+  STAMPP(stp, 5);
+  if (!kth_select<SMAX>(kr, S, n, lo, hi, k, hist, misc, &Tge, &rem, stp)) return false;
+  STAMPP(stp, 3);
   *got = emit_segments<SMAX>(kr, pr, S, Tge, rem, out, k, misc);
   return true;
 }
@@ -1463,7 +1543,7 @@ __device__ __forceinline__ int emit_merged(const uint64_t* cand, int E0, int E1,
 // through a position bitmap when a tie at the k-th key is cut (select_explicit).
 // Returns true when it selected, false to fall back to the multi-pass select over
 // memory.  Every thread must call.
-__device__ __forceinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact, int E, int C, uint32_t lo,
+__device__ __noinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact, int E, int C, uint32_t lo,
                                             __amdgpu_buffer_rsrc_t rs, uint64_t* cand, uint32_t* bm,
                                             uint32_t* hist, int* misc, int32_t* out) {
   const int tid = threadIdx.x;
@@ -1725,6 +1805,7 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
     if (R == 1) score_chunk<P, 8, PATCH>(a, smem, R, c, phys, pt, srec, sg);
     else if (R == 2) score_chunk<P, 4, PATCH>(a, smem, R, c, phys, pt, srec, sg);
     else score_chunk<P, 2, PATCH>(a, smem, R, c, phys, pt, srec, sg);
+    STAMPCLK(a, srec, 13);
     STAMP(a, srec, 3);
   } else {
 #pragma unroll
@@ -1786,8 +1867,7 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
       }
       const uint32_t cmax = wave_max_u32(lmax);
       uint32_t thr;
-      // the queries are in registers: their LDS area holds each wave's scratch
-      if (!chunk_bound_linear(fv, key, lmax, cmax, m, cap, LDS_PTR(uint32_t, L_Q) + 1024 + i * 128, &thr)) {
+      if (!chunk_bound_linear(fv, key, lmax, cmax, m, cap, LDS_PTR(uint32_t, L_PHIST) + i * 128, &thr)) {
         const uint32_t thr0 = wave_kth_bound(lmax, m, wave_min_u32(lmax), cmax, 12);
         int cnt0 = 0;
 #pragma unroll
@@ -1796,7 +1876,7 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
         const int total0 = __builtin_amdgcn_readlane(incl0, 63);
         thr = thr0;
         if (total0 <= 64) {
-          uint32_t* kst = LDS_PTR(uint32_t, L_Q) + i * 64;
+          uint32_t* kst = LDS_PTR(uint32_t, L_KST) + i * 64;
           int o = incl0 - cnt0;
 #pragma unroll
           for (int j = 0; j < 8; j++)
@@ -1817,7 +1897,7 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
       const int incl = wave_incl_scan(cnt);
       const int total = __shfl(incl, 63);
       const int SL = 32 * G;
-      uint64_t* stg = LDS_PTR(uint64_t, L_KEYS) + i * CAP_MAX;   // the pages are consumed
+      uint64_t* stg = LDS_PTR(uint64_t, L_STG) + i * CAP_MAX;    // the ring is free by now
       for (int q = lane; q < SL; q += 64) stg[q] = 0ull;
       const bool fits = total <= cap;
       if (fits) {
@@ -1860,6 +1940,12 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
   const int grow = (int)(ge & 0xFFFFFFu) + (i < R ? i : R - 1);   // a row of the group either way
   const int qrec = STAMP_SELECT + blockIdx.y * 4 + i;
   STAMP(a, qrec, 0);
+  STAMPCLK(a, qrec, 12);
+#ifdef IDX_STAMPS
+  uint64_t* const stp = reinterpret_cast<uint64_t*>(a.ws + a.off_stamps) + (uint64_t)qrec * STAMP_SLOTS;
+#else
+  uint64_t* const stp = nullptr;
+#endif
   uint8_t* const ws = a.ws;
   // the magic word and the row's key count in flight together, before any branch
   const uint32_t magic = *reinterpret_cast<const uint32_t*>(ws + WS_MAGIC_OFF);
@@ -1921,8 +2007,9 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
         *reinterpret_cast<v4u*>(fk + p) = v4u{y[0], y[1], y[2], y[3]};
       }
     block_min_max(mn, mx, misc);                     // its barriers also publish fk
+    STAMP(a, qrec, 1);
     int got = -1;
-    done = select_all<ALL_MAX / NT>(fk, nr, mn + 1u, mx, k, hist, misc, out, &got);
+    done = select_all<ALL_MAX / NT>(fk, nr, mn + 1u, mx, k, hist, misc, out, &got, stp);
     if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
   } else if (path == PATH_CAND) {
     const int wact = (nr + C - 1) >> a.chunk_shift;
@@ -1932,6 +2019,57 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
     candidate_params(nr, C, k, &m_unused, &cap, &G);
     const int SL = 32 * G;                           // slots a chunk
     __amdgpu_buffer_rsrc_t rent = make_rsrc(erow, (int64_t)wact * SL * 8);
+    if (wact * SL <= NT * 16) {
+      // One load of everything: thread t holds slots [16 t, 16 t + 16) of the row's blocks
+      // (chunk t / 2G), the header and maximum of chunk t / 2G among them when t % 2G == 0;
+      // slots past the row's blocks read zeros.  Across threads the candidates run in
+      // position order, so the selection works on the registers as loaded: a header,
+      // maximum or empty slot has an upper word below every key, and the keys below t*
+      // are dropped as absent.
+      v4u sv[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++)
+        sv[u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rent, (16 * tid + 2 * u) * 8, 0, 0));
+      uint32_t t4[4] = {0u, 0u, 0u, 0u};
+      if (tid % (2 * G) == 0) {                      // a header (zeros past the row: no effect)
+        const uint32_t tw = sv[0][0], flags = sv[0][1], cmax = sv[0][2];
+        const bool ov = (flags >> 16) & 1u;
+        t4[0] = ov ? 0u : (flags & 0xFFFFu);
+        t4[1] = ov ? 0u : tw;
+        t4[2] = cmax;
+        t4[3] = ov ? 1u : 0u;
+      }
+      block_sum_max_max_sum(t4, misc);
+      STAMP(a, qrec, 1);
+      if (t4[3] == 0u) {
+        const uint32_t lo = t4[1] > 0x00800000u ? t4[1] : 0x00800000u;
+        const uint32_t hi = t4[2] > lo ? t4[2] : lo;
+        uint32_t kr[16], pr[16];
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; h2++) {
+            const uint32_t key = sv[u][2 * h2 + 1];
+            kr[2 * u + h2] = key >= lo ? key : 0u;
+            pr[2 * u + h2] = sv[u][2 * h2];
+          }
+        uint32_t Tge;
+        int rem;
+        STAMPP(stp, 5);
+        // the count of keys >= t* is unknown here: kth_select finds out whether k are present
+        if (kth_select<16>(kr, 16, -1, lo, hi, k, hist, misc, &Tge, &rem, stp)) {
+          STAMPP(stp, 3);
+          const int got = emit_segments<16>(kr, pr, 16, Tge, rem, out, k, misc);
+          if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
+          done = true;
+        }
+      }
+      if (!done) {
+        __syncthreads();                             // misc may still be read
+        clear_hist(hist);                            // the general path below expects clear histograms
+      }
+    }
+    if (!done) {
     // the chunk headers with their maxima (thread t: chunks t + NT u; past wact outside
     // the buffer resource), then the first gather batch, in flight together
     uint64_t e[2 * GQ];
@@ -2009,7 +2147,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
         __syncthreads();
         if (t4[3] == 0u) {
           int got = -1;
-          done = select_cand<FIN_ENT / NT>(cand, E, lo, hi, k, hist, misc, out, &got);
+          done = select_cand<FIN_ENT / NT>(cand, E, lo, hi, k, hist, misc, out, &got, stp);
           if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
         }
         if (!done && nr <= BITMAP_KEYS && (E >= k || (int)t4[0] <= FIN_ENT)) {
@@ -2027,6 +2165,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
         }
       }
     }
+    }
   }
   if (!done) {
     // ---- exact multi-pass select over the row's scores in memory
@@ -2034,6 +2173,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
     global_select_row(srow, nr, k, out, hist, misc);
   }
   STAMP(a, qrec, 4);
+  STAMPCLK(a, qrec, 13);
   return true;
 }
 

@@ -9,10 +9,13 @@ the time from the call's first scoring workgroup start, and the stage's own dura
 
     python -m key_scoring_exact_amd.stage_stamps [--config c2] [--calls 50]
 
-Stages of the scoring launch (per workgroup): 1 key counts, page ids and queries in
-registers/LDS; 2 the first key page in LDS; 3 MFMA loop and epilogue done; 4 score
-stores issued; 5 candidate publication done (wave 0's row).  Of the selection launch
-(per row): 0 start; 1 chunk headers reduced; 2 candidates gathered; 4 list written.
+Stages of the scoring launch (per workgroup): 1 key counts and page ids in registers;
+2 the first key page in LDS; 3 MFMA loop and epilogue done; 4 score stores issued; 5
+candidate publication done (wave 0's row).  Of the selection launch (per row): 0 start;
+1 chunk headers reduced (or, for a row selected from all its scores, those scores in
+LDS); 2 candidates gathered; 5 keys in registers; 6 linear histogram built; 7 bin of the
+k-th key found; 3 k-th key resolved; 4 list written.  A stage a row does not pass is
+left out of that row's figures.
 """
 from __future__ import annotations
 
@@ -31,8 +34,9 @@ TICK_US = 0.01                              # 100 MHz counter
 SCORE_STAGES = [(1, "key counts, page ids, queries loaded"), (2, "first key page in LDS"),
                 (3, "MFMA loop and epilogue done"), (4, "score stores issued"),
                 (5, "publication done (wave 0)")]
-SELECT_STAGES = [(0, "selection start"), (1, "chunk headers reduced"), (2, "candidates gathered"),
-                 (4, "list written")]
+SELECT_STAGES = [(0, "selection start"), (1, "chunk headers reduced, or the row's scores in LDS"),
+                 (2, "candidates gathered"), (5, "keys in registers"), (6, "linear histogram"),
+                 (7, "bin of the k-th key found"), (3, "k-th key resolved"), (4, "list written")]
 
 
 def main(argv=None):
@@ -93,6 +97,7 @@ def main(argv=None):
     durs = {("score", s): [] for s, _ in SCORE_STAGES}
     durs.update({("select", s): [] for s, _ in SELECT_STAGES})
     total = []
+    clocks = {}
     for i in range(args.calls):
         buf[stamps_off: stamps_off + area].zero_()
         call(i)
@@ -109,17 +114,28 @@ def main(argv=None):
                 per_stage[("score", s)].append(float(np.median(sc[ok, s] - t0)))
                 prev = s - 1
                 durs[("score", s)].append(float(np.median(sc[ok, s] - sc[ok, prev])))
-        for s, _ in SELECT_STAGES:
+        order = [p for p, _ in SELECT_STAGES]
+        for idx_s, (s, _) in enumerate(SELECT_STAGES):
             ok = se[:, s] > 0
-            if ok.any():
-                per_stage[("select", s)].append(float(np.median(se[ok, s] - t0)))
-                if s > 0:
-                    prev = max(p for p, _ in SELECT_STAGES if p < s)
-                    ok2 = ok & (se[:, prev] > 0)
-                    durs[("select", s)].append(float(np.median(se[ok2, s] - se[ok2, prev])))
-                else:
-                    durs[("select", s)].append(float(np.median(se[ok, 0] - sc[:, 5][sc[:, 5] > 0].max())))
+            if not ok.any():
+                continue
+            per_stage[("select", s)].append(float(np.median(se[ok, s] - t0)))
+            if s == 0:
+                durs[("select", s)].append(float(np.median(se[ok, 0] - sc[:, 5][sc[:, 5] > 0].max())))
+                continue
+            # the stage's duration from the latest earlier stage the row passed
+            prev = np.zeros(len(se), dtype=np.int64)
+            for p in order[:idx_s]:
+                prev = np.where(se[:, p] > 0, se[:, p], prev)
+            durs[("select", s)].append(float(np.median(se[ok, s] - prev[ok])))
         total.append(float(se[:, 4].max() - t0) if len(se) else float("nan"))
+        # shader clock over the tile loop and over the selection: s_memtime ticks per
+        # real-time tick (100 MHz), in GHz
+        for name, r in (("score", sc), ("select", se)):
+            ok = (r[:, 15] > r[:, 14]) & (r[:, 13] > r[:, 12])
+            if ok.any():
+                clocks.setdefault(name, []).append(
+                    float(np.median((r[ok, 13] - r[ok, 12]) / (r[ok, 15] - r[ok, 14]) * 0.1)))
     print(f"# stage stamps, {args.config}: {prob.rows} rows, n_keys {int(prob.n_keys.min())}..{int(prob.n_keys.max())}, "
           f"{args.calls} calls over {copies} key-cache copies; median over calls of the median over workgroups, us")
     print("| launch | stage | ends at (from first scoring workgroup start) | takes (per workgroup) |")
@@ -128,10 +144,15 @@ def main(argv=None):
         print(f"| scoring | {name} | {statistics.median(per_stage[('score', s)]) * TICK_US:.2f} | "
               f"{statistics.median(durs[('score', s)]) * TICK_US:.2f} |")
     for s, name in SELECT_STAGES:
+        if not per_stage[("select", s)]:
+            continue
         lab = name if s else name + " (after the last scoring workgroup's stamp 5)"
         print(f"| selection | {lab} | {statistics.median(per_stage[('select', s)]) * TICK_US:.2f} | "
               f"{statistics.median(durs[('select', s)]) * TICK_US:.2f} |")
     print(f"| call | first scoring start to last list written | {statistics.median(total) * TICK_US:.2f} | |")
+    for name, v in clocks.items():
+        lab = "the tile loop of a scoring workgroup" if name == "score" else "a row's selection"
+        print(f"shader clock over {lab}: {statistics.median(v):.2f} GHz (median)")
 
 
 if __name__ == "__main__":
