@@ -1161,15 +1161,20 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
     }
     return s0 + s1;
   };
-  // tile i's score: both M tiles' sums, the two lane halves, then x s (canonical +0)
-  auto finish = [&](int i, float part0, float part1) {
+  // the key scale of this lane's key in tile i (read ahead of the tile's last sums)
+  auto key_scale = [&](int i) {
     const int t = toff + i * TS;
-    const int j = t >> 1;
-    const int kn = (t & 1) * 32 + (lane & 31);
-    const float ksv = ksl[j * PS + kn];
-    float sum = part0 + part1;
-    sum += __shfl_xor(sum, 32);
-    if (live && lane < 32) sc_lds[lr * CMAX + t * 32 + lane] = sum * ksv + 0.0f;
+    return ksl[(t >> 1) * PS + (t & 1) * 32 + (lane & 31)];
+  };
+  // tile i's score: both M tiles' sums, the two lane halves (lane l < 32 takes lane l + 32's
+  // sum by a permlane32 swap, a VALU lane move: no LDS round trip inside the MFMA chains),
+  // then x s (canonical +0)
+  auto finish = [&](int i, float part0, float part1, float ksv) {
+    const int t = toff + i * TS;
+    const float sum = part0 + part1;
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
+    const float tot = sum + __uint_as_float(sw[1]);
+    if (live && lane < 32) sc_lds[lr * CMAX + t * 32 + lane] = tot * ksv + 0.0f;
   };
   // the highest page any wave reads at iteration i
   auto page_of_iter = [&](int i) { return ((i * TS + TS - 1) >> 1) < P - 1 ? ((i * TS + TS - 1) >> 1) : P - 1; };
@@ -1242,16 +1247,17 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
 #pragma unroll
   for (int st = 0; st < 8; st++) bq[st] = load_b(0, st);
   v16f accp1 = {};
-  float part0 = 0.f;
+  float part0 = 0.f, kscp = 0.f;
 #pragma unroll
   for (int i = 0; i < T; i++) {
+    const float ksc = key_scale(i);
     // the ring slot the next tile's page takes was last read two iterations ago: this
     // barrier orders those reads before the staging writes
     if (i + 1 < T) ensure_page(page_of_iter(i + 1));
     v16f acc0 = {};
 #pragma unroll
     for (int st = 0; st < 8; st++) acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[0][st], bq[st], acc0, 0, 0, 0);
-    if (i > 0) finish(i - 1, part0, head_sum(1, accp1));
+    if (i > 0) finish(i - 1, part0, head_sum(1, accp1), kscp);
 #pragma unroll
     for (int st = 0; st < 8; st++) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                             // 1 MFMA
@@ -1271,8 +1277,9 @@ __device__ __forceinline__ void score_chunk(const KArgs& a, uint8_t* smem, int R
       if (i + 1 < T) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // 1 DS read
     }
     accp1 = acc1;
+    kscp = ksc;
   }
-  finish(T - 1, part0, head_sum(1, accp1));
+  finish(T - 1, part0, head_sum(1, accp1), kscp);
   __syncthreads();
 }
 
