@@ -97,7 +97,6 @@ def main(argv=None):
     durs = {("score", s): [] for s, _ in SCORE_STAGES}
     durs.update({("select", s): [] for s, _ in SELECT_STAGES})
     total = []
-    clocks = {}
     for i in range(args.calls):
         buf[stamps_off: stamps_off + area].zero_()
         call(i)
@@ -129,13 +128,6 @@ def main(argv=None):
                 prev = np.where(se[:, p] > 0, se[:, p], prev)
             durs[("select", s)].append(float(np.median(se[ok, s] - prev[ok])))
         total.append(float(se[:, 4].max() - t0) if len(se) else float("nan"))
-        # shader clock over the tile loop and over the selection: s_memtime ticks per
-        # real-time tick (100 MHz), in GHz
-        for name, r in (("score", sc), ("select", se)):
-            ok = (r[:, 15] > r[:, 14]) & (r[:, 13] > r[:, 12])
-            if ok.any():
-                clocks.setdefault(name, []).append(
-                    float(np.median((r[ok, 13] - r[ok, 12]) / (r[ok, 15] - r[ok, 14]) * 0.1)))
     print(f"# stage stamps, {args.config}: {prob.rows} rows, n_keys {int(prob.n_keys.min())}..{int(prob.n_keys.max())}, "
           f"{args.calls} calls over {copies} key-cache copies; median over calls of the median over workgroups, us")
     print("| launch | stage | ends at (from first scoring workgroup start) | takes (per workgroup) |")
@@ -150,9 +142,6 @@ def main(argv=None):
         print(f"| selection | {lab} | {statistics.median(per_stage[('select', s)]) * TICK_US:.2f} | "
               f"{statistics.median(durs[('select', s)]) * TICK_US:.2f} |")
     print(f"| call | first scoring start to last list written | {statistics.median(total) * TICK_US:.2f} | |")
-    for name, v in clocks.items():
-        lab = "the tile loop of a scoring workgroup" if name == "score" else "a row's selection"
-        print(f"shader clock over {lab}: {statistics.median(v):.2f} GHz (median)")
 
 
 if __name__ == "__main__":
