@@ -67,7 +67,6 @@ constexpr int CMAX = PMAX * PS;         // keys per chunk at most (512)
 __host__ __device__ constexpr int lookahead(int TS) { return TS == 2 ? 2 : 1; }
 constexpr int ALL_MAX = 24576;          // rows up to this many keys select from all scores at once
 constexpr int FIN_ENT = 12288;          // candidate capacity of a selecting workgroup
-constexpr int BITMAP_KEYS = 131072;     // positions covered by the finisher's LDS bitmap
 constexpr int CAP_MAX = 128;            // candidate slots per chunk and row
 constexpr uint32_t WS_MAGIC = 0x1D5C0DE5u;
 
@@ -100,13 +99,13 @@ constexpr int HIST_WORDS = 4096 + 64;                       // one histogram: 40
 constexpr int L_HIST = 0;                                   // 2 histograms (low addresses: offsets fold into ds_add)
 constexpr int L_MISC = L_HIST + 2 * HIST_WORDS * 4;         // 64 u32 scratch
 constexpr int L_CAND = L_MISC + 64 * 4;                     // FIN_ENT u64 candidates + 64 dummies (or ALL_MAX u32 keys)
-constexpr int L_BM = L_CAND + (FIN_ENT + 64) * 8;           // bitmap: BITMAP_KEYS / 32 words
-constexpr int L_FIN_END = L_BM + BITMAP_KEYS / 8;
-static_assert(BITMAP_KEYS / 8 >= 4 * NT * 8, "the failing-chunk list (2 words a chunk) fits the bitmap");
+constexpr int BM_WORDS = 8 * NT;                            // chunk thresholds, then failing chunks or a list
+constexpr int L_BM = L_CAND + (FIN_ENT + 64) * 8;           // [4 NT] chunk thresholds, [4 NT] failing chunks
+constexpr int L_FIN_END = L_BM + BM_WORDS * 4;
 static_assert(ALL_MAX % (4 * NT) == 0 && FIN_ENT % (4 * NT) == 0, "register segments of whole slot groups");
 static_assert(ALL_MAX * 4 <= FIN_ENT * 8, "all-keys rows fit the candidate area");
-static_assert(IDX_KMAX <= 4 * NT && IDX_KMAX + 64 <= BITMAP_KEYS / 32,
-              "a list is four entries a thread; it and 64 dummy words fit the bitmap area");
+static_assert(IDX_KMAX <= 4 * NT && IDX_KMAX + 64 <= BM_WORDS,
+              "a list is four entries a thread; it and 64 dummy words fit the threshold area");
 static_assert(L_CAND % 16 == 0, "16-byte candidate reads");
 static_assert(CAP_MAX == 128, "a chunk's candidate block has at most four 32-slot groups");
 static_assert(L_SCORE_END <= 160 * 1024 && L_FIN_END <= 160 * 1024, "LDS budget");
@@ -721,89 +720,6 @@ __device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], const u
   const int tg = tot & 0xFFFF, te = tot >> 16;
   const int got = tg + (te < rem ? te : rem);
   return got;
-}
-
-// Position of the rem-th set bit of bm[0 .. words) (1-based rem).  Every thread must call.
-__device__ uint32_t nth_set_bit(const uint32_t* bm, int words, int rem, int* misc) {
-  const int tid = threadIdx.x;
-  const int wpt = (words + NT - 1) / NT;
-  const int w0 = tid * wpt;
-  int c = 0;
-  for (int i = 0; i < wpt; i++) c += (w0 + i < words) ? __popc(bm[w0 + i]) : 0;
-  int tot;
-  const int before = block_excl_scan(c, misc, &tot);
-  if (before < rem && rem <= before + c) {
-    int need = rem - before;
-    for (int i = 0; i < wpt; i++) {
-      const uint32_t x = (w0 + i < words) ? bm[w0 + i] : 0u;
-      const int pc = __popc(x);
-      if (need <= pc) {
-        uint32_t y = x;
-        for (int s = 1; s < need; s++) y &= y - 1;
-        misc[12] = (w0 + i) * 32 + (__ffs(y) - 1);
-        break;
-      }
-      need -= pc;
-    }
-  }
-  __syncthreads();
-  const uint32_t r = (uint32_t)misc[12];
-  __syncthreads();
-  return r;
-}
-
-// Emit the set bits of bm[0 .. words) as ascending positions into out[0 .. kk).
-// Returns how many bits were set.  Every thread must call.
-__device__ int emit_bitmap(const uint32_t* bm, int words, int* misc, int32_t* out, int kk) {
-  const int tid = threadIdx.x;
-  const int wpt = (words + NT - 1) / NT;
-  const int w0 = tid * wpt;
-  int c = 0;
-  for (int i = 0; i < wpt; i++) c += (w0 + i < words) ? __popc(bm[w0 + i]) : 0;
-  int tot;
-  int o = block_excl_scan(c, misc, &tot);
-  for (int i = 0; i < wpt; i++) {
-    if (w0 + i >= words) break;
-    uint32_t x = bm[w0 + i];
-    while (x) {
-      const int b = __ffs(x) - 1;
-      x &= x - 1;
-      if (o < kk) out[o] = (w0 + i) * 32 + b;
-      o++;
-    }
-  }
-  return tot;
-}
-
-// Top k of the candidates cand[0 .. E) (key << 32 | position) over positions [0, n),
-// given a threshold from kth_select (keys > T, and the first rem keys equal to T in
-// position order), through a position bitmap (the candidates need not be in position
-// order).  Returns the number emitted.  Every thread must call.
-__device__ int select_explicit(const uint64_t* cand, int E, int n, int k, uint32_t T, int rem, uint32_t* bm,
-                               int* misc, int32_t* out) {
-  const int tid = threadIdx.x;
-  const int words = (n + 31) >> 5;
-  for (int i = tid; i < words; i += NT) bm[i] = 0;
-  __syncthreads();
-  int pos_cut = -1;                                   // keys equal to T at positions <= pos_cut
-  if (rem > 0) {
-    for (int e = tid; e < E; e += NT) {
-      const uint64_t c = cand[e];
-      const uint32_t p = (uint32_t)c;
-      if ((uint32_t)(c >> 32) == T) atomicOr(&bm[p >> 5], 1u << (p & 31));
-    }
-    __syncthreads();
-    pos_cut = (int)nth_set_bit(bm, words, rem, misc);
-    for (int i = tid; i < words; i += NT) bm[i] = 0;
-    __syncthreads();
-  }
-  for (int e = tid; e < E; e += NT) {
-    const uint64_t c = cand[e];
-    const uint32_t key = (uint32_t)(c >> 32), p = (uint32_t)c;
-    if (key > T || (key == T && (int)p <= pos_cut)) atomicOr(&bm[p >> 5], 1u << (p & 31));
-  }
-  __syncthreads();
-  return emit_bitmap(bm, words, misc, out, k);
 }
 
 // Exact top-k of row scores in global memory (n > k), one workgroup, LDS for the
@@ -1448,15 +1364,23 @@ __device__ __forceinline__ bool select_all(uint32_t* fk, int n, uint32_t lo, uin
   return true;
 }
 
-// The list of the keys >= Tge among cand[0 .. E1), when cand[0 .. E0) and cand[E0 .. E1)
+// A position as a radix key that decreases with the position: the key of the finite f32
+// 2^20 - pos (exact for the positions of a candidate row, which has at most 2,048 chunks
+// of at most 512 keys).  kth_select over these keys picks the lowest positions.
+constexpr uint32_t CAND_POS_LIMIT = 1u << 20;
+__device__ __forceinline__ uint32_t pos_key(uint32_t pos) { return radix_key((float)(CAND_POS_LIMIT - pos)); }
+static_assert(4 * NT * CMAX <= (int)CAND_POS_LIMIT && CAND_POS_LIMIT <= (1u << 24), "positions as exact f32");
+
+// The list of the keys >= Tge among cand[0 .. E1), and of the keys equal to tkey whose
+// position key (pos_key) is at least pcut, when cand[0 .. E0) and cand[E0 .. E1)
 // each hold distinct positions in ascending order (and no position is in both): each
 // run's kept positions are compacted in order into buf (wave ballots, one block scan),
 // then the two sorted runs are merged, thread t writing list entries [4 t, 4 t + 4)
 // from the split a binary search finds on its diagonal (merge path).  The work is
 // spread over the entries however the kept ones crowd together.  buf holds k words.
 // Returns the number kept.  Every thread must call.
-__device__ __forceinline__ int emit_merged(const uint64_t* cand, int E0, int E1, uint32_t Tge, int k, uint32_t* buf,
-                                           int* misc, int32_t* out) {
+__device__ __forceinline__ int emit_merged(const uint64_t* cand, int E0, int E1, uint32_t Tge, uint32_t tkey,
+                                           uint32_t pcut, int k, uint32_t* buf, int* misc, int32_t* out) {
   constexpr int SR = FIN_ENT / NT;
   static_assert(SR * 64 * NWAVE == FIN_ENT, "the waves' ranges tile the candidate area");
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
@@ -1474,7 +1398,8 @@ __device__ __forceinline__ int emit_merged(const uint64_t* cand, int E0, int E1,
 #pragma unroll
   for (int j = 0; j < SR; j++) {
     const int e = e0 + j * 64 + lane;
-    const bool keep = (j < nj) & (e < E1) & ((uint32_t)(cv[j] >> 32) >= Tge);
+    const uint32_t key = (uint32_t)(cv[j] >> 32);
+    const bool keep = (j < nj) & (e < E1) & ((key >= Tge) | ((key == tkey) & (pos_key((uint32_t)cv[j]) >= pcut)));
     const uint64_t m = __ballot(keep);
     const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
     rk[j] = keep ? cnt + below : -1;
@@ -1527,14 +1452,41 @@ __device__ __forceinline__ int emit_merged(const uint64_t* cand, int E0, int E1,
   return tot;
 }
 
+// The (ceil(k / m) + 1)-th largest local threshold t_w among a row's chunks that did not
+// overflow (bm[w] for w < wact; 0xFFFFFFFF marks an overflowed chunk), or *ok = false when
+// fewer chunks have one.  Every thread must call.
+__device__ __noinline__ uint32_t header_floor(const uint32_t* bm, int wact, int k, int m, uint32_t* hist, int* misc,
+                                              bool* ok) {
+  const int tid = threadIdx.x;
+  uint32_t kr[4];
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    const int w = tid + NT * u;                       // wact <= 4 NT
+    const uint32_t b = w < wact ? bm[w] : 0xFFFFFFFFu;
+    kr[u] = b == 0xFFFFFFFFu ? 0u : b;
+    mn = min(mn, kr[u] != 0u ? kr[u] : 0xFFFFFFFFu);
+    mx = max(mx, kr[u]);
+  }
+  block_min_max(mn, mx, misc);
+  clear_hist(hist);
+  __syncthreads();
+  uint32_t T = 0u;
+  int rem = 0;
+  const int kk = (k + m - 1) / m + 1;
+  *ok = mx != 0u && kth_select<4>(kr, 4, -1, mn, mx, kk, hist, misc, &T, &rem);
+  return rem > 0 ? T - 1u : T;
+}
+
 // Candidate path when the certificate fails.  cand[0 .. E) holds every published key >=
 // lo (chunk w published its keys >= bm[w]; bm[w] = 0xFFFFFFFF marks an overflowed chunk,
 // which published none), so chunk w holds its keys >= held(w) = max(bm[w], lo).  T0 =
 // the k-th candidate (if there are k), at most the row's k-th key; every chunk whose
 // held range does not reach down to T0 is re-read from the row's scores for its keys in
 // [T0, held(w)), after which every key >= T0 of the row is a candidate, and the top k is
-// taken from that set: by merging the two position-ordered runs (emit_merged), or
-// through a position bitmap when a tie at the k-th key is cut (select_explicit).
+// taken from that set by merging the two position-ordered runs (emit_merged); a tie cut
+// at the k-th key keeps the lowest positions, found by a selection over the ties'
+// position keys.
 // Returns true when it selected, false to fall back to the multi-pass select over
 // memory.  Every thread must call.
 __device__ __noinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact, int E, int C, uint32_t lo,
@@ -1573,6 +1525,27 @@ __device__ __noinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact, i
   const bool full = E >= k && kth_select<SR>(kr, S0, E, kmn, kmx, k, hist, misc, &T, &rem);
   // the k-th largest candidate is Tge - 1 when ties are cut, else at least Tge
   const uint32_t lowT = full ? (rem > 0 ? T - 1u : T) : 0u;
+  if (full) {
+    // only the candidates >= lowT can be selected: keep them, in place and in position
+    // order (thread t compacts its run [t S0, t S0 + S0); every run is read before the
+    // scan's barrier, and an entry only moves down), to make room for the re-read
+    uint64_t cv[SR];
+    const int b0 = tid * S0;
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < SR; j++) {
+      const bool in = j < S0 && b0 + j < E;
+      cv[j] = in ? cand[b0 + j] : 0ull;
+      c += (in && (uint32_t)(cv[j] >> 32) >= lowT) ? 1 : 0;
+    }
+    int tot;
+    int o = block_excl_scan(c, misc, &tot);
+#pragma unroll
+    for (int j = 0; j < SR; j++)
+      if (j < S0 && b0 + j < E && (uint32_t)(cv[j] >> 32) >= lowT) cand[o++] = cv[j];
+    E = tot;
+    __syncthreads();
+  }
   // failing chunks listed in bm[4 NT ...] (the thresholds occupy bm[0 .. 4 NT))
   auto held = [&](uint32_t w) {
     const uint32_t b = bm[w];
@@ -1642,10 +1615,30 @@ __device__ __noinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact, i
   __syncthreads();
   const int S1 = load_keys(Ecur);
   if (!kth_select<SR>(kr, S1, Ecur, kmn, kmx, k, hist, misc, &T, &rem)) return false;
-  // without ties to cut, a merge of the two runs in position order; else select_explicit
-  // (keys > Tge - 1 and the first rem keys equal to Tge - 1)
-  const int got = rem == 0 ? emit_merged(cand, E, Ecur, T, k, bm, misc, out)
-                           : select_explicit(cand, Ecur, nr, k, T - 1u, rem, bm, misc, out);
+  // the list is the keys >= T and the first rem keys equal to T - 1 in position order:
+  // those are the rem largest position keys among the keys equal to T - 1 (positions are
+  // distinct), found by one more kth_select, and a merge of the two runs emits the list
+  uint32_t tkey = 0u, pcut = 0xFFFFFFFFu;
+  if (rem > 0) {
+    tkey = T - 1u;
+    uint32_t pmn = 0xFFFFFFFFu, pmx = 0u;
+#pragma unroll
+    for (int j = 0; j < SR; j++) {
+      const uint64_t c = cand[j * NT + tid];
+      const bool tie = j < S1 && (uint32_t)(c >> 32) == tkey;
+      kr[j] = tie ? pos_key((uint32_t)c) : 0u;
+      pmn = min(pmn, tie ? kr[j] : 0xFFFFFFFFu);
+      pmx = max(pmx, kr[j]);
+    }
+    block_min_max(pmn, pmx, misc);
+    clear_hist(hist);
+    __syncthreads();
+    uint32_t Tp;
+    int rp;
+    if (!kth_select<SR>(kr, S1, -1, pmn, pmx, rem, hist, misc, &Tp, &rp)) return false;
+    pcut = rp > 0 ? Tp - 1u : Tp;
+  }
+  const int got = emit_merged(cand, E, Ecur, T, tkey, pcut, k, bm, misc, out);
   if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
   return true;
 }
@@ -2007,10 +2000,11 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
     const int wact = (nr + C - 1) >> a.chunk_shift;
     const int upt = (wact + NT - 1) / NT;
     const uint64_t* erow = reinterpret_cast<const uint64_t*>(ws + a.off_ent) + (int64_t)grow * a.ent_stride * CAP_MAX;
-    int m_unused, cap, G;
-    candidate_params(nr, C, k, &m_unused, &cap, &G);
+    int m, cap, G;
+    candidate_params(nr, C, k, &m, &cap, &G);
     const int SL = 32 * G;                           // slots a chunk
     __amdgpu_buffer_rsrc_t rent = make_rsrc(erow, (int64_t)wact * SL * 8);
+    bool fast_rare = false;
     if (wact * SL <= NT * 16) {
       // One load of everything: thread t holds slots [16 t, 16 t + 16) of the row's blocks
       // (chunk t / 2G), the header and maximum of chunk t / 2G among them when t % 2G == 0;
@@ -2057,11 +2051,42 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
         }
       }
       if (!done) {
+        // the rare cases from the registers as loaded: the chunk thresholds for a re-read
+        // (bm), the mass ties at the top (as in the general path below), else every
+        // published key into cand in position order (they fit: at most 16 NT slots) and
+        // the re-read of the chunks that may hide keys
         __syncthreads();                             // misc may still be read
-        clear_hist(hist);                            // the general path below expects clear histograms
+        if (tid % (2 * G) == 0 && tid / (2 * G) < wact) bm[tid / (2 * G)] = ((sv[0][1] >> 16) & 1u) ? 0xFFFFFFFFu : sv[0][0];
+        if (t4[3] != 0u) {
+          const uint32_t V = t4[2];
+          uint32_t t2[4] = {0u, 0u, 0u, 0u};
+          if (tid % (2 * G) == 0 && tid / (2 * G) < wact && sv[0][0] == V) t2[0] = sv[0][1] & 0xFFFFu;
+          block_sum_max_max_sum(t2, misc);
+          if ((int)t2[0] >= k) {
+            emit_ordered(srow, nr, k, V + 1u, k, out, misc);
+            done = true;
+          }
+        }
+        if (!done) {
+          int c = 0;
+#pragma unroll
+          for (int u = 0; u < 8; u++)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; h2++) c += sv[u][2 * h2 + 1] >= 0x00800000u ? 1 : 0;
+          int tot;
+          int o = block_excl_scan(c, misc, &tot);
+#pragma unroll
+          for (int u = 0; u < 8; u++)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; h2++)
+              if (sv[u][2 * h2 + 1] >= 0x00800000u)
+                cand[o++] = ((uint64_t)sv[u][2 * h2 + 1] << 32) | sv[u][2 * h2];
+          done = rare_select(ws, nr, k, wact, tot, C, 0x00800000u, rs, cand, bm, hist, misc, out);
+          fast_rare = true;                          // the general path would find the same
+        }
       }
     }
-    if (!done) {
+    if (!done && !fast_rare) {
     // the chunk headers with their maxima (thread t: chunks t + NT u; past wact outside
     // the buffer resource), then the first gather batch, in flight together
     uint64_t e[2 * GQ];
@@ -2142,18 +2167,28 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
           done = select_cand<FIN_ENT / NT>(cand, E, lo, hi, k, hist, misc, out, &got, stp);
           if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
         }
-        if (!done && nr <= BITMAP_KEYS && (E >= k || (int)t4[0] <= FIN_ENT)) {
+        if (!done) {
           uint32_t glo = lo;
+          bool ok = true;
           if (E < k) {
-            // fewer than k keys >= t*: every published key instead, chunk w held from its own t_w
+            // fewer than k keys >= t*: gather from a lower floor (chunk w then holds its keys
+            // >= max(t_w, floor)).  Every published key when they fit (the highest T0 below,
+            // so the fewest chunks to re-read); else the keys >= L, the (ceil(k / m) + 1)-th
+            // largest t_w: the chunks at or above L publish at least m keys >= L each but for
+            // the row's last (partial) chunk, so k in all.
             glo = 0x00800000u;
-            E = 0;
-            for (int b0 = 0; b0 < wact; b0 += per_batch) {
-              if (wact > per_batch) issue(b0);         // else e still holds the one batch
-              E += gather_place(e, glo, E, cand, misc);
+            if ((int)t4[0] > FIN_ENT) glo = header_floor(bm, wact, k, m, hist, misc, &ok);
+            if (ok) {
+              E = 0;
+              for (int b0 = 0; b0 < wact && ok; b0 += per_batch) {
+                if (wact > per_batch) issue(b0);       // else e still holds the one batch
+                const int got = gather_place(e, glo, E, cand, misc);
+                if (got < 0) ok = false;
+                else E += got;
+              }
             }
           }
-          done = rare_select(ws, nr, k, wact, E, C, glo, rs, cand, bm, hist, misc, out);
+          if (ok) done = rare_select(ws, nr, k, wact, E, C, glo, rs, cand, bm, hist, misc, out);
         }
       }
     }

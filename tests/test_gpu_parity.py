@@ -11,6 +11,7 @@ import torch
 
 from oracle import indexer as O
 from workloads import make_config, make_problem
+from workloads.synth import quantize_keys
 
 from .gpu_helpers import check_against_oracle, device_problem, run_all
 
@@ -44,10 +45,12 @@ def test_candidate_path(n, k):
 
 
 @pytest.mark.parametrize("n,rows,keys", [(262144, 4, "normal"), (524287, 1, "normal"), (524288, 4, "normal"),
-                                         (262144, 2, "recent"), (300001, 3, "ties")])
+                                         (200000, 2, "recent"), (262144, 2, "recent"), (524287, 1, "recent"),
+                                         (300001, 3, "ties")])
 def test_rows_past_128k(n, rows, keys):
     """Rows of 2-4x the 128K keys (512 to 1,024 chunks): the candidate gather runs in several
-    batches; recent keys and ties at this length take the multi-pass select over memory."""
+    batches; with recent keys the certificate fails and the rare path re-reads the hot
+    chunks from a floor taken from the chunk headers; ties finish from the headers."""
     prob = make_problem([n], [rows], seed=6000 + n + rows, keys=keys, recent=4096, name=f"long{n}x{rows}{keys}")
     print(f"case n={n} rows={rows} keys={keys}", flush=True)
     check_against_oracle(prob, run_all(prob))
@@ -330,3 +333,40 @@ def test_topk_over_more_than_1024_rows():
     for r in range(rows):
         want = O.select(sc[r].astype(np.float64), int(n[r]), k)
         assert np.array_equal(out[r], want), (r, int(n[r]))
+
+
+def _hot_ties(n, rows, k, seed, hot=4096):
+    """Normal keys, except that positions n - hot .. n - 1 carry one of four key vectors
+    (position p the vector p mod 4), scaled 8x: each row's top keys are four tie groups of
+    hot / 4 positions in the hot chunks, whose candidate blocks overflow."""
+    prob = make_problem([n], [rows], seed=seed, k=k, name=f"hotties{n}x{rows}")
+    # four vectors near sum_{r,h} max(w, 0) q: a large positive score in every row
+    q = O.decode_bf16(prob.q[:rows])
+    w = np.maximum(O.decode_bf16(prob.w[:rows]), 0.0)
+    base = np.einsum("rh,rhd->d", w, q)
+    noise = np.random.default_rng(seed + 1).standard_normal((4, base.size))
+    vecs = base / np.linalg.norm(base) + 0.2 * noise / np.sqrt(base.size)
+    vecs *= 8.0 * np.sqrt(base.size) / np.linalg.norm(vecs, axis=1, keepdims=True)
+    codes, scales = quantize_keys(vecs.astype(np.float32))
+    ps = np.arange(n - hot, n)
+    for r in range(rows):                 # every row of the chain reads the same pages
+        pages = prob.page_table[r][ps // 64]
+        prob.k_cache[pages, ps % 64] = codes[ps % 4]
+        prob.k_scale[pages, ps % 64] = scales[ps % 4]
+    return prob
+
+
+@pytest.mark.parametrize("n", [100000, 200000, 300000])
+def test_rare_path_tie_cut(n):
+    """The certificate fails (the hot chunks overflow) and the k-th key falls inside a tie
+    group of the hot positions: the rare path re-reads the hot chunks and keeps the lowest
+    positions of the cut group, at row lengths below and above 131,072 keys."""
+    prob = _hot_ties(n, 2, 2000, seed=9100 + n)
+    print(f"case n={n}", flush=True)
+    res = run_all(prob)
+    check_against_oracle(prob, res)
+    for r in range(prob.rows):
+        nr = int(prob.n_keys[r])
+        g = res["scores"][r, :nr]
+        kth = np.sort(g)[::-1][prob.k - 1]
+        assert np.count_nonzero(g == kth) > 1 and np.count_nonzero(g > kth) < prob.k    # a tie is cut
