@@ -2012,10 +2012,20 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
       // position order, so the selection works on the registers as loaded: a header,
       // maximum or empty slot has an upper word below every key, and the keys below t*
       // are dropped as absent.
+      // (coalesced 16-byte loads, slot pair u NT + t to thread t, through the candidate
+      // area in LDS to each thread's run)
       v4u sv[8];
+      {
+        v4u* const cq = reinterpret_cast<v4u*>(cand);
 #pragma unroll
-      for (int u = 0; u < 8; u++)
-        sv[u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rent, (16 * tid + 2 * u) * 8, 0, 0));
+        for (int u = 0; u < 8; u++)
+          sv[u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rent, (u * NT + tid) * 16, 0, 0));
+#pragma unroll
+        for (int u = 0; u < 8; u++) cq[u * NT + tid] = sv[u];
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 8; u++) sv[u] = cq[8 * tid + u];
+      }
       uint32_t t4[4] = {0u, 0u, 0u, 0u};
       if (tid % (2 * G) == 0) {                      // a header (zeros past the row: no effect)
         const uint32_t tw = sv[0][0], flags = sv[0][1], cmax = sv[0][2];
