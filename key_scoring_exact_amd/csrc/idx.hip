@@ -89,8 +89,7 @@ __host__ __device__ constexpr int l_q(int P, int TS) { return L_KEYS + key_slots
 __host__ __device__ constexpr int l_end(int P, int TS) { return l_q(P, TS) + (8 / TS) * H * D * 2; }
 constexpr int L_SCORE_END = l_end(PMAX, 8) > l_end(PMAX, 2) ? l_end(PMAX, 8) : l_end(PMAX, 2);
 // the publication's scratch, in the ring once the tile loop is done
-constexpr int L_STG = L_KEYS;                               // [GR][CAP_MAX] u64 staged candidate blocks
-constexpr int L_PHIST = L_STG + GR * CAP_MAX * 8;           // [GR][128] u32 chunk histograms
+constexpr int L_PHIST = L_KEYS;                             // [GR][128] u32 chunk histograms
 constexpr int L_KST = L_PHIST + GR * 128 * 4;               // [GR][64] u32 keys of a bisection
 static_assert(L_KST + GR * 64 * 4 <= L_KEYS + PAGE16, "publication scratch fits one ring slot");
 static_assert(L_KEYS % 16 == 0 && l_end(PMAX, 4) <= L_SCORE_END, "layout");
@@ -184,6 +183,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u_t __attribute__((ext_vector_type(2)));
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
@@ -1827,7 +1827,7 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
     const int nr = n[i];
     const int nv = nr - chunk_base;
     if (nv > 0 && row_path(nr, k, shift) == PATH_CAND) {
-      // the chunk's candidate block (32 G slots, staged in LDS, then stored coalesced):
+      // the chunk's candidate block (32 G slots, stored from registers):
       // slot 0 = t_w | (overflow << 16 | count) << 32 (count = the keys >= t_w, published
       // or not), slot 1 = the chunk's largest key,
       // slots 2 .. count + 1 = every key of the chunk >= t_w as key << 32 | position,
@@ -1883,28 +1883,27 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
       const int incl = wave_incl_scan(cnt);
       const int total = __shfl(incl, 63);
       const int SL = 32 * G;
-      uint64_t* stg = LDS_PTR(uint64_t, L_STG) + i * CAP_MAX;    // the ring is free by now
-      for (int q = lane; q < SL; q += 64) stg[q] = 0ull;
       const bool fits = total <= cap;
-      if (fits) {
-        int o = 2 + incl - cnt;
-#pragma unroll
-        for (int j = 0; j < 8; j++)
-          if (key[j] != 0u && key[j] >= thr) {
-            stg[o] = ((uint64_t)key[j] << 32) | (uint32_t)(chunk_base + lane * 8 + j);
-            o++;
-          }
-      }
-      if (lane == 0) {
-        stg[0] = ((uint64_t)((fits ? 0u : (1u << 16)) | (uint32_t)total) << 32) | thr;
-        stg[1] = cmax;
-      }
-      // this wave's LDS writes before its reads (LDS executes a wave's operations in order)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // Straight to the block, branch-free (a store that has no slot goes outside the
+      // buffer resource and is dropped): the candidates to slots 2 .. total + 1 in position
+      // order, then the header, the maximum and zeros over every other slot.
       uint64_t* blk = ent + (int64_t)grow * a.ent_stride * CAP_MAX + (int64_t)c * SL;
-      for (int q = lane; q < SL; q += 64) blk[q] = stg[q];
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(blk, (int64_t)SL * 8);
+      constexpr int OOB = 0x7FFFFFF0;
+      int o = 2 + incl - cnt;
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const bool sel = fits && key[j] != 0u && key[j] >= thr;
+        const uint64_t word = ((uint64_t)key[j] << 32) | (uint32_t)(chunk_base + lane * 8 + j);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u_t, word), rb, sel ? o * 8 : OOB, 0, 0);
+        o += sel ? 1 : 0;
+      }
+      const int used = fits ? total + 2 : 2;
+      const uint64_t head = ((uint64_t)((fits ? 0u : (1u << 16)) | (uint32_t)total) << 32) | thr;
+      for (int q = lane; q < SL; q += 64) {
+        const uint64_t v = q == 0 ? head : (q == 1 ? (uint64_t)cmax : 0ull);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u_t, v), rb, (q < 2 || q >= used) ? q * 8 : OOB, 0, 0);
+      }
     }
   }
   STAMP(a, srec, 5);
