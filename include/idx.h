@@ -88,9 +88,11 @@ typedef struct idx_problem {
   int32_t max_pages;         /* columns of page_table, >= 1 */
   int32_t max_keys;          /* host bound on every n_keys[r]; 0 <= max_keys <= max_pages * page_size,
                                 and max_keys <= IDX_MAX_KEYS (else IDX_EUNSUPPORTED) */
-  const void* q;             /* bf16 [rows][heads][dim], contiguous, 16-byte aligned */
-  const void* w;             /* bf16 [rows][heads], contiguous, 4-byte aligned */
-  const uint8_t* k_cache;    /* E4M3FN codes [num_pages][page_size][dim], 16-byte aligned */
+  const void* q;             /* bf16 [rows][heads][dim], finite, contiguous, 16-byte aligned */
+  const void* w;             /* bf16 [rows][heads], finite, contiguous, 4-byte aligned */
+  const uint8_t* k_cache;    /* E4M3FN codes [num_pages][page_size][dim], 16-byte aligned; no NaN
+                                codes (0x7F, 0xFF) in the keys a row sees: a NaN score has no
+                                place in the order and its row's list is unspecified */
   const float* k_scale;      /* f32 [num_pages][page_size], finite and >= 0, 16-byte aligned */
   const int32_t* page_table; /* int32 [rows][max_pages]: logical page j of row r is physical page
                                 page_table[r][j]; rows of one request must hold the same entries for
