@@ -18,16 +18,22 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 PROBES = {"mfma_accum": ("mfma_probe", [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+          "mfma_rate": ("mfma_rate", [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.POINTER(ctypes.c_double)]),
           "xcd_coherence": ("xcd_coherence_probe", [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                     ctypes.POINTER(ctypes.c_uint32),
                                                     ctypes.POINTER(ctypes.c_uint32)])}
 
 
+LIBS = {"mfma_rate": "mfma_accum"}          # entry points that live in another probe's library
+
+
 def _paths(name):
+    name = LIBS.get(name, name)
     return os.path.join(HERE, name + ".hip"), os.path.join(HERE, "lib" + name + ".so")
 
 
-def build(names=tuple(PROBES)) -> None:
+def build(names=("mfma_accum", "xcd_coherence")) -> None:
     """Compile the probe libraries (every call)."""
     for name in names:
         src, out = _paths(name)

@@ -12,6 +12,9 @@ the score bound of 1e-4 of the row's largest score.  These tests measure it:
   through each instruction with the query split into two E4M3 terms (FP8) or kept in
   bf16, error over the row's largest oracle score.
 
+* ``test_instruction_rate``: the dense issue rate of each instruction on this card,
+  operands in registers, against the published peaks (2.5 PFLOP/s bf16, 5.0 fp8).
+
 Run with ``-s`` to print the tables.  The bf16 instruction is held to the recursive
 summation bound (terms · 2^-24 of sum |a·b|).
 """
@@ -167,3 +170,22 @@ def test_scoring_through_each_instruction():
         print(f"  {name:48s} max {max(errs):10.3e}   rows " + " ".join(f"{e:.2e}" for e in errs))
     assert max(rows["split q, exact sums"]) < 1e-6
     assert max(rows[f"bf16 q on {MODES[2]}"]) < 1e-6
+
+
+def test_instruction_rate():
+    from tests import probes
+    lib = probes.load("mfma_rate")
+    rng = np.random.default_rng(5)
+    inp = torch.from_numpy(rng.integers(0, 2 ** 32, 256, dtype=np.uint64).astype(np.uint32).view(np.int32)).to("cuda")
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    import ctypes
+    peak = {0: 5000.0, 1: 5000.0, 2: 2500.0, 3: 2500.0}
+    names = {**MODES, 3: "v_mfma_f32_16x16x32_bf16"}
+    print("\nDense issue rate, 2048 x 256 threads, two independent chains a wave")
+    for mode in (2, 3, 0, 1):
+        t = ctypes.c_double()
+        rc = lib.mfma_rate(mode, inp.data_ptr(), out.data_ptr(), 4000, ctypes.byref(t))
+        assert rc == 0, f"mfma_rate returned {rc}"
+        assert torch.isfinite(out).all()
+        print(f"  {names[mode]:34s} {t.value:8.1f} TFLOP/s   {t.value / peak[mode]:.3f} of the published peak")
+        assert 0.2 * peak[mode] < t.value < 1.1 * peak[mode], (names[mode], t.value)
