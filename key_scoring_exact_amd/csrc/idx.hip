@@ -407,7 +407,8 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, int 
 // 0 finds the r-th largest exactly.  A bin of more than 64 keys (ties, or a degenerate
 // spread) falls back to radix passes over the keys in [min, max] of that bin, in digits
 // of up to 12 bits below the common prefix.  Absent keys and keys outside the range in
-// play go to per-lane dummy words.  Every thread must call.
+// play go to per-lane dummy words past the bins (with SPARSE, for slots mostly absent,
+// they are skipped instead).  Every thread must call.
 // ---------------------------------------------------------------------------
 // the f32 score a key encodes (the inverse of radix_key for keys of finite scores)
 __device__ __forceinline__ float key_float(uint32_t key) {
@@ -456,7 +457,7 @@ __device__ __forceinline__ void clear_hist(uint32_t* hist) {
   }
 }
 
-template <int SMAX>
+template <int SMAX, bool SPARSE = false>
 __device__ __forceinline__ bool kth_select(const uint32_t (&kr)[SMAX], int S, int cnt, uint32_t lo, uint32_t hi,
                                            int k, uint32_t* hist, int* misc, uint32_t* Tge_out, int* rem_out,
                                            uint64_t* stp = nullptr) {
@@ -501,7 +502,10 @@ __device__ __forceinline__ bool kth_select(const uint32_t (&kr)[SMAX], int S, in
           const uint32_t key = kr[j];
           const uint32_t b = min(__float2uint_rz(fmaf(key_float(max(key, lo)), scale, off)), 4095u);
           idx[j] = key != 0u ? b : dummy;
-          atomicAdd(&hist[idx[j]], 1u);
+          // most slots absent (SPARSE): count only the present keys; else every slot,
+          // the absent ones into the lane's dummy word, without a branch
+          if (!SPARSE) atomicAdd(&hist[idx[j]], 1u);
+          else if (key != 0u) atomicAdd(&hist[b], 1u);
         }
       } else {
 #pragma unroll
@@ -621,7 +625,8 @@ __device__ __forceinline__ bool kth_select(const uint32_t (&kr)[SMAX], int S, in
         const uint32_t key = kr[g * 4 + jj];
         const uint32_t dg = __builtin_amdgcn_ubfe(key, (uint32_t)shift, (uint32_t)width);
         const bool in = key - klo <= span_k && (key & mask) == prefix;   // absent keys wrap out
-        atomicAdd(&h[in ? dg : dummy], 1u);
+        if (!SPARSE) atomicAdd(&h[in ? dg : dummy], 1u);
+        else if (in) atomicAdd(&h[dg], 1u);
       }
     }
     {
@@ -889,7 +894,7 @@ __device__ __forceinline__ bool chunk_bound_linear(const float (&fv)[8], const u
   if (lmin == cmax) return false;
   const float hf = key_float(cmax), lf = key_float(lmin);
   const float span = hf - lf;
-  const float scale = 128.0f / span;
+  const float scale = 128.0f * __builtin_amdgcn_rcpf(span);   // any positive scale keeps the bins monotone
   if (!(span <= 3.0e38f) || !(scale <= 3.0e38f)) return false;
   reinterpret_cast<uint64_t*>(hst)[lane] = 0ull;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1297,6 +1302,14 @@ __device__ __forceinline__ int gather_place(const uint64_t (&e)[2 * GQ], uint32_
 }
 
 // slots a thread holds for E entries: a multiple of 4
+// The LDS slot of 16-byte piece c of an area that threads fill in one order and read in
+// another: c / 8 keeps its 128-byte group, and the piece's place in the group is XORed
+// with (c / 8) % 8.  A lane that reads a run of pieces, at a stride of 4 to 16 pieces
+// between lanes, then meets distinct banks in eight consecutive lanes (with a plain
+// layout they would all meet one bank group); consecutive pieces, as written, still fall
+// in one permuted group.
+__device__ __forceinline__ int swz16(int c) { return (c & ~7) | ((c ^ (c >> 3)) & 7); }
+
 __device__ __forceinline__ int slots_for(int E) { return ((E + NT - 1) / NT + 3) & ~3; }
 
 // zero cand[E .. NT S) (S = slots_for(E)); no barrier
@@ -1337,18 +1350,19 @@ __device__ __forceinline__ bool select_cand(uint64_t* cand, int E, uint32_t lo, 
   return true;
 }
 
-// Top k of all n keys of a row held at their positions (fk[p], zero up to NT
-// slots_for(n)), keys within [lo, hi].  As select_cand otherwise.
+// Top k of all n keys of a row held at their positions (the 16-byte piece of positions
+// 4c .. 4c + 3 at piece swz16(c) of fk, zero up to NT slots_for(n)), keys within
+// [lo, hi].  As select_cand otherwise.
 template <int SMAX>
 __device__ __forceinline__ bool select_all(uint32_t* fk, int n, uint32_t lo, uint32_t hi, int k, uint32_t* hist,
                                            int* misc, int32_t* out, int* got, uint64_t* stp = nullptr) {
   const int S = slots_for(n);
   const int e0 = threadIdx.x * S;
-  const v4u* src = reinterpret_cast<const v4u*>(fk + e0);
+  const v4u* src = reinterpret_cast<const v4u*>(fk);
   uint32_t kr[SMAX], pr[SMAX];
 #pragma unroll
   for (int g = 0; g < SMAX / 4; g++) {
-    const v4u x = g * 4 < S ? src[g] : v4u{0u, 0u, 0u, 0u};
+    const v4u x = g * 4 < S ? src[swz16((e0 >> 2) + g)] : v4u{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int jj = 0; jj < 4; jj++) {
       kr[g * 4 + jj] = x[jj];
@@ -1845,10 +1859,11 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
       const float fv[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
       uint32_t key[8];
       uint32_t lmax = 0;
+      const int lim = nv < C ? nv : C;
 #pragma unroll
       for (int j = 0; j < 8; j++) {
-        const int p = lane * 8 + j;
-        key[j] = (p < nv && p < C) ? radix_key(fv[j]) : 0u;
+        // branch-free: the key, masked off past the chunk's keys
+        key[j] = radix_key(fv[j]) & (lane * 8 + j < lim ? 0xFFFFFFFFu : 0u);
         lmax = lmax > key[j] ? lmax : key[j];
       }
       const uint32_t cmax = wave_max_u32(lmax);
@@ -1881,7 +1896,7 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; j++) cnt += (key[j] != 0u && key[j] >= thr) ? 1 : 0;
       const int incl = wave_incl_scan(cnt);
-      const int total = __shfl(incl, 63);
+      const int total = __builtin_amdgcn_readlane(incl, 63);
       const int SL = 32 * G;
       const bool fits = total <= cap;
       // Straight to the block, branch-free (a store that has no slot goes outside the
@@ -1988,7 +2003,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
           mn = min(mn, y[c] - 1u);
           mx = max(mx, y[c]);
         }
-        *reinterpret_cast<v4u*>(fk + p) = v4u{y[0], y[1], y[2], y[3]};
+        reinterpret_cast<v4u*>(fk)[swz16(p >> 2)] = v4u{y[0], y[1], y[2], y[3]};
       }
     block_min_max(mn, mx, misc);                     // its barriers also publish fk
     STAMP(a, qrec, 1);
@@ -2012,7 +2027,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
       // maximum or empty slot has an upper word below every key, and the keys below t*
       // are dropped as absent.
       // (coalesced 16-byte loads, slot pair u NT + t to thread t, through the candidate
-      // area in LDS to each thread's run)
+      // area in LDS, at swz16 places, to each thread's run)
       v4u sv[8];
       {
         v4u* const cq = reinterpret_cast<v4u*>(cand);
@@ -2020,10 +2035,10 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
         for (int u = 0; u < 8; u++)
           sv[u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rent, (u * NT + tid) * 16, 0, 0));
 #pragma unroll
-        for (int u = 0; u < 8; u++) cq[u * NT + tid] = sv[u];
+        for (int u = 0; u < 8; u++) cq[swz16(u * NT + tid)] = sv[u];
         __syncthreads();
 #pragma unroll
-        for (int u = 0; u < 8; u++) sv[u] = cq[8 * tid + u];
+        for (int u = 0; u < 8; u++) sv[u] = cq[swz16(8 * tid + u)];
       }
       uint32_t t4[4] = {0u, 0u, 0u, 0u};
       if (tid % (2 * G) == 0) {                      // a header (zeros past the row: no effect)
@@ -2052,7 +2067,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
         int rem;
         STAMPP(stp, 5);
         // the count of keys >= t* is unknown here: kth_select finds out whether k are present
-        if (kth_select<16>(kr, 16, -1, lo, hi, k, hist, misc, &Tge, &rem, stp)) {
+        if (kth_select<16, true>(kr, 16, -1, lo, hi, k, hist, misc, &Tge, &rem, stp)) {
           STAMPP(stp, 3);
           const int got = emit_segments<16>(kr, pr, 16, Tge, rem, out, k, misc);
           if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
