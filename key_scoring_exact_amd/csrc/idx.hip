@@ -207,8 +207,8 @@ __device__ inline void raise_error(uint8_t* ws, uint32_t bits) {
 // -0 is first folded into +0 so that equal reals get equal keys.  Finite scores map
 // to keys >= 0x00800000, so 0 never denotes a real score.
 __device__ inline uint32_t radix_key(float f) {
-  uint32_t u = __float_as_uint(f + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);   // ~u if negative, else u | 2^31
 }
 
 __device__ inline int lane_id() { return (int)(threadIdx.x & 63); }
