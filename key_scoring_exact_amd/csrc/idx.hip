@@ -193,9 +193,18 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 // memory helpers
 // ---------------------------------------------------------------------------
+// A raw buffer resource over [base, base + bytes), bytes clamped to [0, 0x7FFFFFF0].  Every
+// caller passes values the wave holds alike; they go through readfirstlane so that the
+// resource sits in scalar registers also where the compiler cannot see that (arguments of
+// a function that is not inlined), else each buffer instruction over it would become a
+// loop over the lanes' distinct values.
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  int64_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : (bytes < 0 ? 0 : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+  const int64_t n = bytes > 0x7FFFFFF0LL ? 0x7FFFFFF0LL : (bytes < 0 ? 0 : bytes);
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const int nn = __builtin_amdgcn_readfirstlane((int)n);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, nn, 0x00020000);
 }
 
 __device__ inline void raise_error(uint8_t* ws, uint32_t bits) {
@@ -1504,9 +1513,10 @@ __device__ __noinline__ uint32_t header_floor(const uint32_t* bm, int wact, int 
 // Returns true when it selected, false to fall back to the multi-pass select over
 // memory.  Every thread must call.
 __device__ __noinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact, int E, int C, uint32_t lo,
-                                            __amdgpu_buffer_rsrc_t rs, uint64_t* cand, uint32_t* bm,
+                                            const float* srow, uint64_t* cand, uint32_t* bm,
                                             uint32_t* hist, int* misc, int32_t* out) {
   const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(srow, (int64_t)nr * 4);
   constexpr int SR = FIN_ENT / NT;
   uint32_t kr[SR];
   // the keys into registers, and their range: lo is only a floor (the smallest finite
@@ -1653,6 +1663,165 @@ __device__ __noinline__ bool rare_select(uint8_t* ws, int nr, int k, int wact, i
     pcut = rp > 0 ? Tp - 1u : Tp;
   }
   const int got = emit_merged(cand, E, Ecur, T, tkey, pcut, k, bm, misc, out);
+  if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
+  return true;
+}
+
+// The fast path's fallback when the chunks holding the row's top keys publish too few of
+// them (the certificate failed: fewer than k keys reach t*).  The candidate set is every
+// key of the J chunks with the highest thresholds t_w (the overflowed chunks first, J as
+// many as the candidate area holds) and the published keys of every other chunk, placed in
+// position order.  A chunk w outside the set hides only keys below t_w, so the set's top k
+// is the row's when its k-th key is at least Y, the largest t_w left out; keys below Y
+// count as absent.  Returns false, with nothing written to out, when the set does not fit
+// or falls short of that.  On entry bm[w] holds t_w (all ones for an overflowed chunk)
+// and bm[6 NT + w] the upper word of chunk w's header; bm[0 .. 4 NT) is left as it was,
+// while the candidate area, both histograms and bm[4 NT .. 6 NT) are overwritten.
+// wact <= NT.  Every thread must call.
+__device__ __noinline__ bool select_hot_chunks(uint8_t* ws, int nr, int k, int wact, int C, int SL,
+                                               const uint64_t* erow, const float* srow,
+                                               uint64_t* cand, uint32_t* bm, uint32_t* hist, int* misc,
+                                               int32_t* out) {
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rent = make_rsrc(erow, (int64_t)wact * SL * 8);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(srow, (int64_t)nr * 4);
+  constexpr int SR = FIN_ENT / NT;
+  constexpr int OOB = 0x7FFFFFF0;
+  const int cshift = 31 - __clz(C);
+  const int sshift = 31 - __clz(SL);
+  // thread w < wact: chunk w's threshold and header flags
+  const bool act = tid < wact;
+  const uint32_t tw = act ? bm[tid] : 0u;
+  const uint32_t hf = act ? bm[6 * NT + tid] : 0u;
+  const bool ov = act && ((hf >> 16) & 1u);
+  const uint32_t cnt = act && !ov ? (hf & 0xFFFFu) : 0u;
+  const int cw_all = act ? min(C, nr - (tid << cshift)) : 0;
+  uint32_t t4[4] = {ov ? 1u : 0u, 0u, 0u, cnt};
+  block_sum_max_max_sum(t4, misc);
+  const int n_ov = (int)t4[0], e_pub = (int)t4[3];
+  const int J = min(wact, (FIN_ENT - e_pub) / C);
+  if (J < n_ov) return false;
+  // X: the (J - n_ov)-th largest threshold of the chunks that did not overflow (all of
+  // them when J covers them; none when J = n_ov)
+  const int jn = J - n_ov, n_kept = wact - n_ov;
+  uint32_t X = 0xFFFFFFFFu;                          // above every key
+  if (jn >= n_kept) {
+    X = 0u;
+  } else if (jn > 0) {
+    uint32_t kr4[4] = {act && !ov ? tw : 0u, 0u, 0u, 0u};
+    uint32_t mn = kr4[0] != 0u ? kr4[0] : 0xFFFFFFFFu, mx = kr4[0];
+    block_min_max(mn, mx, misc);
+    clear_hist(hist);
+    __syncthreads();
+    uint32_t T;
+    int rem;
+    if (!kth_select<4>(kr4, 4, -1, mn, mx, jn, hist, misc, &T, &rem)) return false;
+    X = rem > 0 ? T - 1u : T;
+  }
+  const bool inF = act && (ov || tw >= X);
+  const int cw = inF ? cw_all : (int)cnt;
+  uint32_t t5[4] = {inF ? 1u : 0u, act && !inF && !ov ? tw : 0u, 0u, 0u};
+  int E;
+  const int off = block_excl_scan(cw, misc, &E);
+  int nF;
+  const int fr = block_excl_scan(inF ? 1 : 0, misc, &nF);
+  block_sum_max_max_sum(t5, misc);
+  const uint32_t Y = t5[1];                          // the largest threshold left out (0: none)
+  if (E > FIN_ENT || (nF << cshift) > FIN_ENT) return false;
+  // per chunk: its first entry and whether all its keys are taken, its published count,
+  // and the list of chunks taken whole
+  uint32_t* meta = bm + 4 * NT;
+  uint32_t* flist = bm + 5 * NT;
+  if (act) {
+    meta[tid] = (uint32_t)off | (inF ? 0x80000000u : 0u);
+    hist[tid] = cnt;
+    if (inF) flist[fr] = (uint32_t)tid;
+  }
+  __syncthreads();
+  // All loads first, one round trip: the blocks' slot pairs u NT + t (slot j >= 2 of
+  // chunk w is its published entry j - 2), and 4 consecutive keys a thread a round of the
+  // chunks taken whole.  A group that runs past the row (its last, when nr % 4 != 0) is
+  // read from nr - 4 and shifted into place (nr > ALL_MAX here); groups past the chunks
+  // read from outside the resource.
+  constexpr int RW = FIN_ENT / (4 * NT);
+  v4u pv[8];
+#pragma unroll
+  for (int u = 0; u < 8; u++)
+    pv[u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rent, (u * NT + tid) * 16, 0, 0));
+  const int whole = nF << cshift;
+  v4u kv[RW];
+  int kp[RW], ksh[RW];
+#pragma unroll
+  for (int r = 0; r < RW; r++) {
+    const int i = (r * NT + tid) * 4;
+    const int w = i < whole ? (int)flist[i >> cshift] : 0;
+    const int p = i < whole ? (w << cshift) + (i & (C - 1)) : nr;
+    const int at = p < nr ? min(p, nr - 4) : -1;
+    kp[r] = p;
+    ksh[r] = p - at;
+    kv[r] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, at >= 0 ? at * 4 : OOB, 0, 0));
+  }
+#pragma unroll
+  for (int u = 0; u < 8; u++)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; h2++) {
+      const int sl = 2 * (u * NT + tid) + h2;
+      const int w = sl >> sshift, j = sl & (SL - 1);
+      const bool in = w < wact;
+      const uint32_t m = in ? meta[w] : 0x80000000u;
+      if (!(m >> 31) && j >= 2 && j - 2 < (int)hist[in ? w : 0])
+        cand[(m & 0x7FFFFFFFu) + j - 2] = ((uint64_t)pv[u][2 * h2 + 1] << 32) | pv[u][2 * h2];
+    }
+#pragma unroll
+  for (int r = 0; r < RW; r++) {
+    const int p = kp[r], sh = ksh[r];
+    if (p < nr) {
+      const int w = p >> cshift;
+      const int base = (int)(meta[w] & 0x7FFFFFFFu) + (p & (C - 1));
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const uint32_t x = q + sh == 0 ? kv[r][0] : (q + sh == 1 ? kv[r][1] : (q + sh == 2 ? kv[r][2] : kv[r][3]));
+        if (p + q < nr) cand[base + q] = ((uint64_t)radix_key(__uint_as_float(x)) << 32) | (uint32_t)(p + q);
+      }
+    }
+  }
+  pad_cand(cand, E);
+  __syncthreads();
+  // the top k of the set, keys below Y absent
+  const int S = slots_for(E);
+  const v4u* src = reinterpret_cast<const v4u*>(cand + tid * S);
+  uint32_t kr[SR], pr[SR];
+  uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+#pragma unroll
+  for (int g = 0; g < SR / 4; g++) {
+    if (g * 4 < S) {
+      const v4u x = src[2 * g], y = src[2 * g + 1];
+      pr[g * 4 + 0] = x[0]; kr[g * 4 + 0] = x[1];
+      pr[g * 4 + 1] = x[2]; kr[g * 4 + 1] = x[3];
+      pr[g * 4 + 2] = y[0]; kr[g * 4 + 2] = y[1];
+      pr[g * 4 + 3] = y[2]; kr[g * 4 + 3] = y[3];
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) { kr[g * 4 + jj] = 0u; pr[g * 4 + jj] = 0u; }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; jj++) {
+      kr[g * 4 + jj] = kr[g * 4 + jj] >= Y ? kr[g * 4 + jj] : 0u;
+      kmn = min(kmn, kr[g * 4 + jj] != 0u ? kr[g * 4 + jj] : 0xFFFFFFFFu);
+      kmx = max(kmx, kr[g * 4 + jj]);
+    }
+  }
+  block_min_max(kmn, kmx, misc);
+  if (kmx == 0u) return false;
+  clear_hist(hist);
+  __syncthreads();
+  uint32_t Tge;
+  int rem;
+  if (!kth_select<SR>(kr, S, -1, kmn, kmx, k, hist, misc, &Tge, &rem)) return false;
+  // the k-th key is Tge - 1 when ties are cut, else at least Tge: every key left out must
+  // lie below it (they lie below Y)
+  if (Y > (rem > 0 ? Tge - 1u : Tge)) return false;
+  const int got = emit_segments<SR>(kr, pr, S, Tge, rem, out, k, misc);
   if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
   return true;
 }
@@ -2080,7 +2249,10 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
         // published key into cand in position order (they fit: at most 16 NT slots) and
         // the re-read of the chunks that may hide keys
         __syncthreads();                             // misc may still be read
-        if (tid % (2 * G) == 0 && tid / (2 * G) < wact) bm[tid / (2 * G)] = ((sv[0][1] >> 16) & 1u) ? 0xFFFFFFFFu : sv[0][0];
+        if (tid % (2 * G) == 0 && tid / (2 * G) < wact) {
+          bm[tid / (2 * G)] = ((sv[0][1] >> 16) & 1u) ? 0xFFFFFFFFu : sv[0][0];
+          bm[6 * NT + tid / (2 * G)] = sv[0][1];
+        }
         if (t4[3] != 0u) {
           const uint32_t V = t4[2];
           uint32_t t2[4] = {0u, 0u, 0u, 0u};
@@ -2089,6 +2261,15 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
           if ((int)t2[0] >= k) {
             emit_ordered(srow, nr, k, V + 1u, k, out, misc);
             done = true;
+          }
+        }
+        if (!done && wact <= NT) {
+          __syncthreads();                           // misc may still be read
+          done = select_hot_chunks(ws, nr, k, wact, C, SL, erow, srow, cand, bm, hist, misc, out);
+          if (!done) {
+            // the blocks again (the candidate area and histograms were overwritten)
+            __syncthreads();
+            clear_hist(hist);
           }
         }
         if (!done) {
@@ -2105,7 +2286,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
             for (int h2 = 0; h2 < 2; h2++)
               if (sv[u][2 * h2 + 1] >= 0x00800000u)
                 cand[o++] = ((uint64_t)sv[u][2 * h2 + 1] << 32) | sv[u][2 * h2];
-          done = rare_select(ws, nr, k, wact, tot, C, 0x00800000u, rs, cand, bm, hist, misc, out);
+          done = rare_select(ws, nr, k, wact, tot, C, 0x00800000u, srow, cand, bm, hist, misc, out);
           fast_rare = true;                          // the general path would find the same
         }
       }
@@ -2212,7 +2393,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
               }
             }
           }
-          if (ok) done = rare_select(ws, nr, k, wact, E, C, glo, rs, cand, bm, hist, misc, out);
+          if (ok) done = rare_select(ws, nr, k, wact, E, C, glo, srow, cand, bm, hist, misc, out);
         }
       }
     }
