@@ -98,10 +98,10 @@ def test_recent_region_of_repeated_keys(distinct):
     """The last 4,096 positions of a 131,072-key request (scaled x8, as in the recent
     cache) repeat `distinct` key vectors, position p taking the vector of p mod
     `distinct`.  The 8 chunks there overflow their caps and publish nothing, so every
-    row re-reads them.  With this seed, rows 1 and 2 cut a tie at the k-th key among
-    the re-read keys (273 or 132 positions share it, some selected): the list goes
-    through the position bitmap.  Rows 0 and 3 end with no tie to cut: the two
-    position-ordered runs are merged."""
+    row takes all keys of those chunks (and of the next few by threshold) with the other
+    chunks' published keys.  With this seed, rows 1 and 2 cut a tie at the k-th key
+    among them (273 or 132 positions share it, some selected); rows 0 and 3 end with no
+    tie to cut."""
     prob = make_problem([131072], [4], seed=31, keys="recent", name=f"recent_rep{distinct}")
     n, lo = 131072, 131072 - 4096
     pt = prob.page_table[0]
@@ -118,6 +118,23 @@ def test_recent_region_of_repeated_keys(distinct):
         s = g[r, : int(prob.n_keys[r])].astype(np.float64)
         kth = np.sort(s)[::-1][prob.k - 1]
         assert np.sum(s == kth) > 1 and np.sum(s > kth) < prob.k - 1, (distinct, r)
+
+
+@pytest.mark.parametrize("recent", [2048, 12000, 40000])
+def test_recent_regions_of_several_sizes(recent):
+    """Recent caches whose scaled region covers 4, about 24 or about 78 chunks of a
+    131,072-key request.  The chunks there publish few of the top keys, so the fast path
+    fails its certificate.  The first region fits the chunks taken whole.  The larger
+    ones leave hot chunks out, whose thresholds lie above the k-th key of the set taken;
+    those rows re-read the chunks that may hide keys, or, when the re-read does not fit,
+    select over all their scores in memory (seen on a stamped build: 12,000 takes the
+    re-read in three rows and the memory select in one, 40,000 the memory select in
+    three)."""
+    prob = make_problem([131072], [4], seed=77 + recent, keys="recent", recent=recent,
+                        name=f"recent{recent}")
+    print(f"case recent={recent}", flush=True)
+    res = run_all(prob)
+    check_against_oracle(prob, res)
 
 
 @pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4a", "c4b", "c4c"])
