@@ -736,6 +736,107 @@ __device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], const u
   return got;
 }
 
+// Emission of the top k from slots held piece-major: thread t holds pieces u NT + t
+// (u < np, np uniform) of W slots each, kr/pr[W u + h], and the slots run in the order
+// (u, t, h), which the caller makes ascending in position.  Selection as in
+// emit_segments: key >= Tge, or key == Tge - 1 among the first rem such.  A selected
+// slot's place in the list is the count of selected slots before it: the counts of each
+// (piece u, wave) go through LDS (tot: 128 ceil(NP / 8) words, free on entry), one wave scan
+// over them gives each wave its offset for every u, and ballots with mbcnt give each
+// lane its place within the wave.  The stores of one (u, h) are then short runs of
+// consecutive places.  Returns the number selected.  Every thread must call; one
+// barrier, none after (tot is left dirty).
+template <int NP, int W, bool EQ>
+__device__ __forceinline__ int emit_pieces_impl(const uint32_t (&kr)[NP * W], const uint32_t (&pr)[NP * W], int np,
+                                                uint32_t Tge, int rem, int32_t* out, int k, uint32_t* tot,
+                                                uint64_t* stp) {
+  static_assert(NWAVE == 8 && NP <= 16, "a block of 64 counts holds 8 pieces of every wave");
+  constexpr int QB = (NP + 7) / 8;                  // blocks of 64 (piece, wave) counts
+  const int lane = lane_id(), wv = wave_id();
+  const uint32_t T = Tge - 1u;
+  uint32_t* const tg = tot;
+  uint32_t* const te = tot + QB * 64;
+  uint32_t cg_l = 0u, ce_l = 0u;
+#pragma unroll
+  for (int u = 0; u < NP; u++) {
+    uint32_t g = 0u, e = 0u;
+    if (u < np) {
+#pragma unroll
+      for (int h = 0; h < W; h++) {
+        g += (uint32_t)__popcll(__ballot(kr[W * u + h] >= Tge));
+        if (EQ) e += (uint32_t)__popcll(__ballot(kr[W * u + h] == T));
+      }
+    }
+    cg_l = lane == u ? g : cg_l;                    // lane u writes piece u's counts
+    if (EQ) ce_l = lane == u ? e : ce_l;
+  }
+  if (lane < NP) {
+    tg[lane * NWAVE + wv] = cg_l;
+    if (EQ) te[lane * NWAVE + wv] = ce_l;
+  }
+  __syncthreads();
+  STAMPP(stp, 11);
+  uint32_t og[QB], oe[QB];
+  uint32_t cg = 0u, ce = 0u;
+#pragma unroll
+  for (int c = 0; c < QB; c++) {
+    const int q = c * 64 + lane;
+    const uint32_t xg = q < NP * NWAVE ? tg[q] : 0u;
+    const uint32_t ig = (uint32_t)wave_incl_scan((int)xg);
+    og[c] = cg + ig - xg;
+    cg += rl(ig, 63);
+    if (EQ) {
+      const uint32_t xe = q < NP * NWAVE ? te[q] : 0u;
+      const uint32_t ie = (uint32_t)wave_incl_scan((int)xe);
+      oe[c] = ce + ie - xe;
+      ce += rl(ie, 63);
+    }
+  }
+  STAMPP(stp, 12);
+  const __amdgpu_buffer_rsrc_t rout = make_rsrc(out, (int64_t)k * 4);
+  constexpr int OOB = 0x7FFFFFF0;
+#pragma unroll
+  for (int u = 0; u < NP; u++) {
+    if (u >= np) continue;                          // (no break: the loop must unroll, kr and pr stay in registers)
+    const int ql = (u % 8) * 8 + wv;                // this wave's count of piece u in block u / 8
+    int rg = (int)rl(og[u / 8], ql), re = 0;
+    if (EQ) re = (int)rl(oe[u / 8], ql);
+#pragma unroll
+    for (int h = 0; h < W; h++) {
+      const uint64_t mg = __ballot(kr[W * u + h] >= Tge);
+      rg += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mg, 0u));
+      if (EQ) {
+        const uint64_t me = __ballot(kr[W * u + h] == T);
+        re += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(me >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)me, 0u));
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < W; h++) {
+      const uint32_t key = kr[W * u + h];
+      const bool sg = key >= Tge;
+      bool sel = sg;
+      int o = rg;
+      if (EQ) {
+        const bool se = key == T;
+        sel = sg || (se && re < rem);
+        o = rg + (re < rem ? re : rem);
+        re += se ? 1 : 0;
+      }
+      __builtin_amdgcn_raw_buffer_store_b32(pr[W * u + h], rout, sel ? o * 4 : OOB, 0, 0);
+      rg += sg ? 1 : 0;
+    }
+  }
+  return (int)cg + (EQ ? ((int)ce < rem ? (int)ce : rem) : 0);
+}
+
+template <int NP, int W>
+__device__ __forceinline__ int emit_pieces(const uint32_t (&kr)[NP * W], const uint32_t (&pr)[NP * W], int np,
+                                           uint32_t Tge, int rem, int32_t* out, int k, uint32_t* tot,
+                                           uint64_t* stp = nullptr) {
+  return rem > 0 ? emit_pieces_impl<NP, W, true>(kr, pr, np, Tge, rem, out, k, tot, stp)
+                 : emit_pieces_impl<NP, W, false>(kr, pr, np, Tge, 0, out, k, tot, stp);
+}
+
 // Exact top-k of row scores in global memory (n > k), one workgroup, LDS for the
 // histogram only.  Radix passes of 11, 11 and 10 bits over all scores (16-byte loads, 32
 // keys a thread in flight) find the k-th key; they stop early once every key of the
@@ -1223,6 +1324,34 @@ __device__ __forceinline__ void block_sum_max_max_sum(uint32_t (&t)[4], int* mis
     sd += (uint32_t)misc[3 * NWAVE + i];
   }
   __syncthreads();
+  t[0] = sa;
+  t[1] = mb;
+  t[2] = mc;
+  t[3] = sd;
+}
+
+// The same four figures when only lanes 0, 16, 32 and 48 of each wave can hold nonzero
+// values (a row's chunk headers, piece-major): readlanes instead of row reductions,
+// misc[32 .. 64) as scratch.  One barrier: the caller orders any later write of
+// misc[32 .. 64) behind another.  Every thread must call.
+__device__ __forceinline__ void header_reduce_sparse(uint32_t (&t)[4], int* misc) {
+  uint32_t v[4];
+  v[0] = rl(t[0], 0) + rl(t[0], 16) + rl(t[0], 32) + rl(t[0], 48);
+  v[1] = max(max(rl(t[1], 0), rl(t[1], 16)), max(rl(t[1], 32), rl(t[1], 48)));
+  v[2] = max(max(rl(t[2], 0), rl(t[2], 16)), max(rl(t[2], 32), rl(t[2], 48)));
+  v[3] = rl(t[3], 0) + rl(t[3], 16) + rl(t[3], 32) + rl(t[3], 48);
+  v4u* const red = reinterpret_cast<v4u*>(misc + 32);
+  if (lane_id() == 0) red[wave_id()] = v4u{v[0], v[1], v[2], v[3]};
+  __syncthreads();
+  uint32_t sa = 0, mb = 0, mc = 0, sd = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; i++) {
+    const v4u x = red[i];
+    sa += x[0];
+    mb = max(mb, x[1]);
+    mc = max(mc, x[2]);
+    sd += x[3];
+  }
   t[0] = sa;
   t[1] = mb;
   t[2] = mc;
@@ -2097,6 +2226,7 @@ __global__ __launch_bounds__(NT, 1) void score_kernel(const KArgs a) {
 // Launch 2: workgroup (i, g) selects row i of request g.  Launch 1 has ended, so its
 // scores and candidates are in memory.
 // ---------------------------------------------------------------------------
+template <bool SHORT>
 __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -2179,7 +2309,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
     int got = -1;
     done = select_all<ALL_MAX / NT>(fk, nr, mn + 1u, mx, k, hist, misc, out, &got, stp);
     if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
-  } else if (path == PATH_CAND) {
+  } else if (!SHORT && path == PATH_CAND) {
     const int wact = (nr + C - 1) >> a.chunk_shift;
     const int upt = (wact + NT - 1) / NT;
     const uint64_t* erow = reinterpret_cast<const uint64_t*>(ws + a.off_ent) + (int64_t)grow * a.ent_stride * CAP_MAX;
@@ -2189,36 +2319,32 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
     __amdgpu_buffer_rsrc_t rent = make_rsrc(erow, (int64_t)wact * SL * 8);
     bool fast_rare = false;
     if (wact * SL <= NT * 16) {
-      // One load of everything: thread t holds slots [16 t, 16 t + 16) of the row's blocks
-      // (chunk t / 2G), the header and maximum of chunk t / 2G among them when t % 2G == 0;
-      // slots past the row's blocks read zeros.  Across threads the candidates run in
-      // position order, so the selection works on the registers as loaded: a header,
-      // maximum or empty slot has an upper word below every key, and the keys below t*
-      // are dropped as absent.
-      // (coalesced 16-byte loads, slot pair u NT + t to thread t, through the candidate
-      // area in LDS, at swz16 places, to each thread's run)
+      // One load of everything, piece-major: thread t holds the 16-byte slot pairs
+      // u NT + t (u < 8) of the row's blocks, coalesced; pairs past the row's blocks read
+      // zeros.  A chunk's block is 16 G pairs, so its header and maximum are pair u NT + t
+      // of a thread with t % 16 G == 0 (lanes 0, 16, 32 or 48).  In the order (u, t, slot)
+      // the candidates run in position order, so the selection works on the registers as
+      // loaded: a header, maximum or empty slot has an upper word below every key, and the
+      // keys below t* are dropped as absent.
       v4u sv[8];
-      {
-        v4u* const cq = reinterpret_cast<v4u*>(cand);
 #pragma unroll
-        for (int u = 0; u < 8; u++)
-          sv[u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rent, (u * NT + tid) * 16, 0, 0));
-#pragma unroll
-        for (int u = 0; u < 8; u++) cq[swz16(u * NT + tid)] = sv[u];
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < 8; u++) sv[u] = cq[swz16(8 * tid + u)];
-      }
+      for (int u = 0; u < 8; u++)
+        sv[u] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rent, (u * NT + tid) * 16, 0, 0));
+      const int psh = G == 1 ? 4 : (G == 2 ? 5 : 6);  // pairs a block: 16 G = 1 << psh
+      const bool hdr = (tid & ((1 << psh) - 1)) == 0;
       uint32_t t4[4] = {0u, 0u, 0u, 0u};
-      if (tid % (2 * G) == 0) {                      // a header (zeros past the row: no effect)
-        const uint32_t tw = sv[0][0], flags = sv[0][1], cmax = sv[0][2];
-        const bool ov = (flags >> 16) & 1u;
-        t4[0] = ov ? 0u : (flags & 0xFFFFu);
-        t4[1] = ov ? 0u : tw;
-        t4[2] = cmax;
-        t4[3] = ov ? 1u : 0u;
+      if (hdr) {                                     // headers (zeros past the row: no effect)
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          const uint32_t tw = sv[u][0], flags = sv[u][1], cmax = sv[u][2];
+          const bool ov = (flags >> 16) & 1u;
+          t4[0] += ov ? 0u : (flags & 0xFFFFu);
+          t4[1] = max(t4[1], ov ? 0u : tw);
+          t4[2] = max(t4[2], cmax);
+          t4[3] += ov ? 1u : 0u;
+        }
       }
-      block_sum_max_max_sum(t4, misc);
+      header_reduce_sparse(t4, misc);
       STAMP(a, qrec, 1);
       if (t4[3] == 0u) {
         const uint32_t lo = t4[1] > 0x00800000u ? t4[1] : 0x00800000u;
@@ -2238,25 +2364,35 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
         // the count of keys >= t* is unknown here: kth_select finds out whether k are present
         if (kth_select<16, true>(kr, 16, -1, lo, hi, k, hist, misc, &Tge, &rem, stp)) {
           STAMPP(stp, 3);
-          const int got = emit_segments<16>(kr, pr, 16, Tge, rem, out, k, misc);
+          const int got = emit_pieces<8, 2>(kr, pr, 8, Tge, rem, out, k, hist, stp);
           if (got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
           done = true;
         }
       }
       if (!done) {
         // the rare cases from the registers as loaded: the chunk thresholds for a re-read
-        // (bm), the mass ties at the top (as in the general path below), else every
-        // published key into cand in position order (they fit: at most 16 NT slots) and
-        // the re-read of the chunks that may hide keys
+        // (bm, from the headers), the mass ties at the top (as in the general path below),
+        // the hot-chunk set, else every published key into cand in position order (they
+        // fit: at most 16 NT slots) and the re-read of the chunks that may hide keys
         __syncthreads();                             // misc may still be read
-        if (tid % (2 * G) == 0 && tid / (2 * G) < wact) {
-          bm[tid / (2 * G)] = ((sv[0][1] >> 16) & 1u) ? 0xFFFFFFFFu : sv[0][0];
-          bm[6 * NT + tid / (2 * G)] = sv[0][1];
+        if (hdr) {
+#pragma unroll
+          for (int u = 0; u < 8; u++) {
+            const int w = (u * NT + tid) >> psh;
+            if (w < wact) {
+              bm[w] = ((sv[u][1] >> 16) & 1u) ? 0xFFFFFFFFu : sv[u][0];
+              bm[6 * NT + w] = sv[u][1];
+            }
+          }
         }
         if (t4[3] != 0u) {
           const uint32_t V = t4[2];
           uint32_t t2[4] = {0u, 0u, 0u, 0u};
-          if (tid % (2 * G) == 0 && tid / (2 * G) < wact && sv[0][0] == V) t2[0] = sv[0][1] & 0xFFFFu;
+          if (hdr) {
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+              if (((u * NT + tid) >> psh) < wact && sv[u][0] == V) t2[0] += sv[u][1] & 0xFFFFu;
+          }
           block_sum_max_max_sum(t2, misc);
           if ((int)t2[0] >= k) {
             emit_ordered(srow, nr, k, V + 1u, k, out, misc);
@@ -2273,6 +2409,17 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
           }
         }
         if (!done) {
+          // each thread's pairs made a run in position order first (slots [16 t, 16 t + 16))
+          // through the candidate area at swz16 places; the scan below orders these reads
+          // before the placement overwrites the area
+          {
+            v4u* const cq = reinterpret_cast<v4u*>(cand);
+#pragma unroll
+            for (int u = 0; u < 8; u++) cq[swz16(u * NT + tid)] = sv[u];
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < 8; u++) sv[u] = cq[swz16(8 * tid + u)];
+          }
           int c = 0;
 #pragma unroll
           for (int u = 0; u < 8; u++)
@@ -2414,11 +2561,13 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
 // already reported).  OUT_TAGGED: the same slots, each stored as one 8-byte word
 // tag << 32 | slot with a device-scope store, so that a consumer polling the word sees
 // the old word or the whole new one.
+// SHORT: every group's bound is at most ALL_MAX keys, so no row selects from candidate
+// blocks; the kernel then carries only the paths such rows take.
 constexpr int OUT_LIST = 0, OUT_SLOTS = 1, OUT_TAGGED = 2;
-template <int OUT>
+template <int OUT, bool SHORT>
 __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  if (!select_row(a, smem) || OUT == OUT_LIST) return;
+  if (!select_row<SHORT>(a, smem) || OUT == OUT_LIST) return;
   __syncthreads();                                   // the list's stores, visible to the workgroup
   const uint32_t ge = a.grp[blockIdx.y];
   const int grow = (int)(ge & 0xFFFFFFu) + (int)blockIdx.x;
@@ -2607,13 +2756,14 @@ constexpr int SELECT_LDS = L_FIN_END;
 
 int set_attrs() {
   if (g_attr_done) return IDX_OK;
-  const void* fs[11] = {(const void*)score_kernel<1, false>,      (const void*)score_kernel<2, false>,
-                        (const void*)score_kernel<4, false>,      (const void*)score_kernel<8, false>,
-                        (const void*)score_kernel<1, true>,       (const void*)score_kernel<2, true>,
-                        (const void*)score_kernel<4, true>,       (const void*)score_kernel<8, true>,
-                        (const void*)select_kernel<OUT_LIST>,     (const void*)select_kernel<OUT_SLOTS>,
-                        (const void*)select_kernel<OUT_TAGGED>};
-  for (int i = 0; i < 11; i++) {
+  const void* fs[14] = {(const void*)score_kernel<1, false>,        (const void*)score_kernel<2, false>,
+                        (const void*)score_kernel<4, false>,        (const void*)score_kernel<8, false>,
+                        (const void*)score_kernel<1, true>,         (const void*)score_kernel<2, true>,
+                        (const void*)score_kernel<4, true>,         (const void*)score_kernel<8, true>,
+                        (const void*)select_kernel<OUT_LIST, false>, (const void*)select_kernel<OUT_SLOTS, false>,
+                        (const void*)select_kernel<OUT_TAGGED, false>, (const void*)select_kernel<OUT_LIST, true>,
+                        (const void*)select_kernel<OUT_SLOTS, true>, (const void*)select_kernel<OUT_TAGGED, true>};
+  for (int i = 0; i < 14; i++) {
     const hipError_t e =
         hipFuncSetAttribute(fs[i], hipFuncAttributeMaxDynamicSharedMemorySize, i < 8 ? SCORE_LDS : SELECT_LDS);
     if (e != hipSuccess) return hip_fail(e);
@@ -2644,12 +2794,17 @@ int launch(const KArgs& args, int P, dim3 grid, bool score_launch, bool select_l
   }
   if (select_launch) {
     const dim3 sg(IDX_GROUP_ROWS, grid.y);
-    if (args.tagged)
-      hipLaunchKernelGGL(select_kernel<OUT_TAGGED>, sg, dim3(NT), SELECT_LDS, st, args);
-    else if (args.slots)
-      hipLaunchKernelGGL(select_kernel<OUT_SLOTS>, sg, dim3(NT), SELECT_LDS, st, args);
-    else
-      hipLaunchKernelGGL(select_kernel<OUT_LIST>, sg, dim3(NT), SELECT_LDS, st, args);
+    bool short_rows = true;
+    for (unsigned g = 0; g < grid.y; g++) short_rows = short_rows && args.gmax[g] <= ALL_MAX;
+    const int kind = (args.tagged ? OUT_TAGGED : (args.slots ? OUT_SLOTS : OUT_LIST)) + (short_rows ? 4 : 0);
+    switch (kind) {
+      case OUT_LIST: hipLaunchKernelGGL((select_kernel<OUT_LIST, false>), sg, dim3(NT), SELECT_LDS, st, args); break;
+      case OUT_SLOTS: hipLaunchKernelGGL((select_kernel<OUT_SLOTS, false>), sg, dim3(NT), SELECT_LDS, st, args); break;
+      case OUT_TAGGED: hipLaunchKernelGGL((select_kernel<OUT_TAGGED, false>), sg, dim3(NT), SELECT_LDS, st, args); break;
+      case 4 + OUT_LIST: hipLaunchKernelGGL((select_kernel<OUT_LIST, true>), sg, dim3(NT), SELECT_LDS, st, args); break;
+      case 4 + OUT_SLOTS: hipLaunchKernelGGL((select_kernel<OUT_SLOTS, true>), sg, dim3(NT), SELECT_LDS, st, args); break;
+      default: hipLaunchKernelGGL((select_kernel<OUT_TAGGED, true>), sg, dim3(NT), SELECT_LDS, st, args); break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e);
   }

@@ -266,6 +266,31 @@ def test_random_sweep(case):
     check_against_oracle(prob, run_all(prob, req_max_keys=bounds if case % 2 else None))
 
 
+@pytest.mark.parametrize("n,distinct", [(8192, 1000), (20000, 1500), (40000, 2500), (131072, 2000)])
+def test_repeated_key_vectors(n, distinct):
+    """Position p carries key vector p mod `distinct` of normal keys, so every score value
+    repeats about n / distinct times, each chunk holding at most one copy.  No chunk
+    overflows and no tie is massive, yet the k-th key is shared by positions in and out
+    of the list (checked on the oracle's scores: 8 to 66 positions share it).  The
+    selection from all scores (8,192 and 20,000 keys), the gathered candidates (40,000)
+    and the candidate fast path (131,072) each cut that tie in position order."""
+    prob = make_problem([n], [4], seed=9700 + n, name=f"repeat{distinct}")
+    pt = prob.page_table[0]
+    pos = np.arange(distinct, n)
+    src = pos % distinct
+    prob.k_cache[pt[pos // 64], pos % 64] = prob.k_cache[pt[src // 64], src % 64]
+    prob.k_scale[pt[pos // 64], pos % 64] = prob.k_scale[pt[src // 64], src % 64]
+    print(f"case repeated key vectors n={n} distinct={distinct}", flush=True)
+    res = run_all(prob)
+    check_against_oracle(prob, res)
+    cut = 0
+    for r in range(prob.rows):
+        s = res["scores"][r, : int(prob.n_keys[r])].astype(np.float64)
+        kth = np.sort(s)[::-1][prob.k - 1]
+        cut += int(np.sum(s == kth) > 1 and np.sum(s > kth) < prob.k - 1)
+    assert cut > 0, (n, distinct)
+
+
 @pytest.mark.parametrize("n", [40000, 131072])
 def test_ties_at_random_positions(n):
     """The ties cache with the 4 vectors laid out at seeded random positions: each block of
