@@ -279,19 +279,21 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return (int)v;
 }
 
-// within each row of 16 lanes, lane 15 ends up holding the row's max / min / sum
+// within each row of 16 lanes, lane 15 ends up holding the row's max / min / sum (lanes
+// shifted in from outside the row read the operation's identity, so each step is one
+// DPP-modified max, min or add)
 __device__ __forceinline__ uint32_t row_max(uint32_t v) {
-  v = max(v, dpp<0x111>(v, v));
-  v = max(v, dpp<0x112>(v, v));
-  v = max(v, dpp<0x114>(v, v));
-  v = max(v, dpp<0x118>(v, v));
+  v = max(v, dpp<0x111>(0u, v));
+  v = max(v, dpp<0x112>(0u, v));
+  v = max(v, dpp<0x114>(0u, v));
+  v = max(v, dpp<0x118>(0u, v));
   return v;
 }
 __device__ __forceinline__ uint32_t row_min(uint32_t v) {
-  v = min(v, dpp<0x111>(v, v));
-  v = min(v, dpp<0x112>(v, v));
-  v = min(v, dpp<0x114>(v, v));
-  v = min(v, dpp<0x118>(v, v));
+  v = min(v, dpp<0x111>(0xFFFFFFFFu, v));
+  v = min(v, dpp<0x112>(0xFFFFFFFFu, v));
+  v = min(v, dpp<0x114>(0xFFFFFFFFu, v));
+  v = min(v, dpp<0x118>(0xFFFFFFFFu, v));
   return v;
 }
 __device__ __forceinline__ uint32_t row_sum(uint32_t v) {
