@@ -556,6 +556,7 @@ __device__ __forceinline__ bool kth_select(const uint32_t (&kr)[SMAX], int S, in
         for (int jj = 0; jj < 4; jj++)
           if (idx[g * 4 + jj] == d) lst[atomicAdd(&misc[11], 1)] = kr[g * 4 + jj];
       }
+      STAMPP(stp, 8);
       __syncthreads();
       if (wv == 0) {
         // the r-th largest listed key: the x with #{> x} < r <= #{>= x} (lanes past c
@@ -580,6 +581,7 @@ __device__ __forceinline__ bool kth_select(const uint32_t (&kr)[SMAX], int S, in
           misc[13] = r - gt == eq ? 0 : r - gt;
         }
       }
+      STAMPP(stp, 10);
       __syncthreads();
       *Tge_out = (uint32_t)misc[12];
       *rem_out = misc[13];

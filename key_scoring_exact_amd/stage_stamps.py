@@ -36,7 +36,10 @@ SCORE_STAGES = [(1, "key counts, page ids, queries loaded"), (2, "first key page
                 (5, "publication done (wave 0)")]
 SELECT_STAGES = [(0, "selection start"), (1, "chunk headers reduced, or the row's scores in LDS"),
                  (2, "candidates gathered"), (5, "keys in registers"), (6, "linear histogram"),
-                 (7, "bin of the k-th key found"), (3, "k-th key resolved"), (4, "list written")]
+                 (7, "bin of the k-th key found"), (8, "the bin's keys listed"),
+                 (10, "k-th key among them (wave 0)"), (3, "k-th key resolved"),
+                 (11, "list places counted (piece-major)"), (12, "list offsets scanned (piece-major)"),
+                 (4, "list written")]
 
 
 def main(argv=None):
