@@ -2379,14 +2379,14 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
         // the hot-chunk set, else every published key into cand in position order (they
         // fit: at most 16 NT slots) and the re-read of the chunks that may hide keys
         __syncthreads();                             // misc may still be read
+        // (without branches: a pair past the row's blocks read zeros, its entry of bm lies
+        // past wact, where nothing reads, and a zero header never equals V, a key)
         if (hdr) {
 #pragma unroll
           for (int u = 0; u < 8; u++) {
             const int w = (u * NT + tid) >> psh;
-            if (w < wact) {
-              bm[w] = ((sv[u][1] >> 16) & 1u) ? 0xFFFFFFFFu : sv[u][0];
-              bm[6 * NT + w] = sv[u][1];
-            }
+            bm[w] = ((sv[u][1] >> 16) & 1u) ? 0xFFFFFFFFu : sv[u][0];
+            bm[6 * NT + w] = sv[u][1];
           }
         }
         if (t4[3] != 0u) {
@@ -2394,8 +2394,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
           uint32_t t2[4] = {0u, 0u, 0u, 0u};
           if (hdr) {
 #pragma unroll
-            for (int u = 0; u < 8; u++)
-              if (((u * NT + tid) >> psh) < wact && sv[u][0] == V) t2[0] += sv[u][1] & 0xFFFFu;
+            for (int u = 0; u < 8; u++) t2[0] += sv[u][0] == V ? (sv[u][1] & 0xFFFFu) : 0u;
           }
           block_sum_max_max_sum(t2, misc);
           if ((int)t2[0] >= k) {
