@@ -680,8 +680,11 @@ __device__ __forceinline__ bool kth_select(const uint32_t (&kr)[SMAX], int S, in
 // key is selected when key >= Tge, or, when rem > 0, key == Tge - 1 and it is among
 // the first rem such keys.  Each thread stores its selected positions pr[j] straight
 // to their ranks in out[0 .. k) (a contiguous run a thread, the runs in thread order).
-// Returns the number selected.  Every thread must call.
-template <int SMAX>
+// Unselected slots store past the buffer resource, which drops them; with MASKED they
+// store nothing (the lane is masked off), which is faster where every slot of a thread
+// holds a key (rows selected from all their scores).  Returns the number selected.
+// Every thread must call.
+template <int SMAX, bool MASKED = false>
 __device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], const uint32_t (&pr)[SMAX], int S,
                                              uint32_t Tge, int rem, int32_t* out, int k, int* misc) {
   const uint32_t T = Tge - 1u;
@@ -714,7 +717,11 @@ __device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], const u
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
         const bool sel = kr[g * 4 + jj] >= Tge;
-        __builtin_amdgcn_raw_buffer_store_b32(pr[g * 4 + jj], rout, sel ? o * 4 : 0x7FFFFFF0, 0, 0);
+        if (MASKED) {
+          if (sel) __builtin_amdgcn_raw_buffer_store_b32(pr[g * 4 + jj], rout, o * 4, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b32(pr[g * 4 + jj], rout, sel ? o * 4 : 0x7FFFFFF0, 0, 0);
+        }
         o += sel ? 1 : 0;
       }
     }
@@ -730,7 +737,11 @@ __device__ __forceinline__ int emit_segments(const uint32_t (&kr)[SMAX], const u
         const bool e = key == T;
         const bool sel = key >= Tge || (e && er < rem);
         er += e ? 1 : 0;
-        __builtin_amdgcn_raw_buffer_store_b32(pr[g * 4 + jj], rout, sel ? o * 4 : 0x7FFFFFF0, 0, 0);
+        if (MASKED) {
+          if (sel) __builtin_amdgcn_raw_buffer_store_b32(pr[g * 4 + jj], rout, o * 4, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b32(pr[g * 4 + jj], rout, sel ? o * 4 : 0x7FFFFFF0, 0, 0);
+        }
         o += sel ? 1 : 0;
       }
     }
@@ -1494,8 +1505,8 @@ __device__ __forceinline__ bool select_cand(uint64_t* cand, int E, uint32_t lo, 
 
 // Top k of all n keys of a row held at their positions (the 16-byte piece of positions
 // 4c .. 4c + 3 at piece swz16(c) of fk, zero up to NT slots_for(n)), keys within
-// [lo, hi].  As select_cand otherwise.
-template <int SMAX>
+// [lo, hi].  As select_cand otherwise (MASKED: as emit_segments).
+template <int SMAX, bool MASKED>
 __device__ __forceinline__ bool select_all(uint32_t* fk, int n, uint32_t lo, uint32_t hi, int k, uint32_t* hist,
                                            int* misc, int32_t* out, int* got, uint64_t* stp = nullptr) {
   const int S = slots_for(n);
@@ -1516,7 +1527,7 @@ __device__ __forceinline__ bool select_all(uint32_t* fk, int n, uint32_t lo, uin
   STAMPP(stp, 5);
   if (!kth_select<SMAX>(kr, S, n, lo, hi, k, hist, misc, &Tge, &rem, stp)) return false;
   STAMPP(stp, 3);
-  *got = emit_segments<SMAX>(kr, pr, S, Tge, rem, out, k, misc);
+  *got = emit_segments<SMAX, MASKED>(kr, pr, S, Tge, rem, out, k, misc);
   return true;
 }
 
@@ -2311,7 +2322,7 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
     block_min_max(mn, mx, misc);                     // its barriers also publish fk
     STAMP(a, qrec, 1);
     int got = -1;
-    done = select_all<ALL_MAX / NT>(fk, nr, mn + 1u, mx, k, hist, misc, out, &got, stp);
+    done = select_all<ALL_MAX / NT, SHORT>(fk, nr, mn + 1u, mx, k, hist, misc, out, &got, stp);
     if (done && got != k && tid == 0) raise_error(ws, IDX_DERR_SELECT);
   } else if (!SHORT && path == PATH_CAND) {
     const int wact = (nr + C - 1) >> a.chunk_shift;
@@ -2565,7 +2576,8 @@ __device__ __forceinline__ bool select_row(const KArgs& a, uint8_t* smem) {
 // tag << 32 | slot with a device-scope store, so that a consumer polling the word sees
 // the old word or the whole new one.
 // SHORT: every group's bound is at most ALL_MAX keys, so no row selects from candidate
-// blocks; the kernel then carries only the paths such rows take.
+// blocks; the kernel then carries only the paths such rows take, and its list stores
+// mask off the unselected lanes (every slot of such a row holds a key).
 constexpr int OUT_LIST = 0, OUT_SLOTS = 1, OUT_TAGGED = 2;
 template <int OUT, bool SHORT>
 __global__ __launch_bounds__(NT, 1) void select_kernel(const KArgs a) {
