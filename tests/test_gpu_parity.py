@@ -266,6 +266,18 @@ def test_random_sweep(case):
     check_against_oracle(prob, run_all(prob, req_max_keys=bounds if case % 2 else None))
 
 
+@pytest.mark.parametrize("k", [2048, 512])
+def test_fast_path_block_sizes(k):
+    """One launch of 512-key chunks (set by the 131,072-key request) whose other requests
+    hold 40,000 and 32,768 keys: at k = 2048 their chunks publish blocks of 1, 2 and 4
+    slot groups, and every row still fits the fast path, so the chunk headers sit in
+    lanes 0, 16, 32 and 48, in lanes 0 and 32, or in lane 0 of each wave (k = 512: one
+    group everywhere, fewer candidates a chunk)."""
+    prob = make_problem([131072, 40000, 32768], [1, 4, 4], seed=9600 + k, k=k, name=f"blocks{k}")
+    print(f"case fast-path block sizes k={k}", flush=True)
+    check_against_oracle(prob, run_all(prob))
+
+
 @pytest.mark.parametrize("n,distinct", [(8192, 1000), (20000, 1500), (40000, 2500), (131072, 2000)])
 def test_repeated_key_vectors(n, distinct):
     """Position p carries key vector p mod `distinct` of normal keys, so every score value
