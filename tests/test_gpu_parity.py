@@ -266,6 +266,25 @@ def test_random_sweep(case):
     check_against_oracle(prob, run_all(prob, req_max_keys=bounds if case % 2 else None))
 
 
+@pytest.mark.parametrize("case", range(16))
+def test_random_sweep_long(case):
+    """Seeded random problems on the candidate path: 1-2 requests of 1-4 rows over
+    60,000-300,000 keys, every key cache kind, k from 1 to 2048 (so chunk blocks of one,
+    two and four 32-slot groups), chains or full-context rows, spare pool pages."""
+    rng = np.random.default_rng(24680 + case)
+    nreq = int(rng.integers(1, 3))
+    contexts = [int(rng.integers(60000, 300001)) for _ in range(nreq)]
+    rows = [int(rng.integers(1, 5)) for _ in range(nreq)]
+    k = int(rng.choice([1, 7, 64, 300, 1024, 2048]))
+    keys = str(rng.choice(["normal", "normal", "ties", "zeros", "recent"]))
+    chain = bool(rng.random() < 0.7)
+    prob = make_problem(contexts, rows, seed=70000 + case, k=k, keys=keys, recent=int(rng.integers(64, 16384)),
+                        chain=chain, pad_pages=int(rng.integers(0, 5)), name=f"sweeplong{case}")
+    print(f"case sweeplong{case} contexts={contexts} rows={rows} k={k} keys={keys} chain={chain}", flush=True)
+    bounds = [int(prob.n_keys[a:b].max()) for a, b in zip(prob.req_indptr[:-1], prob.req_indptr[1:])]
+    check_against_oracle(prob, run_all(prob, req_max_keys=bounds if case % 2 else None))
+
+
 @pytest.mark.parametrize("k", [2048, 512])
 def test_fast_path_block_sizes(k):
     """One launch of 512-key chunks (set by the 131,072-key request) whose other requests
