@@ -68,6 +68,37 @@ def test_append_keys(contexts, rows, skip):
     assert np.array_equal(ls2.cpu().numpy(), ls.cpu().numpy())
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_append_random(case):
+    """Seeded random chains with keys written in the launch: 1-2 requests of 1-8 rows over
+    100-250,000 keys, every cache kind, k from 1 to 2048, a random set of rows without a
+    new key."""
+    rng = np.random.default_rng(13579 + case)
+    nreq = int(rng.integers(1, 3))
+    contexts = [int(rng.integers(100, 250001)) for _ in range(nreq)]
+    rows = [int(rng.integers(1, 9)) for _ in range(nreq)]
+    k = int(rng.choice([1, 64, 300, 1024, 2048]))
+    keys = str(rng.choice(["normal", "ties", "zeros", "recent"]))
+    prob = make_problem(contexts, rows, seed=80000 + case, k=k, keys=keys, recent=int(rng.integers(64, 8192)),
+                        name=f"append_random{case}")
+    skip = tuple(int(r) for r in np.nonzero(rng.random(prob.rows) < 0.25)[0])
+    codes, scales, pos = new_keys(prob, 90000 + case, skip)
+    bad = poisoned(prob, pos)
+    print(f"case append_random{case} contexts={contexts} rows={rows} k={k} keys={keys} skip={skip}", flush=True)
+    dp = device_problem(bad)
+    ws = idx.Workspace(prob.rows, dp.max_keys, prob.k)
+    sc, ls = idx.score_topk_append(dp, prob.k, ws, torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(),
+                                   torch.from_numpy(pos).cuda())
+    code, detail = idx.device_status(ws)
+    assert code == 0, hex(detail)
+    want = O.with_new_keys(prob, codes, scales, pos)
+    assert np.array_equal(dp.k_cache.cpu().numpy().view(np.uint8), want.k_cache)
+    assert np.array_equal(dp.k_scale.cpu().numpy(), want.k_scale)
+    s_ = sc.cpu().numpy()
+    check_against_oracle(want, dict(scores=s_, lists=ls.cpu().numpy(), scores_only=s_, lists_topk=ls.cpu().numpy(),
+                                    code=0, detail=0))
+
+
 def test_append_bad_position_reported():
     """A position at or past the row's key count is reported (IDX_DERR_NKEYS) and not written."""
     prob = make_problem([3000], [4], seed=31, name="append_bad")
