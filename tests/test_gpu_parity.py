@@ -247,6 +247,39 @@ def test_slot_output(contexts, rows):
     check_against_oracle(prob, res)
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_slot_output_random(case):
+    """idx_score_topk_slots on seeded random problems (1-3 requests of 1-8 rows over
+    1-200,000 keys, every cache kind, k from 1 to 2048, spare pool pages, chains or
+    full-context rows): lists and scores as idx_score_topk, slots as the oracle's map."""
+    import key_scoring_exact_amd as idx
+    from .gpu_helpers import device_problem
+    rng = np.random.default_rng(97531 + case)
+    nreq = int(rng.integers(1, 4))
+    contexts = [int(rng.integers(1, 200001)) for _ in range(nreq)]
+    rows = [int(rng.integers(1, 9)) for _ in range(nreq)]
+    k = int(rng.choice([1, 64, 300, 1024, 2048]))
+    keys = str(rng.choice(["normal", "ties", "zeros", "recent"]))
+    chain = bool(rng.random() < 0.6)
+    prob = make_problem(contexts, rows, seed=60000 + case, k=k, keys=keys, chain=chain,
+                        pad_pages=int(rng.integers(0, 5)), name=f"slots_random{case}")
+    print(f"case slots_random{case} contexts={contexts} rows={rows} k={k} keys={keys} chain={chain}", flush=True)
+    dp = device_problem(prob)
+    ws = idx.Workspace(prob.rows, dp.max_keys, prob.k)
+    sc, ls, sl = idx.score_topk_slots(dp, prob.k, ws)
+    sc2, ls2 = idx.score_topk(dp, prob.k, ws)
+    assert idx.device_status(ws)[0] == 0
+    ls, sl = ls.cpu().numpy(), sl.cpu().numpy()
+    assert np.array_equal(ls, ls2.cpu().numpy())
+    a, b = sc.cpu().numpy().view(np.uint32), sc2.cpu().numpy().view(np.uint32)
+    for r in range(prob.rows):
+        n = int(prob.n_keys[r])
+        assert np.array_equal(a[r, :n], b[r, :n]), r
+    assert np.array_equal(sl, O.list_slots(prob, ls))
+    res = dict(scores=sc.cpu().numpy(), lists=ls, scores_only=sc.cpu().numpy(), lists_topk=ls, code=0, detail=0)
+    check_against_oracle(prob, res)
+
+
 @pytest.mark.parametrize("case", range(24))
 def test_random_sweep(case):
     """Seeded random problems: 1-4 requests of 1-8 rows, 0-60,000 keys a request, every
