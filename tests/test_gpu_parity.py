@@ -441,6 +441,51 @@ def test_topk_over_more_than_1024_rows():
         assert np.array_equal(out[r], want), (r, int(n[r]))
 
 
+def _given_scores(kind, rows, ld, rng):
+    if kind == "signed zeros":                  # the k-th score a zero of either sign
+        x = rng.standard_normal((rows, ld)).astype(np.float32)
+        z = rng.random((rows, ld)) < 0.7
+        x[z] = np.where(rng.random(int(z.sum())) < 0.5, np.float32(0.0), np.float32(-0.0))
+        return x
+    if kind == "subnormals":                    # mostly subnormal magnitudes, both signs
+        bits = rng.integers(1, 1 << 23, size=(rows, ld), dtype=np.int64).astype(np.uint32)
+        bits |= (rng.random((rows, ld)) < 0.5).astype(np.uint32) << 31
+        x = bits.view(np.float32).copy()
+        x[rng.random((rows, ld)) < 0.05] = np.float32(0.0)
+        return x
+    if kind == "wide":                          # magnitudes over the whole f32 range
+        e = rng.uniform(-44.0, 38.0, size=(rows, ld))
+        return (np.sign(rng.standard_normal((rows, ld))) * 10.0 ** e).astype(np.float32)
+    if kind == "three values":
+        return rng.choice(np.array([-1.5, 0.25, 2.0], dtype=np.float32), size=(rows, ld))
+    # near the largest finite f32
+    return (np.float32(3.0e38) * rng.uniform(-1.1, 1.1, size=(rows, ld))).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["signed zeros", "subnormals", "wide", "three values", "near max"])
+def test_topk_given_scores_values(kind):
+    """idx_topk over caller-given scores with values the scoring never makes: zeros of
+    both signs (equal as reals, the lower position first), subnormals, magnitudes over
+    the whole f32 range, three distinct values, values near the largest finite f32.
+    Rows of 0, 1, 2,047-2,049, 24,576-24,577 and 100,000-200,000 keys (all-scores and
+    candidate paths).  Each list equals the oracle's exact selection."""
+    import key_scoring_exact_amd as idx
+    rng = np.random.default_rng(4242 + len(kind))
+    ld = 200000
+    n = np.array([0, 1, 2047, 2048, 2049, 24576, 24577, 100000, 200000], dtype=np.int32)
+    rows = len(n)
+    sc = _given_scores(kind, rows, ld, rng)
+    assert np.isfinite(sc).all()
+    for k in (1, 300, 2048):
+        print(f"case topk values={kind} k={k}", flush=True)
+        ws = idx.Workspace(rows, ld, k)
+        out = idx.topk(torch.from_numpy(sc).cuda(), torch.from_numpy(n).cuda(), k, ld, ws).cpu().numpy()
+        assert idx.device_status(ws)[0] == 0
+        for r in range(rows):
+            want = O.select(sc[r].astype(np.float64), int(n[r]), k)
+            assert np.array_equal(out[r], want), (kind, k, r, int(n[r]))
+
+
 def _hot_ties(n, rows, k, seed, hot=4096):
     """Normal keys, except that positions n - hot .. n - 1 carry one of four key vectors
     (position p the vector p mod 4), scaled 8x: each row's top keys are four tie groups of
