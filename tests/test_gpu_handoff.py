@@ -50,3 +50,31 @@ def test_tagged_slots(contexts, rows):
     _, _, tg2 = idx.score_topk_tagged(dp, prob.k, ws, tag + 1, tagged=tg)
     w2 = tg2.cpu().numpy()
     assert ready(w2, tag + 1).all() and np.array_equal(slots_of(w2), slots_of(words))
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_tagged_slots_random(case):
+    """Seeded random problems (1-3 requests of 1-8 rows over 1-200,000 keys, every cache
+    kind, k from 1 to 2048, spare pool pages) through two tagged calls in a row: every
+    word ready under its call's tag, the slots equal to the oracle's map of the list."""
+    rng = np.random.default_rng(11223 + case)
+    nreq = int(rng.integers(1, 4))
+    contexts = [int(rng.integers(1, 200001)) for _ in range(nreq)]
+    rows = [int(rng.integers(1, 9)) for _ in range(nreq)]
+    k = int(rng.choice([1, 64, 300, 1024, 2048]))
+    keys = str(rng.choice(["normal", "ties", "zeros", "recent"]))
+    prob = make_problem(contexts, rows, seed=30000 + case, k=k, keys=keys, chain=bool(rng.random() < 0.6),
+                        pad_pages=int(rng.integers(0, 5)), name=f"tagged_random{case}")
+    print(f"case {prob.name} contexts={contexts} rows={rows} k={k} keys={keys}", flush=True)
+    dp = device_problem(prob)
+    ws = idx.Workspace(prob.rows, dp.max_keys, prob.k)
+    words = torch.full((prob.rows, prob.k), -1, dtype=torch.int64, device="cuda")
+    for tag in (0x7A650000 + case, 0x7A650100 + case):
+        sc, ls, tg = idx.score_topk_tagged(dp, prob.k, ws, tag, tagged=words)
+        assert idx.device_status(ws)[0] == 0
+        w, l_ = tg.cpu().numpy(), ls.cpu().numpy()
+        assert ready(w, tag).all()
+        assert np.array_equal(slots_of(w), O.list_slots(prob, l_))
+        res = dict(scores=sc.cpu().numpy(), lists=l_, scores_only=sc.cpu().numpy(), lists_topk=l_, code=0, detail=0)
+        check_against_oracle(prob, res)
+
