@@ -24,3 +24,16 @@ def test_measured_traffic_is_keyed_by_the_library_build():
     assert int(fields["hbm_bytes_per_launch"]) == int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
     assert bench.measured_traffic("0" * 16, "c2") is None
     assert bench.measured_traffic(h, "c1") is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """--gpus above 1 exits (status 2) before touching a GPU, with a one-line JSON message."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
